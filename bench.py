@@ -1,0 +1,300 @@
+#!/usr/bin/env python3
+"""One-GPU benchmark of the paged decode step.
+
+A step is one pass of the whole hot path over one batch: the slot of each
+sequence's new token (slot mapping), the KV write, the attention pass over
+the paged cache and the log-sum-exp merge of context partitions.  Inputs are
+resident in HBM before timing starts; the step is captured once in a HIP graph
+and replayed.
+
+Prints one JSON line.  ``value`` is the KV-read throughput of the whole step:
+the bytes the queries read through their block tables (sum over sequences of
+L * 2 * num_kv_heads * head_size * element bytes) divided by the step time.
+``roofline`` relates the attention kernel alone (its own HIP-event duration)
+to the MI355X HBM peak; ``cpu_baseline`` times the CPU oracle on a bounded
+sample of the same workload.
+
+Usage: python bench.py [--steps K] [--warmup W] [--workload NAME]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "paged decode attn µs/step + KV-read GB/s (% of MI355X HBM peak)"
+PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E, AMD's published figure
+DEFAULT_WORKLOAD = "opt13b_mha"
+KERNEL_SOURCES = ["paged_kv_cache_81_amd/csrc/attention_bf16.hip",
+                  "paged_kv_cache_81_amd/csrc/attention_f32.hip",
+                  "paged_kv_cache_81_amd/csrc/common.hpp"]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_sha() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def kv_bytes(w) -> int:
+    import numpy as np
+    return int(w.context_lens.astype(np.int64).sum()) * 2 * w.num_kv_heads * w.head_size * w.elem_bytes
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per attention launch from the committed rocprofv3 counter
+    summary, if it was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "attention_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f).get(workload)
+    if not rec or rec.get("kernel_source_sha") != kernel_source_sha():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, seconds: float) -> dict:
+    """The CPU oracle, one thread, on a bounded sample of the workload's
+    sequences: slot mapping + write of the new token, gather through the
+    table, float64 attention."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    import oracle
+    from tests import gpu_harness as H
+
+    with threadpool_limits(limits=1):
+        pool = H.nan_pool_numpy(w)
+        oracle.write_ref(pool, w.cached_k, w.cached_v,
+                         oracle.slot_mapping_ref(w.block_tables, w.cached_seq, w.cached_pos,
+                                                 w.block_size))
+        per_tok = 2 * w.num_kv_heads * w.head_size * w.elem_bytes
+        done = 0
+        n = 0
+        t0 = time.perf_counter()
+        for s in range(w.num_seqs):
+            slot = oracle.slot_mapping_ref(w.block_tables, np.array([s]), w.new_pos[s:s + 1],
+                                           w.block_size)
+            oracle.write_ref(pool, w.new_k[s:s + 1], w.new_v[s:s + 1], slot)
+            L = int(w.context_lens[s])
+            k, v = oracle.gather_ref(pool, w.block_tables[s], L)
+            oracle.attention_ref(oracle.to_f64(w.query[s], w.dtype), oracle.to_f64(k, w.dtype),
+                                 oracle.to_f64(v, w.dtype), w.scale)
+            done += L * per_tok
+            n += 1
+            if time.perf_counter() - t0 > seconds:
+                break
+        dt = time.perf_counter() - t0
+    return {"value": round(done / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{n} of {w.num_seqs} sequences of {w.name} ({done / 1e6:.1f} MB of KV), "
+                      f"one decode step each, float64 numpy, {dt:.1f} s",
+            "us_per_step_extrapolated": round(dt / n * w.num_seqs * 1e6, 1)}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--partition-size", type=int, default=None)
+    ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying a graph")
+    ap.add_argument("--no-flush", action="store_true",
+                    help="do not evict caches between the per-kernel timing launches")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}): "
+              "this build runs the decode path on a single MI355X; see the design notes for how "
+              "it would shard.", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_81_amd as pkv
+    import workloads
+    from paged_kv_cache_81_amd._lib import check, lib
+    from tests import gpu_harness as H
+
+    if not torch.cuda.is_available():
+        log("no GPU visible")
+        return 1
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    t = time.time()
+    w = workloads.make(args.workload)
+    log(f"[bench] workload {w.name}: S={w.num_seqs} Hq={w.num_q_heads} Hkv={w.num_kv_heads} "
+        f"D={w.head_size} B={w.block_size} NB={w.num_blocks} sumL={int(w.context_lens.sum())} "
+        f"(generated in {time.time() - t:.1f} s)")
+    st = H.upload(w, device=dev)
+    torch.cuda.synchronize()
+    log("[bench] inputs resident, pool filled")
+
+    S, B, NB = w.num_seqs, w.block_size, w.num_blocks
+    Hq, Hkv, D = w.num_q_heads, w.num_kv_heads, w.head_size
+    dt = 1 if w.dtype == "bf16" else 0
+    P = w.partition_size if args.partition_size is None else args.partition_size
+    P = pkv.partition_size(S, Hq, Hkv, D, B, w.max_context_len, P,
+                           torch.bfloat16 if dt else torch.float32)
+    ws_bytes = pkv.workspace_bytes(S, Hq, Hkv, D, B, w.max_context_len, P,
+                                   torch.bfloat16 if dt else torch.float32)
+    ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+    out = torch.empty((S, Hq, D), dtype=torch.float32, device=dev)
+
+    def calls(stream_handle):
+        slot_a = (st.new_slots.data_ptr(), st.tables.data_ptr(), w.table_width, None,
+                  st.new_pos.data_ptr(), S, S, B, NB, stream_handle)
+        write_a = (st.new_k.data_ptr(), st.new_v.data_ptr(), st.kv.data_ptr(),
+                   st.new_slots.data_ptr(), S, NB, B, Hkv, D, dt, stream_handle)
+        attn_a = (out.data_ptr(), 0, st.query.data_ptr(), st.kv.data_ptr(), st.tables.data_ptr(),
+                  w.table_width, st.lens.data_ptr(), S, Hq, Hkv, D, B, NB, w.scale,
+                  w.max_context_len, P, ws.data_ptr(), ws.numel(), dt, stream_handle)
+        return {
+            "slot_mapping": lambda: check(lib.paged_kv_slot_mapping(*slot_a), "slot mapping"),
+            "kv_write": lambda: check(lib.paged_kv_write(*write_a), "kv write"),
+            "attention": lambda: check(lib.paged_attention_partitions(*attn_a), "attention"),
+            "merge": lambda: check(lib.paged_attention_merge(*attn_a), "merge"),
+        }
+
+    cur = torch.cuda.current_stream(dev)
+    eager = calls(cur.cuda_stream)
+
+    def eager_step():
+        for f in eager.values():
+            f()
+
+    eager_step()
+    torch.cuda.synchronize()
+    ref_out = out.clone()
+
+    if args.no_graph:
+        run_step = eager_step
+    else:
+        graph = torch.cuda.CUDAGraph()
+        cap = torch.cuda.Stream(device=dev)
+        cap.wait_stream(cur)
+        with torch.cuda.stream(cap):
+            captured = calls(cap.cuda_stream)
+            for f in captured.values():
+                f()
+            cap.synchronize()
+            with torch.cuda.graph(graph, stream=cap):
+                for f in captured.values():
+                    f()
+        cur.wait_stream(cap)
+        torch.cuda.synchronize()
+        run_step = graph.replay
+
+    for _ in range(args.warmup):
+        run_step()
+    torch.cuda.synchronize()
+    if not torch.equal(out, ref_out):
+        log("[bench] replayed step differs from the eager step")
+        return 1
+
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t0.record(cur)
+    for _ in range(args.steps):
+        run_step()
+    t1.record(cur)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_per_step = t0.elapsed_time(t1) / args.steps
+    log(f"[bench] {args.steps} steps: {ms_per_step * 1e3:.1f} us/step (wall {wall / args.steps * 1e6:.1f} us)")
+
+    # each kernel on its own: HIP events around every launch on the launch
+    # stream, caches evicted in between (outside the event pair)
+    flush = None if args.no_flush else torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    reps = max(10, min(args.steps, 100))
+    per = {k: [] for k in eager}
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(reps * len(eager))]
+    i = 0
+    for r in range(reps):
+        for name, f in eager.items():
+            if flush is not None:
+                flush.fill_(r & 0xFF)
+            ev[i][0].record(cur)
+            f()
+            ev[i][1].record(cur)
+            per[name].append(i)
+            i += 1
+    torch.cuda.synchronize()
+    kernel_us = {k: float(np.mean([ev[j][0].elapsed_time(ev[j][1]) for j in idx])) * 1e3
+                 for k, idx in per.items()}
+    log("[bench] per-kernel us: " + ", ".join(f"{k} {v:.1f}" for k, v in kernel_us.items()))
+
+    kvb = kv_bytes(w)
+    value = kvb / (ms_per_step * 1e-3) / 1e9
+    attn_gbps = kvb / (kernel_us["attention"] * 1e-6) / 1e9
+    kname = f"attention_bf16_kernel<{D},{B}>" if dt else f"attention_f32_kernel<{D}>"
+    traffic = measured_traffic(w.name)
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "us_per_step": round(ms_per_step * 1e3, 2),
+        "hbm_frac_step": round(value / PEAK_HBM_GBPS, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if dt else "f32",
+        "accumulate": "f32",
+        "data": "synthetic (seeded N(0,1) K/V/q, shuffled block pool)",
+        "config": {
+            "workload": w.name, "num_seqs": S, "num_q_heads": Hq, "num_kv_heads": Hkv,
+            "head_size": D, "block_size": B, "num_blocks": NB,
+            "sum_context_len": int(w.context_lens.sum()), "max_context_len": w.max_context_len,
+            "kv_read_bytes": kvb, "partition_size": P, "graph": not args.no_graph,
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(attn_gbps, 2),
+            "peak": PEAK_HBM_GBPS,
+            "unit": "GB/s",
+            "frac": round(attn_gbps / PEAK_HBM_GBPS, 4),
+            "traffic": traffic,
+            "kernel": kname,
+            "kernel_us": round(kernel_us["attention"], 2),
+            "algorithmic_bytes": kvb,
+            "caches": "evicted before each launch" if flush is not None else "warm",
+        },
+        "kernel_us": {k: round(v, 2) for k, v in kernel_us.items()},
+        "kernel_source_sha": kernel_source_sha(),
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle")
+        result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,196 @@
+"""Paged KV cache decode path for AMD Instinct MI355X (gfx950).
+
+Thin PyTorch-facing wrappers around the C ABI of ``libpagedkv.so``
+(include/paged_kv.h).  They only check shapes, dtypes and devices and pass
+``data_ptr()``s and the current HIP stream; every step of the computation runs
+in the library's HIP kernels.  PyTorch provides device memory and streams.
+
+Cache layout (one attention layer): ``kv_cache[2, num_blocks, block_size,
+num_kv_heads, head_size]``, index 0 keys and index 1 values.
+"""
+from __future__ import annotations
+
+from typing import Optional, Tuple
+
+import torch
+
+from ._lib import PKV_BF16, PKV_F32, PagedKVError, check, lib
+
+__all__ = ["slot_mapping", "write", "gather", "partition_size", "workspace_bytes",
+           "attention_decode", "attention_partitions", "attention_merge", "PagedKVError"]
+
+_DTYPES = {torch.float32: PKV_F32, torch.bfloat16: PKV_BF16}
+
+
+def _dt(t: torch.Tensor) -> int:
+    try:
+        return _DTYPES[t.dtype]
+    except KeyError:
+        raise TypeError(f"unsupported element type {t.dtype} (float32 or bfloat16)") from None
+
+
+def _stream(t: torch.Tensor) -> int:
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _need(t: torch.Tensor, name: str, dtype=None, ndim=None, device=None) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on a GPU")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got {tuple(t.shape)}")
+
+
+def _cache_dims(kv_cache: torch.Tensor):
+    _need(kv_cache, "kv_cache", ndim=5)
+    two, nb, b, hkv, d = kv_cache.shape
+    if two != 2:
+        raise ValueError("kv_cache must be [2, num_blocks, block_size, num_kv_heads, head_size]")
+    return nb, b, hkv, d
+
+
+def slot_mapping(block_tables: torch.Tensor, positions: torch.Tensor, block_size: int,
+                 num_blocks: int, seq_ids: Optional[torch.Tensor] = None,
+                 out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """int64 slot of each (sequence, position); -1 where nothing is written."""
+    _need(block_tables, "block_tables", torch.int32, 2)
+    dev = block_tables.device
+    _need(positions, "positions", torch.int32, 1, dev)
+    T = positions.shape[0]
+    if seq_ids is not None:
+        _need(seq_ids, "seq_ids", torch.int32, 1, dev)
+        if seq_ids.shape[0] != T:
+            raise ValueError("seq_ids and positions differ in length")
+    elif T > block_tables.shape[0]:
+        raise ValueError("without seq_ids, token i belongs to sequence i")
+    if out is None:
+        out = torch.empty(T, dtype=torch.int64, device=dev)
+    _need(out, "out", torch.int64, 1, dev)
+    rc = lib.paged_kv_slot_mapping(out.data_ptr(), block_tables.data_ptr(), block_tables.shape[1],
+                                   seq_ids.data_ptr() if seq_ids is not None else None,
+                                   positions.data_ptr(), T, block_tables.shape[0], block_size,
+                                   num_blocks, _stream(block_tables))
+    check(rc, "paged_kv_slot_mapping")
+    return out
+
+
+def write(key: torch.Tensor, value: torch.Tensor, kv_cache: torch.Tensor,
+          slot_mapping: torch.Tensor) -> None:
+    """Store key[t] / value[t] ([T, Hkv, D]) at slot_mapping[t] of the cache."""
+    nb, b, hkv, d = _cache_dims(kv_cache)
+    dev = kv_cache.device
+    for name, t in (("key", key), ("value", value)):
+        _need(t, name, kv_cache.dtype, 3, dev)
+        if tuple(t.shape[1:]) != (hkv, d):
+            raise ValueError(f"{name} must be [T, {hkv}, {d}]")
+    _need(slot_mapping, "slot_mapping", torch.int64, 1, dev)
+    T = key.shape[0]
+    if value.shape[0] != T or slot_mapping.shape[0] != T:
+        raise ValueError("key, value and slot_mapping differ in length")
+    rc = lib.paged_kv_write(key.data_ptr(), value.data_ptr(), kv_cache.data_ptr(),
+                            slot_mapping.data_ptr(), T, nb, b, hkv, d, _dt(kv_cache),
+                            _stream(kv_cache))
+    check(rc, "paged_kv_write")
+
+
+def gather(kv_cache: torch.Tensor, block_tables: torch.Tensor, context_lens: torch.Tensor,
+           max_context_len: int) -> Tuple[torch.Tensor, torch.Tensor]:
+    """K and V of every sequence in logical order: two [S, max_len, Hkv, D] tensors."""
+    nb, b, hkv, d = _cache_dims(kv_cache)
+    dev = kv_cache.device
+    _need(block_tables, "block_tables", torch.int32, 2, dev)
+    _need(context_lens, "context_lens", torch.int32, 1, dev)
+    S = context_lens.shape[0]
+    if block_tables.shape[0] != S:
+        raise ValueError("block_tables and context_lens differ in length")
+    k = torch.empty((S, max_context_len, hkv, d), dtype=kv_cache.dtype, device=dev)
+    v = torch.empty_like(k)
+    rc = lib.paged_kv_gather(k.data_ptr(), v.data_ptr(), kv_cache.data_ptr(),
+                             block_tables.data_ptr(), block_tables.shape[1],
+                             context_lens.data_ptr(), S, hkv, d, b, nb, max_context_len,
+                             _dt(kv_cache), _stream(kv_cache))
+    check(rc, "paged_kv_gather")
+    return k, v
+
+
+def partition_size(num_seqs, num_q_heads, num_kv_heads, head_size, block_size, max_context_len,
+                   requested: int = 0, dtype: torch.dtype = torch.bfloat16) -> int:
+    p = lib.paged_attention_partition_size(num_seqs, num_q_heads, num_kv_heads, head_size,
+                                           block_size, max_context_len, requested, _DTYPES[dtype])
+    if p < 0:
+        raise PagedKVError(lib.pkv_last_error().decode())
+    return p
+
+
+def workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_size, block_size, max_context_len,
+                    requested: int = 0, dtype: torch.dtype = torch.bfloat16) -> int:
+    return int(lib.paged_attention_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_size,
+                                                   block_size, max_context_len, requested,
+                                                   _DTYPES[dtype]))
+
+
+def _decode_args(query, kv_cache, block_tables, context_lens, scale, max_context_len,
+                 partition, out, out_dtype, workspace):
+    nb, b, hkv, d = _cache_dims(kv_cache)
+    dev = kv_cache.device
+    _need(query, "query", kv_cache.dtype, 3, dev)
+    S, hq, dq = query.shape
+    if dq != d:
+        raise ValueError("query head_size differs from the cache's")
+    _need(block_tables, "block_tables", torch.int32, 2, dev)
+    _need(context_lens, "context_lens", torch.int32, 1, dev)
+    if block_tables.shape[0] != S or context_lens.shape[0] != S:
+        raise ValueError("query, block_tables and context_lens differ in batch size")
+    if out is None:
+        out = torch.empty((S, hq, d), dtype=out_dtype, device=dev)
+    _need(out, "out", None, 3, dev)
+    if tuple(out.shape) != (S, hq, d):
+        raise ValueError("out must be [S, Hq, D]")
+    need = workspace_bytes(S, hq, hkv, d, b, max_context_len, partition, kv_cache.dtype)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _need(workspace, "workspace", torch.uint8, 1, dev)
+    args = (out.data_ptr(), _dt(out), query.data_ptr(), kv_cache.data_ptr(),
+            block_tables.data_ptr(), block_tables.shape[1], context_lens.data_ptr(), S, hq, hkv,
+            d, b, nb, float(scale), int(max_context_len), int(partition), workspace.data_ptr(),
+            workspace.numel(), _dt(kv_cache), _stream(kv_cache))
+    return out, args
+
+
+def attention_decode(query: torch.Tensor, kv_cache: torch.Tensor, block_tables: torch.Tensor,
+                     context_lens: torch.Tensor, scale: float, max_context_len: int,
+                     partition_size: int = 0, out: Optional[torch.Tensor] = None,
+                     out_dtype: torch.dtype = torch.float32,
+                     workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Paged decode attention; returns ``out`` [S, Hq, D]."""
+    out, args = _decode_args(query, kv_cache, block_tables, context_lens, scale, max_context_len,
+                             partition_size, out, out_dtype, workspace)
+    check(lib.paged_attention_decode(*args), "paged_attention_decode")
+    return out
+
+
+def attention_partitions(*a, **k) -> torch.Tensor:
+    """First launch of attention_decode (attention pass); same arguments."""
+    out, args = _decode_args(*_norm(*a, **k))
+    check(lib.paged_attention_partitions(*args), "paged_attention_partitions")
+    return out
+
+
+def attention_merge(*a, **k) -> torch.Tensor:
+    """Second launch of attention_decode (log-sum-exp merge); same arguments."""
+    out, args = _decode_args(*_norm(*a, **k))
+    check(lib.paged_attention_merge(*args), "paged_attention_merge")
+    return out
+
+
+def _norm(query, kv_cache, block_tables, context_lens, scale, max_context_len,
+          partition_size=0, out=None, out_dtype=torch.float32, workspace=None):
+    return (query, kv_cache, block_tables, context_lens, scale, max_context_len, partition_size,
+            out, out_dtype, workspace)

@@ -1,0 +1,61 @@
+"""ctypes loader for ``libpagedkv.so`` (the C ABI declared in include/paged_kv.h).
+
+The library is built in-tree by ``paged_kv_cache_81_amd.build``.  There is no
+fallback: if it is missing, importing this module raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.environ.get("PKV_LIBRARY", os.path.join(_HERE, "libpagedkv.so"))
+
+PKV_F32 = 0
+PKV_BF16 = 1
+
+STATUS = {0: "PKV_OK", -1: "PKV_ERR_INVALID", -2: "PKV_ERR_UNSUPPORTED",
+          -3: "PKV_ERR_WORKSPACE", -4: "PKV_ERR_HIP"}
+
+# every function include/paged_kv.h declares, with its C signature
+_i, _sz, _p, _f = ctypes.c_int, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_float
+SIGNATURES = {
+    "pkv_last_error": (ctypes.c_char_p, []),
+    "paged_kv_slot_mapping": (_i, [_p, _p, _i, _p, _p, _i, _i, _i, _i, _p]),
+    "paged_kv_write": (_i, [_p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _p]),
+    "paged_kv_gather": (_i, [_p, _p, _p, _p, _i, _p, _i, _i, _i, _i, _i, _i, _i, _p]),
+    "paged_attention_partition_size": (_i, [_i, _i, _i, _i, _i, _i, _i, _i]),
+    "paged_attention_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i, _i, _i]),
+    "paged_attention_decode": (_i, [_p, _i, _p, _p, _p, _i, _p, _i, _i, _i, _i, _i, _i, _f,
+                                    _i, _i, _p, _sz, _i, _p]),
+    "paged_attention_partitions": (_i, [_p, _i, _p, _p, _p, _i, _p, _i, _i, _i, _i, _i, _i, _f,
+                                        _i, _i, _p, _sz, _i, _p]),
+    "paged_attention_merge": (_i, [_p, _i, _p, _p, _p, _i, _p, _i, _i, _i, _i, _i, _i, _f,
+                                   _i, _i, _p, _sz, _i, _p]),
+}
+
+
+class PagedKVError(RuntimeError):
+    """A library call returned an error status."""
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build it with `python -m paged_kv_cache_81_amd.build` "
+            "(there is no fallback implementation)")
+    lib = ctypes.CDLL(LIB_PATH)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+lib = _load()
+
+
+def check(rc: int, what: str) -> None:
+    if rc != 0:
+        msg = lib.pkv_last_error().decode(errors="replace")
+        raise PagedKVError(f"{what}: {STATUS.get(rc, rc)}: {msg}")

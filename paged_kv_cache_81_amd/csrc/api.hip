@@ -1,0 +1,294 @@
+// C ABI entry points: host-side argument checks, partition choice and
+// dispatch to the kernels.  Nothing here touches device memory contents.
+#include "common.hpp"
+
+#include <cmath>
+#include <cstdarg>
+#include <string>
+
+namespace pkv {
+
+static thread_local std::string g_error;
+
+void set_error(const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_error = buf;
+}
+
+void clear_error() { g_error.clear(); }
+
+int check_launch(const char* what) {
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) {
+    set_error("%s: launch failed: %s", what, hipGetErrorString(e));
+    return PKV_ERR_HIP;
+  }
+  return PKV_OK;
+}
+
+namespace {
+
+constexpr int kMaxParts = 8192;  // partitions per sequence the merge supports
+constexpr int kGridYZ = 65535;
+
+int elem_bytes(pkv_dtype t) { return t == PKV_F32 ? 4 : (t == PKV_BF16 ? 2 : 0); }
+
+int gcd(int a, int b) { return b ? gcd(b, a % b) : a; }
+
+// Partitions are whole 32-token wave steps and whole blocks.
+int partition_unit(int B) { return 32 / gcd(32, B) * B; }
+
+bool shape_ok(int S, int Hq, int Hkv, int D, int B, int max_len, pkv_dtype dtype) {
+  if (elem_bytes(dtype) == 0) { set_error("unknown dtype %d", static_cast<int>(dtype)); return false; }
+  if (S < 0 || S > kGridYZ) { set_error("num_seqs %d outside [0, %d]", S, kGridYZ); return false; }
+  if (Hq <= 0 || Hkv <= 0 || Hq % Hkv) {
+    set_error("num_q_heads %d must be a positive multiple of num_kv_heads %d", Hq, Hkv);
+    return false;
+  }
+  if (max_len < 0) { set_error("max_context_len %d < 0", max_len); return false; }
+  if (B <= 0) { set_error("block_size %d <= 0", B); return false; }
+  (void)D;
+  return true;
+}
+
+int resolve_partition(int S, int Hq, int Hkv, int D, int B, int max_len, int req, pkv_dtype dtype) {
+  (void)S; (void)Hq; (void)Hkv; (void)D;
+  const int unit = partition_unit(B);
+  const int cap = dtype == PKV_F32 ? 512 : (1 << 20);
+  if (req < 0) return -1;
+  if (req > 0) return (req % unit == 0 && req <= cap) ? req : -1;
+  int P = dtype == PKV_F32 ? 256 : 512;
+  P = (P + unit - 1) / unit * unit;
+  if (P > cap) P = unit;
+  const int whole = static_cast<int>(cdiv64(std::max(max_len, 1), unit) * unit);
+  return std::min(P, whole);
+}
+
+}  // namespace
+}  // namespace pkv
+
+using namespace pkv;
+
+extern "C" {
+
+const char* pkv_last_error(void) { return g_error.c_str(); }
+
+int paged_kv_slot_mapping(int64_t* slot_mapping, const int32_t* block_tables, int table_width,
+                          const int32_t* seq_ids, const int32_t* positions, int num_tokens,
+                          int num_seqs, int block_size, int num_blocks, hipStream_t stream) {
+  clear_error();
+  if (num_tokens < 0 || num_seqs < 0 || table_width <= 0 || block_size <= 0 || num_blocks <= 0) {
+    set_error("slot mapping: bad sizes (tokens %d, seqs %d, width %d, block %d, blocks %d)",
+              num_tokens, num_seqs, table_width, block_size, num_blocks);
+    return PKV_ERR_INVALID;
+  }
+  if (num_tokens > 0 && (!slot_mapping || !block_tables || !positions)) {
+    set_error("slot mapping: null pointer");
+    return PKV_ERR_INVALID;
+  }
+  return launch_slot_mapping(slot_mapping, block_tables, table_width, seq_ids, positions,
+                             num_tokens, num_seqs, block_size, num_blocks, stream);
+}
+
+int paged_kv_write(const void* key, const void* value, void* kv_cache, const int64_t* slot_mapping,
+                   int num_tokens, int num_blocks, int block_size, int num_kv_heads,
+                   int head_size, pkv_dtype dtype, hipStream_t stream) {
+  clear_error();
+  const int eb = elem_bytes(dtype);
+  if (eb == 0) { set_error("kv write: unknown dtype"); return PKV_ERR_INVALID; }
+  if (num_tokens < 0 || num_blocks <= 0 || block_size <= 0 || num_kv_heads <= 0 || head_size <= 0) {
+    set_error("kv write: bad sizes");
+    return PKV_ERR_INVALID;
+  }
+  if ((head_size * eb) % 16) {
+    set_error("kv write: head_size*%d bytes must be a multiple of 16", eb);
+    return PKV_ERR_UNSUPPORTED;
+  }
+  if (num_tokens == 0) return PKV_OK;
+  if (!key || !value || !kv_cache || !slot_mapping) { set_error("kv write: null pointer"); return PKV_ERR_INVALID; }
+  if (!aligned16(key) || !aligned16(value) || !aligned16(kv_cache)) {
+    set_error("kv write: key, value and cache must be 16-byte aligned");
+    return PKV_ERR_INVALID;
+  }
+  return launch_write(key, value, kv_cache, slot_mapping, num_tokens, num_blocks, block_size,
+                      num_kv_heads, head_size, eb, stream);
+}
+
+int paged_kv_gather(void* k_out, void* v_out, const void* kv_cache, const int32_t* block_tables,
+                    int table_width, const int32_t* context_lens, int num_seqs, int num_kv_heads,
+                    int head_size, int block_size, int num_blocks, int max_context_len,
+                    pkv_dtype dtype, hipStream_t stream) {
+  clear_error();
+  const int eb = elem_bytes(dtype);
+  if (eb == 0) { set_error("kv gather: unknown dtype"); return PKV_ERR_INVALID; }
+  if (num_seqs < 0 || num_seqs > kGridYZ || table_width <= 0 || num_kv_heads <= 0 ||
+      head_size <= 0 || block_size <= 0 || num_blocks <= 0 || max_context_len < 0) {
+    set_error("kv gather: bad sizes");
+    return PKV_ERR_INVALID;
+  }
+  if ((head_size * eb) % 16) { set_error("kv gather: head_size bytes must be a multiple of 16"); return PKV_ERR_UNSUPPORTED; }
+  if (num_seqs == 0 || max_context_len == 0) return PKV_OK;
+  if (!k_out || !v_out || !kv_cache || !block_tables || !context_lens) {
+    set_error("kv gather: null pointer");
+    return PKV_ERR_INVALID;
+  }
+  if (!aligned16(k_out) || !aligned16(v_out) || !aligned16(kv_cache)) {
+    set_error("kv gather: buffers must be 16-byte aligned");
+    return PKV_ERR_INVALID;
+  }
+  return launch_gather(k_out, v_out, kv_cache, block_tables, table_width, context_lens, num_seqs,
+                       num_kv_heads, head_size, block_size, num_blocks, max_context_len, eb, stream);
+}
+
+int paged_attention_partition_size(int num_seqs, int num_q_heads, int num_kv_heads, int head_size,
+                                   int block_size, int max_context_len, int partition_size,
+                                   pkv_dtype dtype) {
+  clear_error();
+  if (!shape_ok(num_seqs, num_q_heads, num_kv_heads, head_size, block_size, max_context_len, dtype))
+    return -1;
+  const int P = resolve_partition(num_seqs, num_q_heads, num_kv_heads, head_size, block_size,
+                                  max_context_len, partition_size, dtype);
+  if (P < 0) set_error("partition_size %d is not a positive multiple of %d (fp32: at most 512)",
+                       partition_size, partition_unit(block_size));
+  return P;
+}
+
+size_t paged_attention_workspace_bytes(int num_seqs, int num_q_heads, int num_kv_heads,
+                                       int head_size, int block_size, int max_context_len,
+                                       int partition_size, pkv_dtype dtype) {
+  const int P = paged_attention_partition_size(num_seqs, num_q_heads, num_kv_heads, head_size,
+                                               block_size, max_context_len, partition_size, dtype);
+  if (P <= 0) return 0;
+  const int64_t parts = cdiv64(std::max(max_context_len, 1), P);
+  if (parts <= 1) return 0;
+  const int64_t rows = static_cast<int64_t>(num_seqs) * num_q_heads * parts;
+  const int64_t o_bytes = (rows * head_size * 4 + 255) / 256 * 256;
+  return static_cast<size_t>(o_bytes + rows * 2 * 4);
+}
+
+}  // extern "C"
+
+namespace {
+
+enum Phase { kAttend = 1, kMerge = 2 };
+
+int decode_impl(int phases, void* out, pkv_dtype out_dtype, const void* query,
+                const void* kv_cache, const int32_t* block_tables, int table_width,
+                const int32_t* context_lens, int num_seqs, int num_q_heads, int num_kv_heads,
+                int head_size, int block_size, int num_blocks, float scale, int max_context_len,
+                int partition_size, void* workspace, size_t workspace_bytes, pkv_dtype dtype,
+                hipStream_t stream) {
+  clear_error();
+  if (!shape_ok(num_seqs, num_q_heads, num_kv_heads, head_size, block_size, max_context_len, dtype))
+    return PKV_ERR_INVALID;
+  if (out_dtype != PKV_F32 && out_dtype != PKV_BF16) { set_error("unknown out_dtype"); return PKV_ERR_INVALID; }
+  if (head_size != 64 && head_size != 128) {
+    set_error("head_size %d is not built (64 or 128)", head_size);
+    return PKV_ERR_UNSUPPORTED;
+  }
+  if (dtype == PKV_BF16 && block_size != 16 && block_size != 32 && block_size != 64) {
+    set_error("bf16 path: block_size %d is not built (16, 32 or 64)", block_size);
+    return PKV_ERR_UNSUPPORTED;
+  }
+  if (dtype == PKV_F32 && block_size > 256) {
+    set_error("fp32 path: block_size %d above 256", block_size);
+    return PKV_ERR_UNSUPPORTED;
+  }
+  if (table_width <= 0 || num_blocks <= 0) { set_error("table_width and num_blocks must be positive"); return PKV_ERR_INVALID; }
+  if (!std::isfinite(scale)) { set_error("scale is not finite"); return PKV_ERR_INVALID; }
+  const int G = num_q_heads / num_kv_heads;
+  if (static_cast<int64_t>(num_kv_heads) * ((G + 15) / 16) > kGridYZ) {
+    set_error("too many kv heads for the grid");
+    return PKV_ERR_UNSUPPORTED;
+  }
+  if (num_seqs == 0) return PKV_OK;
+  if (!out || !query || !kv_cache || !block_tables || !context_lens) {
+    set_error("null pointer argument");
+    return PKV_ERR_INVALID;
+  }
+  if (!aligned16(out) || !aligned16(query) || !aligned16(kv_cache)) {
+    set_error("out, query and kv_cache must be 16-byte aligned");
+    return PKV_ERR_INVALID;
+  }
+  const int P = resolve_partition(num_seqs, num_q_heads, num_kv_heads, head_size, block_size,
+                                  max_context_len, partition_size, dtype);
+  if (P <= 0) {
+    set_error("partition_size %d is not a positive multiple of %d (fp32: at most 512)",
+              partition_size, partition_unit(block_size));
+    return PKV_ERR_INVALID;
+  }
+  const int64_t parts = cdiv64(std::max(max_context_len, 1), P);
+  if (parts > kMaxParts) {
+    set_error("%lld partitions per sequence exceed %d; use a larger partition_size",
+              static_cast<long long>(parts), kMaxParts);
+    return PKV_ERR_UNSUPPORTED;
+  }
+  AttnArgs a{};
+  a.out = out;
+  a.query = query;
+  a.kv = kv_cache;
+  a.tables = block_tables;
+  a.lens = context_lens;
+  a.width = table_width;
+  a.S = num_seqs;
+  a.Hq = num_q_heads;
+  a.Hkv = num_kv_heads;
+  a.D = head_size;
+  a.B = block_size;
+  a.NB = num_blocks;
+  a.partition = P;
+  a.max_parts = static_cast<int>(parts);
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.out_bf16 = out_dtype == PKV_BF16 ? 1 : 0;
+  if (parts > 1) {
+    const size_t need = paged_attention_workspace_bytes(num_seqs, num_q_heads, num_kv_heads,
+                                                        head_size, block_size, max_context_len,
+                                                        P, dtype);
+    if (!workspace || workspace_bytes < need) {
+      set_error("workspace of %zu bytes is smaller than the %zu needed", workspace_bytes, need);
+      return PKV_ERR_WORKSPACE;
+    }
+    if (reinterpret_cast<uintptr_t>(workspace) & 255u) {
+      set_error("workspace must be 256-byte aligned");
+      return PKV_ERR_INVALID;
+    }
+    const int64_t rows = static_cast<int64_t>(num_seqs) * num_q_heads * parts;
+    a.ws_o = static_cast<float*>(workspace);
+    a.ws_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                       (rows * head_size * 4 + 255) / 256 * 256);
+  }
+  if (phases & kAttend) {
+    const int rc = dtype == PKV_BF16 ? launch_attention_bf16(a, stream) : launch_attention_f32(a, stream);
+    if (rc != PKV_OK) return rc;
+  }
+  if (phases & kMerge) return launch_reduce(a, stream);
+  return PKV_OK;
+}
+
+}  // namespace
+
+#define PKV_DECODE_ARGS                                                                        \
+  out, out_dtype, query, kv_cache, block_tables, table_width, context_lens, num_seqs,          \
+      num_q_heads, num_kv_heads, head_size, block_size, num_blocks, scale, max_context_len,    \
+      partition_size, workspace, workspace_bytes, dtype, stream
+
+#define PKV_DECODE_PARAMS                                                                      \
+  void *out, pkv_dtype out_dtype, const void *query, const void *kv_cache,                     \
+      const int32_t *block_tables, int table_width, const int32_t *context_lens, int num_seqs, \
+      int num_q_heads, int num_kv_heads, int head_size, int block_size, int num_blocks,        \
+      float scale, int max_context_len, int partition_size, void *workspace,                   \
+      size_t workspace_bytes, pkv_dtype dtype, hipStream_t stream
+
+extern "C" {
+
+int paged_attention_decode(PKV_DECODE_PARAMS) { return decode_impl(kAttend | kMerge, PKV_DECODE_ARGS); }
+
+int paged_attention_partitions(PKV_DECODE_PARAMS) { return decode_impl(kAttend, PKV_DECODE_ARGS); }
+
+int paged_attention_merge(PKV_DECODE_PARAMS) { return decode_impl(kMerge, PKV_DECODE_ARGS); }
+
+}  // extern "C"

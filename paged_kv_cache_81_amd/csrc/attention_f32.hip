@@ -1,0 +1,185 @@
+// Paged decode attention for fp32 caches (vector ALU path).
+//
+// One wave per (partition of <= 512 tokens, kv head, group of <= 16 query
+// heads, sequence).  Phase 1: lane t scores token t of the partition against
+// every query head of the group (q rows staged in LDS).  Phase 2: per-head max
+// and exponentials in the log2 domain.  Phase 3: lanes own dims, walk the
+// partition's tokens and accumulate the weighted values of all heads, so each
+// V row is read once.  fp32 throughout.
+#include "common.hpp"
+
+#include <cmath>
+
+namespace pkv {
+namespace {
+
+constexpr int kMaxPart = 512;
+constexpr int kMaxHeads = 16;
+
+template <int D>
+__global__ void __launch_bounds__(64) attention_f32_kernel(AttnArgs a) {
+  constexpr int PER = D / 64;  // output dims per lane
+  __shared__ float s_q[kMaxHeads][D];
+  __shared__ float s_p[kMaxHeads][kMaxPart];
+
+  const int lane = threadIdx.x;
+  const int G = a.Hq / a.Hkv;
+  const int chunks = (G + kMaxHeads - 1) / kMaxHeads;
+  const int part = blockIdx.x;
+  const int kvh = blockIdx.y / chunks;
+  const int chunk = blockIdx.y - kvh * chunks;
+  const int s = blockIdx.z;
+  const int B = a.B;
+
+  const int L = a.lens[s];
+  const int P = a.partition;
+  const int nparts = L > 0 ? (L + P - 1) / P : 1;
+  const bool bad_seq = L < 0 || (L + B - 1) / B > a.width || nparts > a.max_parts;
+  if (part > 0 && (bad_seq || part >= nparts)) return;
+
+  const int nh = min(kMaxHeads, G - chunk * kMaxHeads);
+  const int h0 = kvh * G + chunk * kMaxHeads;
+  const float* q = static_cast<const float*>(a.query);
+  for (int i = lane; i < nh * D; i += 64)
+    s_q[i / D][i % D] = q[(static_cast<int64_t>(s) * a.Hq + h0) * D + i];
+  __syncthreads();
+
+  const int t_begin = part * P;
+  const int t_end = bad_seq ? t_begin : min(L, t_begin + P);
+  const int n = max(0, t_end - t_begin);
+  const int64_t row = static_cast<int64_t>(a.Hkv) * D;
+  const float* kbase = static_cast<const float*>(a.kv) + static_cast<int64_t>(kvh) * D;
+  const float* vbase = kbase + static_cast<int64_t>(a.NB) * B * row;
+  const int32_t* trow = a.tables + static_cast<int64_t>(s) * a.width;
+  bool bad = bad_seq;
+
+  // phase 1: scores
+  for (int i = lane; i < n; i += 64) {
+    const int t = t_begin + i;
+    const int phys = trow[t / B];
+    float dot[kMaxHeads];
+#pragma unroll
+    for (int h = 0; h < kMaxHeads; ++h) dot[h] = 0.f;
+    if (phys < 0 || phys >= a.NB) {
+      bad = true;
+    } else {
+      const float4* kr = reinterpret_cast<const float4*>(kbase + (static_cast<int64_t>(phys) * B + t % B) * row);
+      for (int c = 0; c < D / 4; ++c) {
+        const float4 kk = kr[c];
+#pragma unroll
+        for (int h = 0; h < kMaxHeads; ++h) {
+          if (h < nh) {
+            dot[h] = fmaf(kk.x, s_q[h][4 * c + 0], dot[h]);
+            dot[h] = fmaf(kk.y, s_q[h][4 * c + 1], dot[h]);
+            dot[h] = fmaf(kk.z, s_q[h][4 * c + 2], dot[h]);
+            dot[h] = fmaf(kk.w, s_q[h][4 * c + 3], dot[h]);
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int h = 0; h < kMaxHeads; ++h)
+      if (h < nh) s_p[h][i] = dot[h] * a.scale_log2;
+  }
+  __syncthreads();
+
+  // phase 2: per-head max and exponentials (log2 domain)
+  float m[kMaxHeads], l[kMaxHeads];
+#pragma unroll
+  for (int h = 0; h < kMaxHeads; ++h) {
+    m[h] = -INFINITY;
+    l[h] = 0.f;
+    if (h < nh) {
+      float mx = -INFINITY;
+      for (int i = lane; i < n; i += 64) mx = fmaxf(mx, s_p[h][i]);
+      mx = wave_max(mx);
+      const float mu = (mx == -INFINITY) ? 0.f : mx;
+      float sum = 0.f;
+      for (int i = lane; i < n; i += 64) {
+        const float p = __builtin_amdgcn_exp2f(s_p[h][i] - mu);
+        s_p[h][i] = p;
+        sum += p;
+      }
+      m[h] = mx;
+      l[h] = wave_sum(sum);
+    }
+  }
+  __syncthreads();
+
+  // phase 3: weighted values; lane owns dims lane*PER .. +PER
+  float acc[kMaxHeads][PER];
+#pragma unroll
+  for (int h = 0; h < kMaxHeads; ++h)
+#pragma unroll
+    for (int e = 0; e < PER; ++e) acc[h][e] = 0.f;
+  for (int i = 0; i < n; ++i) {
+    const int t = t_begin + i;
+    const int phys = trow[t / B];
+    if (phys < 0 || phys >= a.NB) continue;  // flagged in phase 1
+    const float* vr = vbase + (static_cast<int64_t>(phys) * B + t % B) * row + lane * PER;
+    float v[PER];
+#pragma unroll
+    for (int e = 0; e < PER; ++e) v[e] = vr[e];
+#pragma unroll
+    for (int h = 0; h < kMaxHeads; ++h)
+      if (h < nh) {
+        const float p = s_p[h][i];
+#pragma unroll
+        for (int e = 0; e < PER; ++e) acc[h][e] = fmaf(p, v[e], acc[h][e]);
+      }
+  }
+
+  // any lane that saw a bad block poisons the whole work item
+  bad = __any(bad);
+  // without a workspace (one partition per sequence) results always go to out
+  const bool single = nparts == 1 || a.max_parts == 1;
+#pragma unroll
+  for (int h = 0; h < kMaxHeads; ++h) {
+    if (h >= nh) continue;
+    const float inv = l[h] > 0.f ? 1.f / l[h] : 0.f;
+    const int hq = h0 + h;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+      const float o = bad ? NAN : acc[h][e] * inv;
+      const int d = lane * PER + e;
+      if (single) {
+        const int64_t off = (static_cast<int64_t>(s) * a.Hq + hq) * D + d;
+        if (a.out_bf16)
+          static_cast<uint16_t*>(a.out)[off] = f32_to_bf16(o);
+        else
+          static_cast<float*>(a.out)[off] = o;
+      } else {
+        const int64_t sp = (static_cast<int64_t>(s) * a.Hq + hq) * a.max_parts + part;
+        a.ws_o[sp * D + d] = o;
+        if (d == 0) {
+          a.ws_ml[2 * sp] = bad ? NAN : m[h];
+          a.ws_ml[2 * sp + 1] = bad ? NAN : l[h];
+        }
+      }
+    }
+  }
+}
+
+}  // namespace
+
+int launch_attention_f32(const AttnArgs& a, hipStream_t stream) {
+  if (a.S == 0) return PKV_OK;
+  if (a.partition > kMaxPart) {
+    set_error("paged attention (fp32): partition of %d tokens exceeds %d", a.partition, kMaxPart);
+    return PKV_ERR_UNSUPPORTED;
+  }
+  const int G = a.Hq / a.Hkv;
+  const int chunks = (G + kMaxHeads - 1) / kMaxHeads;
+  dim3 grid(a.max_parts, a.Hkv * chunks, a.S);
+  if (a.D == 64) {
+    attention_f32_kernel<64><<<grid, dim3(64), 0, stream>>>(a);
+  } else if (a.D == 128) {
+    attention_f32_kernel<128><<<grid, dim3(64), 0, stream>>>(a);
+  } else {
+    set_error("paged attention (fp32): head_size %d is not built", a.D);
+    return PKV_ERR_UNSUPPORTED;
+  }
+  return check_launch("paged attention (fp32)");
+}
+
+}  // namespace pkv

@@ -1,0 +1,82 @@
+// Internal helpers shared by the HIP sources of the paged KV library (gfx950).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstdio>
+#include <string>
+
+#include "paged_kv.h"
+
+namespace pkv {
+
+// ---------------------------------------------------------------- host side
+
+// Records the message returned by pkv_last_error() for this thread.
+void set_error(const char* fmt, ...) __attribute__((format(printf, 1, 2)));
+void clear_error();
+
+// Turns the last launch error into PKV_ERR_HIP (or PKV_OK).
+int check_launch(const char* what);
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+inline int64_t cdiv64(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// ---------------------------------------------------------------- device side
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// Round to nearest even (hardware conversion on gfx950).
+__device__ __forceinline__ uint16_t f32_to_bf16(float x) {
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(x));
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, 64));
+  return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
+  return v;
+}
+
+// Kernel launchers (one per source file), called from api.hip after the
+// arguments have been checked.
+int launch_slot_mapping(int64_t* slot_mapping, const int32_t* tables, int width,
+                        const int32_t* seq_ids, const int32_t* positions, int T, int S, int B,
+                        int NB, hipStream_t stream);
+int launch_write(const void* key, const void* value, void* kv, const int64_t* slots, int T, int NB,
+                 int B, int Hkv, int D, int elem_bytes, hipStream_t stream);
+int launch_gather(void* k_out, void* v_out, const void* kv, const int32_t* tables, int width,
+                  const int32_t* lens, int S, int Hkv, int D, int B, int NB, int max_len,
+                  int elem_bytes, hipStream_t stream);
+
+struct AttnArgs {
+  void* out;          // [S][Hq][D] fp32 or bf16
+  float* ws_o;        // [S][Hq][max_parts][D]   (split path only)
+  float* ws_ml;       // [S][Hq][max_parts][2]   (m in log2 units, l)
+  const void* query;  // [S][Hq][D]
+  const void* kv;     // [2][NB][B][Hkv][D]
+  const int32_t* tables;
+  const int32_t* lens;
+  int width, S, Hq, Hkv, D, B, NB;
+  int partition;      // tokens per partition
+  int max_parts;      // partitions the grid covers per sequence
+  float scale_log2;   // scale * log2(e)
+  int out_bf16;
+};
+
+int launch_attention_bf16(const AttnArgs& a, hipStream_t stream);
+int launch_attention_f32(const AttnArgs& a, hipStream_t stream);
+int launch_reduce(const AttnArgs& a, hipStream_t stream);
+
+}  // namespace pkv

@@ -28,6 +28,8 @@ model weights or datasets are involved.
 """
 from __future__ import annotations
 
+import os
+from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass, field
 from typing import Dict, List, Optional, Sequence
 
@@ -35,7 +37,7 @@ import numpy as np
 
 TABLE_PAD = np.int32(-2**31)  # value of block-table entries that hold no block
 
-_ROW_CHUNK = 1 << 15  # rows drawn per chunk, bounds the float32 temporaries
+_ROW_CHUNK = 1 << 10  # rows per independently seeded chunk
 
 
 def to_bf16_bits(x: np.ndarray) -> np.ndarray:
@@ -118,14 +120,32 @@ class Workload:
 
 
 def _normal(rng: np.random.Generator, shape, dtype: str) -> np.ndarray:
-    """N(0,1) draws of ``shape`` in the workload's element representation."""
+    """N(0,1) draws of ``shape`` in the workload's element representation.
+
+    One 63-bit seed is taken from ``rng``; the array is then drawn in chunks of
+    ``_ROW_CHUNK`` rows, chunk ``i`` from its own PCG64 stream seeded with
+    (seed, i).  Chunks are independent, so they are drawn in parallel threads
+    and the result does not depend on the number of threads.
+    """
+    seed = int(rng.integers(0, 2**63 - 1))
     rows = shape[0]
     inner = tuple(shape[1:])
     out = np.empty(shape, dtype=np.float32 if dtype == "f32" else np.uint16)
-    for r0 in range(0, rows, _ROW_CHUNK):
+
+    def draw(i: int) -> None:
+        r0 = i * _ROW_CHUNK
         r1 = min(rows, r0 + _ROW_CHUNK)
-        x = rng.standard_normal((r1 - r0,) + inner, dtype=np.float32)
+        g = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, i])))
+        x = g.standard_normal((r1 - r0,) + inner, dtype=np.float32)
         out[r0:r1] = x if dtype == "f32" else to_bf16_bits(x)
+
+    nchunks = (rows + _ROW_CHUNK - 1) // _ROW_CHUNK
+    if nchunks <= 1:
+        for i in range(nchunks):
+            draw(i)
+    else:
+        with ThreadPoolExecutor(max_workers=min(16, os.cpu_count() or 1, nchunks)) as ex:
+            list(ex.map(draw, range(nchunks)))
     return out
 
 
