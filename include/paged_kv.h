@@ -48,6 +48,15 @@ extern "C" {
 
 typedef enum { PKV_F32 = 0, PKV_BF16 = 1 } pkv_dtype;
 
+/* Flags of the attention entry points. */
+enum {
+  /* Blocks may be referenced by several sequences of the batch (shared
+   * prefixes, parallel sampling, beam search): read K/V through the caches so
+   * that sequences sharing a block can hit on it.  Without this flag K/V are
+   * streamed with nontemporal loads, the faster way to read data used once. */
+  PKV_ATTN_CACHED_KV = 1u
+};
+
 typedef enum {
   PKV_OK = 0,
   PKV_ERR_INVALID = -1,     /* bad argument (null pointer, size, alignment)   */
@@ -125,8 +134,11 @@ int paged_kv_gather(void* k_out, void* v_out, const void* kv_cache, const int32_
 
 /*
  * Partition size the decode kernel will use for these arguments: a request of
- * 0 selects one from the shapes; otherwise the request is returned if it is a
- * positive multiple of 32 (and of block_size), else -1.  Host only.
+ * 0 selects one from the shapes (bf16: whole sequences when the batch has
+ * enough (sequence, kv-head group) work items to fill the GPU, else 512
+ * tokens; fp32: 64 tokens); otherwise the request is returned if it is a
+ * positive multiple of 32 and of block_size (fp32: at most 512), else -1.
+ * Host only.
  */
 int paged_attention_partition_size(int num_seqs, int num_q_heads, int num_kv_heads, int head_size,
                                    int block_size, int max_context_len, int partition_size,
@@ -168,6 +180,7 @@ size_t paged_attention_workspace_bytes(int num_seqs, int num_q_heads, int num_kv
  *   context_lens  int32 [num_seqs], 0 <= L <= min(max_context_len, table_width*B)
  *   max_context_len  host int, an upper bound of context_lens (sizes the grid)
  *   partition_size   0 = chosen by the library, else a multiple of 32 and of B
+ *   flags         0 or PKV_ATTN_CACHED_KV
  *   workspace     device scratch of at least paged_attention_workspace_bytes()
  *                 bytes (may be NULL when that is 0), 256-byte aligned
  * Supported: head_size 64 or 128; block_size 16, 32 or 64 (PKV_BF16) and any
@@ -178,7 +191,8 @@ int paged_attention_decode(void* out, pkv_dtype out_dtype, const void* query,
                            const int32_t* context_lens, int num_seqs, int num_q_heads,
                            int num_kv_heads, int head_size, int block_size, int num_blocks,
                            float scale, int max_context_len, int partition_size, void* workspace,
-                           size_t workspace_bytes, pkv_dtype dtype, hipStream_t stream);
+                           size_t workspace_bytes, pkv_dtype dtype, unsigned flags,
+                           hipStream_t stream);
 
 /*
  * The two launches paged_attention_decode makes, exposed so that a caller can
@@ -197,14 +211,15 @@ int paged_attention_partitions(void* out, pkv_dtype out_dtype, const void* query
                                int num_kv_heads, int head_size, int block_size, int num_blocks,
                                float scale, int max_context_len, int partition_size,
                                void* workspace, size_t workspace_bytes, pkv_dtype dtype,
-                               hipStream_t stream);
+                               unsigned flags, hipStream_t stream);
 
 int paged_attention_merge(void* out, pkv_dtype out_dtype, const void* query,
                           const void* kv_cache, const int32_t* block_tables, int table_width,
                           const int32_t* context_lens, int num_seqs, int num_q_heads,
                           int num_kv_heads, int head_size, int block_size, int num_blocks,
                           float scale, int max_context_len, int partition_size, void* workspace,
-                          size_t workspace_bytes, pkv_dtype dtype, hipStream_t stream);
+                          size_t workspace_bytes, pkv_dtype dtype, unsigned flags,
+                          hipStream_t stream);
 
 #ifdef __cplusplus
 }

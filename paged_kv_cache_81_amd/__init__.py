@@ -14,7 +14,7 @@ from typing import Optional, Tuple
 
 import torch
 
-from ._lib import PKV_BF16, PKV_F32, PagedKVError, check, lib
+from ._lib import PKV_ATTN_CACHED_KV, PKV_BF16, PKV_F32, PagedKVError, check, lib
 
 __all__ = ["slot_mapping", "write", "gather", "partition_size", "workspace_bytes",
            "attention_decode", "attention_partitions", "attention_merge", "PagedKVError"]
@@ -137,7 +137,7 @@ def workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_size, block_size, 
 
 
 def _decode_args(query, kv_cache, block_tables, context_lens, scale, max_context_len,
-                 partition, out, out_dtype, workspace):
+                 partition, out, out_dtype, workspace, shared_blocks=False):
     nb, b, hkv, d = _cache_dims(kv_cache)
     dev = kv_cache.device
     _need(query, "query", kv_cache.dtype, 3, dev)
@@ -160,7 +160,8 @@ def _decode_args(query, kv_cache, block_tables, context_lens, scale, max_context
     args = (out.data_ptr(), _dt(out), query.data_ptr(), kv_cache.data_ptr(),
             block_tables.data_ptr(), block_tables.shape[1], context_lens.data_ptr(), S, hq, hkv,
             d, b, nb, float(scale), int(max_context_len), int(partition), workspace.data_ptr(),
-            workspace.numel(), _dt(kv_cache), _stream(kv_cache))
+            workspace.numel(), _dt(kv_cache), PKV_ATTN_CACHED_KV if shared_blocks else 0,
+            _stream(kv_cache))
     return out, args
 
 
@@ -168,10 +169,15 @@ def attention_decode(query: torch.Tensor, kv_cache: torch.Tensor, block_tables: 
                      context_lens: torch.Tensor, scale: float, max_context_len: int,
                      partition_size: int = 0, out: Optional[torch.Tensor] = None,
                      out_dtype: torch.dtype = torch.float32,
-                     workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """Paged decode attention; returns ``out`` [S, Hq, D]."""
+                     workspace: Optional[torch.Tensor] = None,
+                     shared_blocks: bool = False) -> torch.Tensor:
+    """Paged decode attention; returns ``out`` [S, Hq, D].
+
+    ``shared_blocks``: some physical blocks are referenced by several sequences
+    of the batch; K/V are then read through the caches (PKV_ATTN_CACHED_KV).
+    """
     out, args = _decode_args(query, kv_cache, block_tables, context_lens, scale, max_context_len,
-                             partition_size, out, out_dtype, workspace)
+                             partition_size, out, out_dtype, workspace, shared_blocks)
     check(lib.paged_attention_decode(*args), "paged_attention_decode")
     return out
 
@@ -191,6 +197,7 @@ def attention_merge(*a, **k) -> torch.Tensor:
 
 
 def _norm(query, kv_cache, block_tables, context_lens, scale, max_context_len,
-          partition_size=0, out=None, out_dtype=torch.float32, workspace=None):
+          partition_size=0, out=None, out_dtype=torch.float32, workspace=None,
+          shared_blocks=False):
     return (query, kv_cache, block_tables, context_lens, scale, max_context_len, partition_size,
-            out, out_dtype, workspace)
+            out, out_dtype, workspace, shared_blocks)

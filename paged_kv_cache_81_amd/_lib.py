@@ -13,12 +13,13 @@ LIB_PATH = os.environ.get("PKV_LIBRARY", os.path.join(_HERE, "libpagedkv.so"))
 
 PKV_F32 = 0
 PKV_BF16 = 1
+PKV_ATTN_CACHED_KV = 1
 
 STATUS = {0: "PKV_OK", -1: "PKV_ERR_INVALID", -2: "PKV_ERR_UNSUPPORTED",
           -3: "PKV_ERR_WORKSPACE", -4: "PKV_ERR_HIP"}
 
 # every function include/paged_kv.h declares, with its C signature
-_i, _sz, _p, _f = ctypes.c_int, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_float
+_i, _sz, _p, _f, _u = ctypes.c_int, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_float, ctypes.c_uint
 SIGNATURES = {
     "pkv_last_error": (ctypes.c_char_p, []),
     "paged_kv_slot_mapping": (_i, [_p, _p, _i, _p, _p, _i, _i, _i, _i, _p]),
@@ -27,11 +28,11 @@ SIGNATURES = {
     "paged_attention_partition_size": (_i, [_i, _i, _i, _i, _i, _i, _i, _i]),
     "paged_attention_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i, _i, _i]),
     "paged_attention_decode": (_i, [_p, _i, _p, _p, _p, _i, _p, _i, _i, _i, _i, _i, _i, _f,
-                                    _i, _i, _p, _sz, _i, _p]),
+                                    _i, _i, _p, _sz, _i, _u, _p]),
     "paged_attention_partitions": (_i, [_p, _i, _p, _p, _p, _i, _p, _i, _i, _i, _i, _i, _i, _f,
-                                        _i, _i, _p, _sz, _i, _p]),
+                                        _i, _i, _p, _sz, _i, _u, _p]),
     "paged_attention_merge": (_i, [_p, _i, _p, _p, _p, _i, _p, _i, _i, _i, _i, _i, _i, _f,
-                                   _i, _i, _p, _sz, _i, _p]),
+                                   _i, _i, _p, _sz, _i, _u, _p]),
 }
 
 

@@ -55,17 +55,45 @@ bool shape_ok(int S, int Hq, int Hkv, int D, int B, int max_len, pkv_dtype dtype
   return true;
 }
 
+constexpr int kResidentGroups = 512;  // workgroups of the bf16 kernel resident at once (2 per CU)
+
+// (sequence, kv-head group, query-head chunk) work units of the bf16 kernel
+int64_t bf16_units(int S, int Hq, int Hkv) {
+  const int G = Hq / Hkv;
+  return static_cast<int64_t>(S) * (Hkv / bf16_heads_per_group(Hkv)) * ((G + 15) / 16);
+}
+
+// Partition size: a request is checked; 0 picks one.  The bf16 kernel keeps
+// whole sequences in one partition (no merge pass) when there are enough work
+// units to fill the GPU without splitting; otherwise contexts are split into
+// 256-token partitions, short enough that the longest sequence of a ragged
+// batch is spread over many workgroups.  fp32 uses 64-token partitions.
 int resolve_partition(int S, int Hq, int Hkv, int D, int B, int max_len, int req, pkv_dtype dtype) {
-  (void)S; (void)Hq; (void)Hkv; (void)D;
+  (void)D;
   const int unit = partition_unit(B);
   const int cap = dtype == PKV_F32 ? 512 : (1 << 20);
   if (req < 0) return -1;
   if (req > 0) return (req % unit == 0 && req <= cap) ? req : -1;
-  int P = dtype == PKV_F32 ? 256 : 512;
-  P = (P + unit - 1) / unit * unit;
-  if (P > cap) P = unit;
   const int whole = static_cast<int>(cdiv64(std::max(max_len, 1), unit) * unit);
-  return std::min(P, whole);
+  if (dtype == PKV_F32) return std::min(whole, std::max(unit, 64 / unit * unit));
+  if (bf16_units(S, Hq, Hkv) >= kResidentGroups && whole <= (1 << 20)) return whole;
+  return std::min(whole, std::max(unit, 256 / unit * unit));
+}
+
+// Partitions one bf16 workgroup covers.  A small batch of long sequences
+// (at most 32) gets as many per wave as keep one full round of resident
+// workgroups, so each wave streams a long token range; a larger batch gets one
+// per wave, since its lengths may be ragged and a long run on its longest
+// sequence would become the critical path.  Capped by what the waves can hold
+// in LDS until they write it.
+int bf16_parts_per_wg(int S, int Hq, int Hkv, int D, int max_parts) {
+  const int nslot = 4 / bf16_heads_per_group(Hkv);
+  const int64_t units = bf16_units(S, Hq, Hkv);
+  if (S > 32) return nslot;
+  int64_t pps = units * max_parts / (static_cast<int64_t>(kResidentGroups) * nslot);
+  pps = std::max<int64_t>(1, std::min<int64_t>(pps, cdiv64(max_parts, nslot)));
+  while (pps > 1 && bf16_lds_bytes(static_cast<int>(pps), Hq / Hkv, D) > bf16_lds_limit()) --pps;
+  return static_cast<int>(pps) * nslot;
 }
 
 }  // namespace
@@ -181,7 +209,7 @@ int decode_impl(int phases, void* out, pkv_dtype out_dtype, const void* query,
                 const int32_t* context_lens, int num_seqs, int num_q_heads, int num_kv_heads,
                 int head_size, int block_size, int num_blocks, float scale, int max_context_len,
                 int partition_size, void* workspace, size_t workspace_bytes, pkv_dtype dtype,
-                hipStream_t stream) {
+                unsigned flags, hipStream_t stream) {
   clear_error();
   if (!shape_ok(num_seqs, num_q_heads, num_kv_heads, head_size, block_size, max_context_len, dtype))
     return PKV_ERR_INVALID;
@@ -200,6 +228,10 @@ int decode_impl(int phases, void* out, pkv_dtype out_dtype, const void* query,
   }
   if (table_width <= 0 || num_blocks <= 0) { set_error("table_width and num_blocks must be positive"); return PKV_ERR_INVALID; }
   if (!std::isfinite(scale)) { set_error("scale is not finite"); return PKV_ERR_INVALID; }
+  if (flags & ~static_cast<unsigned>(PKV_ATTN_CACHED_KV)) {
+    set_error("unknown flags 0x%x", flags);
+    return PKV_ERR_INVALID;
+  }
   const int G = num_q_heads / num_kv_heads;
   if (static_cast<int64_t>(num_kv_heads) * ((G + 15) / 16) > kGridYZ) {
     set_error("too many kv heads for the grid");
@@ -244,6 +276,10 @@ int decode_impl(int phases, void* out, pkv_dtype out_dtype, const void* query,
   a.max_parts = static_cast<int>(parts);
   a.scale_log2 = scale * 1.4426950408889634f;
   a.out_bf16 = out_dtype == PKV_BF16 ? 1 : 0;
+  a.nontemporal = (flags & PKV_ATTN_CACHED_KV) ? 0 : 1;
+  a.parts_per_wg = dtype == PKV_BF16
+                       ? bf16_parts_per_wg(num_seqs, num_q_heads, num_kv_heads, head_size, a.max_parts)
+                       : 1;
   if (parts > 1) {
     const size_t need = paged_attention_workspace_bytes(num_seqs, num_q_heads, num_kv_heads,
                                                         head_size, block_size, max_context_len,
@@ -274,14 +310,14 @@ int decode_impl(int phases, void* out, pkv_dtype out_dtype, const void* query,
 #define PKV_DECODE_ARGS                                                                        \
   out, out_dtype, query, kv_cache, block_tables, table_width, context_lens, num_seqs,          \
       num_q_heads, num_kv_heads, head_size, block_size, num_blocks, scale, max_context_len,    \
-      partition_size, workspace, workspace_bytes, dtype, stream
+      partition_size, workspace, workspace_bytes, dtype, flags, stream
 
 #define PKV_DECODE_PARAMS                                                                      \
   void *out, pkv_dtype out_dtype, const void *query, const void *kv_cache,                     \
       const int32_t *block_tables, int table_width, const int32_t *context_lens, int num_seqs, \
       int num_q_heads, int num_kv_heads, int head_size, int block_size, int num_blocks,        \
       float scale, int max_context_len, int partition_size, void *workspace,                   \
-      size_t workspace_bytes, pkv_dtype dtype, hipStream_t stream
+      size_t workspace_bytes, pkv_dtype dtype, unsigned flags, hipStream_t stream
 
 extern "C" {
 

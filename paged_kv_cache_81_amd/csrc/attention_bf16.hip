@@ -1,8 +1,13 @@
 // Paged decode attention for bf16 caches on gfx950 matrix cores.
 //
-// Work item: one workgroup (4 waves) per (partition of P tokens, kv head,
-// group of <= 16 query heads, sequence).  The query heads that share a kv head
-// are handled together, so every K/V block is read once per kv head.
+// Work item: one workgroup of 4 waves per (run of partitions of P tokens,
+// group of HG consecutive kv heads, group of <= 16 query heads per kv head,
+// sequence).  Wave w works on kv head (w % HG) of the group and on its own
+// contiguous run of partitions (4/HG runs per workgroup), finishing each
+// partition's softmax statistics as it crosses into the next.  All query heads sharing a kv head are handled by its
+// wave, so every K/V block is read once per kv head; the HG waves of a group
+// walk the same tokens together, so each cached row is read as HG*D*2
+// contiguous bytes (>= 1 KB for HG = 4, D = 128) rather than one head's piece.
 //
 // A wave step covers 32 tokens as two 16-token tiles.  Lane l is (j, g) with
 // j = l % 16 and g = l / 16.
@@ -22,8 +27,12 @@
 //    8 x NV transpose of bf16 pairs in registers (v_perm_b32).
 //  * P is split into bf16 hi + lo parts, so P.V keeps ~16 mantissa bits of
 //    the fp32 weights; accumulation is fp32.
-//  * The 4 waves' (m, l, O) are merged through LDS; the workgroup writes the
-//    normalised output (single partition) or its partition statistics.
+//  * Block-table entries are loaded once per wave (one per lane) and read back
+//    as scalars; each wave keeps two steps of K/V in registers, so the next
+//    step's loads are in flight while the current one computes.
+//  * Each wave writes its results from registers: the normalised output when
+//    the sequence is one partition, else per partition the statistics
+//    (max score, exponent sum, normalised partial output) for the merge kernel.
 #include "common.hpp"
 
 #include <cmath>
@@ -43,60 +52,122 @@ struct Words {
   uint32_t w[NW];
 };
 
-template <int NW>
+// Cached K/V is streamed once per kv head: read it with nontemporal loads,
+// which keep it from displacing other lines in L2 and the memory-side cache
+// and sustain a higher HBM read rate than ordinary loads.
+template <bool NT, typename T>
+__device__ __forceinline__ T ld(const T* p) {
+  if constexpr (NT) return __builtin_nontemporal_load(p);
+  else return *p;
+}
+
+template <int NW, bool NT>
 __device__ __forceinline__ Words<NW> load_words(const uint16_t* p) {
   Words<NW> r;
   if constexpr (NW == 4) {
-    const u32x4 v = *reinterpret_cast<const u32x4*>(p);
+    const u32x4 v = ld<NT>(reinterpret_cast<const u32x4*>(p));
     r.w[0] = v.x; r.w[1] = v.y; r.w[2] = v.z; r.w[3] = v.w;
   } else {
     static_assert(NW == 2, "unsupported");
-    const u32x2 v = *reinterpret_cast<const u32x2*>(p);
+    const u32x2 v = ld<NT>(reinterpret_cast<const u32x2*>(p));
     r.w[0] = v.x; r.w[1] = v.y;
   }
   return r;
 }
 
+template <bool NT>
 __device__ __forceinline__ bf16x8 load_bf16x8(const uint16_t* p) {
-  return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
+  return __builtin_bit_cast(bf16x8, ld<NT>(reinterpret_cast<const u32x4*>(p)));
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-template <int D, int B>
-__global__ void __launch_bounds__(kThreads) attention_bf16_kernel(AttnArgs a) {
+template <int D, int B, int HG, bool NT>
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
+attention_bf16_kernel(AttnArgs a) {
   constexpr int QC = D / 32;  // score MFMAs per tile (32 dims each)
   constexpr int NV = D / 16;  // output blocks of 16 rows; dims per lane per V token
   constexpr int NW = NV / 2;  // 32-bit words per lane per V token
-  constexpr int LDS_ROW = D + 4;
+  constexpr int NSLOT = kWaves / HG;  // waves per kv head, each on its own partitions
 
-  __shared__ float s_o[kWaves][16][LDS_ROW];
-  __shared__ float s_m[kWaves][16];
-  __shared__ float s_l[kWaves][16];
-  __shared__ int s_bad;
+  // Finished partitions stay in LDS until the wave has read its last K/V:
+  // a global store issued between the loads would make the following waits
+  // for those loads also wait for the store to be acknowledged.  Per wave:
+  // pps partitions x nhs heads of SROW floats, then their (m, l) pairs.
+  constexpr int SROW = D + 4;  // padded head row (floats)
+  extern __shared__ float s_dyn[];
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
   const int j = lane & 15;
   const int g = lane >> 4;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int hi = wv % HG;    // kv head inside the group
+  const int slot = wv / HG;  // which run of partitions
 
   const int G = a.Hq / a.Hkv;
   const int chunks = (G + 15) >> 4;
-  const int part = blockIdx.x;
-  const int kvh = blockIdx.y / chunks;
-  const int chunk = blockIdx.y - kvh * chunks;
+  const int hg = blockIdx.y / chunks;
+  const int chunk = blockIdx.y - hg * chunks;
   const int s = blockIdx.z;
+  const int kvh = hg * HG + hi;
+  const int nh = min(16, G - chunk * 16);
+  const int h0 = kvh * G + chunk * 16;
 
   const int L = a.lens[s];
   const int P = a.partition;
   const int nparts = L > 0 ? (L + P - 1) / P : 1;
   const bool bad_seq = L < 0 || (L + B - 1) / B > a.width || nparts > a.max_parts;
-  if (part > 0 && (bad_seq || part >= nparts)) return;
+  // without a workspace (one partition per sequence) results always go to out
+  const bool single = nparts == 1 || a.max_parts == 1;
+  // this workgroup covers partitions [p_first, p_first + parts_per_wg); the
+  // wave covers a contiguous run of pps of them, i.e. one token range
+  const int pps = a.parts_per_wg / NSLOT;
+  const int p_first = blockIdx.x * a.parts_per_wg + slot * pps;
+  if (p_first >= nparts) return;  // (partition 0 always exists)
 
-  const int nh = min(16, G - chunk * 16);
-  const int h0 = kvh * G + chunk * 16;
+  // LDS of this wave: rows [i][hh][SROW] for its i-th partition, then (m, l)
+  const int nhs = min(16, G);  // head rows per partition slot
+  float* stage = s_dyn + static_cast<int64_t>(wv) * bf16_lds_wave_floats(pps, G, D);
+  float* stage_ml = stage + pps * nhs * SROW;  // 16-byte aligned: SROW % 4 == 0
 
-  if (threadIdx.x == 0) s_bad = bad_seq ? 1 : 0;
+  // Write partition p_first + i of heads h0 .. h0+nh-1 from the wave's LDS:
+  // the normalised output (single partition) into out, else the partial
+  // output and (m, l) into the workspace, whose layout [s][p][h][D] keeps a
+  // wave's heads adjacent.  Each store instruction covers 64 consecutive
+  // 16-byte pieces.
+  auto store_rows = [&](int i) {
+    const int p = p_first + i;
+    const float* src = stage + i * nhs * SROW;
+    constexpr int D4 = D / 4;
+    const int64_t row0 = single ? static_cast<int64_t>(s) * a.Hq + h0
+                                : (static_cast<int64_t>(s) * a.max_parts + p) * a.Hq + h0;
+    for (int e = lane; e < nh * D4; e += 64) {
+      const int hh = e / D4;
+      const int d = (e - hh * D4) * 4;
+      const float4 o = *reinterpret_cast<const float4*>(src + hh * SROW + d);
+      const int64_t off = row0 * D + static_cast<int64_t>(e) * 4;
+      if (single && a.out_bf16) {
+        const uint32_t lo = f32_to_bf16(o.x) | (static_cast<uint32_t>(f32_to_bf16(o.y)) << 16);
+        const uint32_t hi2 = f32_to_bf16(o.z) | (static_cast<uint32_t>(f32_to_bf16(o.w)) << 16);
+        *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(a.out) + off) = u32x2{lo, hi2};
+      } else {
+        *reinterpret_cast<float4*>((single ? static_cast<float*>(a.out) : a.ws_o) + off) = o;
+      }
+    }
+    if (!single && lane < nh)
+      *reinterpret_cast<float2*>(a.ws_ml + 2 * (row0 + lane)) =
+          *reinterpret_cast<const float2*>(stage_ml + 2 * (i * nhs + lane));
+  };
+
+  if (bad_seq) {
+    // the merge kernel poisons split sequences itself
+    if (single) {
+      for (int i = lane; i < nh * SROW; i += 64) stage[i] = NAN;
+      __builtin_amdgcn_wave_barrier();
+      store_rows(0);
+    }
+    return;
+  }
 
   // query fragments: q[s][h0 + j][32c + 8g .. +8]
   bf16x8 qf[QC];
@@ -105,73 +176,117 @@ __global__ void __launch_bounds__(kThreads) attention_bf16_kernel(AttnArgs a) {
                          (static_cast<int64_t>(s) * a.Hq + h0 + j) * D + 8 * g;
 #pragma unroll
     for (int c = 0; c < QC; ++c)
-      qf[c] = (j < nh) ? load_bf16x8(qp + 32 * c) : bf16x8{};
+      qf[c] = (j < nh) ? load_bf16x8<false>(qp + 32 * c) : bf16x8{};
   }
 
-  const int t_begin = part * P;
-  const int t_end = bad_seq ? t_begin : min(L, t_begin + P);
-  const int nsteps = (t_end - t_begin + kStep - 1) / kStep;
+  const int tw_begin = p_first * P;
+  const int tw_end = min(L, (p_first + pps) * P);
+  const int my_steps = (tw_end - tw_begin + kStep - 1) / kStep;  // 0 only when L == 0
 
   const int64_t row = static_cast<int64_t>(a.Hkv) * D;  // elements between slots
   const uint16_t* kbase = static_cast<const uint16_t*>(a.kv) + static_cast<int64_t>(kvh) * D;
   const uint16_t* vbase = kbase + static_cast<int64_t>(a.NB) * B * row;
   const int32_t* trow = a.tables + static_cast<int64_t>(s) * a.width;
-  const int koff = j * static_cast<int>(row) + 8 * g;
-  int voff[4];
+  // per-lane byte offsets inside a 16-token tile (unsigned 32-bit, so a load is
+  // scalar base + vector offset)
+  const uint32_t koff = (j * static_cast<uint32_t>(row) + 8 * g) * 2u;
+  uint32_t voff[4];
 #pragma unroll
-  for (int r = 0; r < 4; ++r) voff[r] = (4 * g + r) * static_cast<int>(row) + NV * j;
+  for (int r = 0; r < 4; ++r) voff[r] = ((4 * g + r) * static_cast<uint32_t>(row) + NV * j) * 2u;
+
+  // Block-table window: lane l holds the physical block of tile (l & 1) of
+  // step q0 + (l >> 1), so 32 steps need one load; per step the entries are
+  // read back as scalars.
+  auto load_window = [&](int q0) -> int {
+    const int tt = tw_begin + (q0 + (lane >> 1)) * kStep + 16 * (lane & 1);
+    return tt < tw_end ? trow[tt / B] : -1;
+  };
+  int win_q0 = 0;
+  int win = load_window(0);
+  asm volatile("" ::"v"(win));
+
+  struct Step {
+    bf16x8 k[2][QC];
+    Words<NW> v[2][4];
+    bool bad;  // a table entry of this step is out of range
+  };
+  bool bad_blk = false;  // ... of some step of the current partition
+
+  // issue the loads of step q (tokens tw_begin + 32q ..).  The same 16 loads
+  // are issued on every path, so the compiler can wait for exactly one
+  // buffer's loads: a tile past the end of the run, or whose table entry is
+  // out of range, reads block 0 instead (always in the pool); its scores are
+  // masked and its values zeroed in compute(), or its partition poisoned.
+  auto issue = [&](Step& d, int q) {
+    if (q - win_q0 >= 32) {
+      win_q0 = q;
+      win = load_window(q);
+      // wait for the entries here: a load still pending where the paths join
+      // would make every step wait for all outstanding K/V loads
+      asm volatile("" ::"v"(win));
+    }
+    const int ts = tw_begin + q * kStep;
+    d.bad = false;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int tt = ts + 16 * u;
+      const int phys = __builtin_amdgcn_readlane(win, 2 * (q - win_q0) + u);
+      const bool in_range = phys >= 0 && phys < a.NB;
+      d.bad = d.bad || (tt < tw_end && !in_range);
+      const int blk = (tt < tw_end && in_range) ? phys : 0;
+      const int64_t base = (static_cast<int64_t>(blk) * B + (tt % B)) * row;
+      const char* kp = reinterpret_cast<const char*>(kbase + base);
+      const char* vp = reinterpret_cast<const char*>(vbase + base);
+#pragma unroll
+      for (int c = 0; c < QC; ++c)
+        d.k[u][c] = load_bf16x8<NT>(reinterpret_cast<const uint16_t*>(kp + koff + 64 * c));
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        d.v[u][r] = load_words<NW, NT>(reinterpret_cast<const uint16_t*>(vp + voff[r]));
+    }
+  };
 
   float m_run = -INFINITY;
   float l_run = 0.f;
   f32x4 acc[NV];
 #pragma unroll
   for (int n = 0; n < NV; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
-  bool bad_blk = false;
 
-  for (int st = wave; st < nsteps; st += kWaves) {
-    const int ts = t_begin + st * kStep;
-
-    // block of each 16-token tile (uniform across the wave)
-    int64_t tile_base[2];
-    bool tile_ok[2];
+  // keep partition p's result in LDS and start the next partition afresh.
+  // lane (j, g) holds head j, dims NV*(4g + r) + n
+  auto finalize = [&](int p) {
+    float lsum = l_run + __shfl_xor(l_run, 16, 64);
+    lsum += __shfl_xor(lsum, 32, 64);
+    const bool bad = bad_blk;
+    const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+    const int i = p - p_first;
+    if (j < nh) {
+      float* dst = stage + (i * nhs + j) * SROW;
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int tt = ts + 16 * u;
-      tile_ok[u] = tt < t_end;
-      tile_base[u] = 0;
-      if (tile_ok[u]) {
-        const int phys = trow[tt / B];
-        if (phys < 0 || phys >= a.NB) {
-          bad_blk = true;
-          tile_ok[u] = false;
-        } else {
-          tile_base[u] = (static_cast<int64_t>(phys) * B + (tt % B)) * row;
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int n0 = 0; n0 < NV; n0 += 4) {
+          float4 o = make_float4(acc[n0][r] * inv, acc[n0 + 1][r] * inv, acc[n0 + 2][r] * inv,
+                                 acc[n0 + 3][r] * inv);
+          if (bad) o = make_float4(NAN, NAN, NAN, NAN);
+          *reinterpret_cast<float4*>(dst + NV * (4 * g + r) + n0) = o;
         }
-      }
+      if (g == 0)
+        *reinterpret_cast<float2*>(stage_ml + 2 * (i * nhs + j)) =
+            make_float2(bad ? NAN : m_run, bad ? NAN : lsum);
     }
+    m_run = -INFINITY;
+    l_run = 0.f;
+#pragma unroll
+    for (int n = 0; n < NV; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+    bad_blk = false;
+  };
 
-    // K tiles (A operand): token j of the tile, dims 32c + 8g .. +8
-    bf16x8 kf[2][QC];
-#pragma unroll
-    for (int u = 0; u < 2; ++u)
-#pragma unroll
-      for (int c = 0; c < QC; ++c)
-        kf[u][c] = tile_ok[u] ? load_bf16x8(kbase + tile_base[u] + koff + 32 * c) : bf16x8{};
-
-    // V pieces: token 4g + r of tile u, dims NV*j .. NV*j + NV - 1; zero past the end
-    Words<NW> vr[2][4];
-#pragma unroll
-    for (int u = 0; u < 2; ++u)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const bool ok = tile_ok[u] && (ts + 16 * u + 4 * g + r < t_end);
-        if (ok) {
-          vr[u][r] = load_words<NW>(vbase + tile_base[u] + voff[r]);
-        } else {
-#pragma unroll
-          for (int w = 0; w < NW; ++w) vr[u][r].w[w] = 0u;
-        }
-      }
+  auto compute = [&](Step& d, int q) {
+    const int ts = tw_begin + q * kStep;
+    if (q > 0 && ts % P == 0) finalize(ts / P - 1);  // a new partition starts here
+    bad_blk = bad_blk || d.bad;
+    const int lim = tw_end - ts;  // valid tokens in this step (>= 1)
 
     // scores
     float x[2][4];
@@ -180,12 +295,20 @@ __global__ void __launch_bounds__(kThreads) attention_bf16_kernel(AttnArgs a) {
       f32x4 sc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int c = 0; c < QC; ++c)
-        sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[u][c], qf[c], sc, 0, 0, 0);
+        sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(d.k[u][c], qf[c], sc, 0, 0, 0);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const bool ok = tile_ok[u] && (ts + 16 * u + 4 * g + r < t_end);
-        x[u][r] = ok ? sc[r] * a.scale_log2 : -INFINITY;
-      }
+      for (int r = 0; r < 4; ++r) x[u][r] = sc[r] * a.scale_log2;
+    }
+    if (lim < kStep) {  // the sequence ends inside this step: mask scores, zero values
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (16 * u + 4 * g + r >= lim) {
+            x[u][r] = -INFINITY;
+#pragma unroll
+            for (int w = 0; w < NW; ++w) d.v[u][r].w[w] = 0u;
+          }
     }
 
     // online softmax (log2 domain), per head j
@@ -221,9 +344,9 @@ __global__ void __launch_bounds__(kThreads) attention_bf16_kernel(AttnArgs a) {
       const uint32_t sel = (n & 1) ? 0x07060302u : 0x05040100u;
       u32x4 va;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int e0 = 2 * q, e1 = 2 * q + 1;  // token slots (u = e/4, r = e%4)
-        va[q] = __builtin_amdgcn_perm(vr[e1 >> 2][e1 & 3].w[n >> 1], vr[e0 >> 2][e0 & 3].w[n >> 1], sel);
+      for (int e = 0; e < 4; ++e) {
+        const int e0 = 2 * e, e1 = 2 * e + 1;  // token slots (u = e/4, r = e%4)
+        va[e] = __builtin_amdgcn_perm(d.v[e1 >> 2][e1 & 3].w[n >> 1], d.v[e0 >> 2][e0 & 3].w[n >> 1], sel);
       }
       const bf16x8 vb = __builtin_bit_cast(bf16x8, va);
       f32x4 o = acc[n] * alpha;
@@ -231,83 +354,60 @@ __global__ void __launch_bounds__(kThreads) attention_bf16_kernel(AttnArgs a) {
       o = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vb, plo, o, 0, 0, 0);
       acc[n] = o;
     }
-  }
+  };
 
-  // per-head sum over the four lane groups
-  l_run += __shfl_xor(l_run, 16, 64);
-  l_run += __shfl_xor(l_run, 32, 64);
-
-  __syncthreads();  // s_bad initialised
-  if (bad_blk) s_bad = 1;
-  if (g == 0) {
-    s_m[wave][j] = m_run;
-    s_l[wave][j] = l_run;
+  // two register buffers: the next step's loads are in flight while the
+  // current step computes (also across partition boundaries)
+  Step bufA, bufB;
+  if (my_steps > 0) issue(bufA, 0);
+  for (int q = 0; q < my_steps; q += 2) {
+    if (q + 1 < my_steps) issue(bufB, q + 1);
+    compute(bufA, q);
+    if (q + 1 >= my_steps) break;
+    if (q + 2 < my_steps) issue(bufA, q + 2);
+    compute(bufB, q + 1);
   }
-  // lane (j, g) holds head j, dims NV*(4g + r) + n
-#pragma unroll
-  for (int r = 0; r < 4; ++r)
-#pragma unroll
-    for (int n = 0; n < NV; ++n) s_o[wave][j][NV * (4 * g + r) + n] = acc[n][r];
-  __syncthreads();
+  // the last partition (or, for an empty sequence, its zero output)
+  const int p_last = my_steps > 0 ? (tw_begin + (my_steps - 1) * kStep) / P : p_first;
+  finalize(p_last);
+  __builtin_amdgcn_wave_barrier();
+  for (int i = 0; i <= p_last - p_first; ++i) store_rows(i);
+}
 
-  const bool bad = s_bad != 0;
-  // without a workspace (one partition per sequence) results always go to out
-  const bool single = nparts == 1 || a.max_parts == 1;
-  constexpr int D4 = D / 4;
-  for (int idx = threadIdx.x; idx < nh * D4; idx += kThreads) {
-    const int hh = idx / D4;
-    const int d = (idx - hh * D4) * 4;
-    float M = s_m[0][hh];
-#pragma unroll
-    for (int w = 1; w < kWaves; ++w) M = fmaxf(M, s_m[w][hh]);
-    const float Mu = (M == -INFINITY) ? 0.f : M;
-    float lsum = 0.f;
-    float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      const float sc = fast_exp2(s_m[w][hh] - Mu);
-      lsum += sc * s_l[w][hh];
-      o.x += sc * s_o[w][hh][d + 0];
-      o.y += sc * s_o[w][hh][d + 1];
-      o.z += sc * s_o[w][hh][d + 2];
-      o.w += sc * s_o[w][hh][d + 3];
+template <int D, int B, int HG, bool NT>
+int launch_one(const AttnArgs& a, dim3 grid, size_t lds, hipStream_t stream) {
+  auto kern = attention_bf16_kernel<D, B, HG, NT>;
+  static bool attr_set = false;  // allow dynamic LDS up to the per-workgroup maximum
+  if (!attr_set) {
+    if (hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                            hipFuncAttributeMaxDynamicSharedMemorySize,
+                            static_cast<int>(bf16_lds_limit())) != hipSuccess) {
+      set_error("paged attention (bf16): cannot raise the LDS limit");
+      return PKV_ERR_HIP;
     }
-    const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
-    o.x *= inv; o.y *= inv; o.z *= inv; o.w *= inv;
-    if (bad) {
-      o = make_float4(NAN, NAN, NAN, NAN);
-      M = NAN;
-      lsum = NAN;
-    }
-    const int h = h0 + hh;
-    if (single) {
-      const int64_t off = (static_cast<int64_t>(s) * a.Hq + h) * D + d;
-      if (a.out_bf16) {
-        uint16_t* op = static_cast<uint16_t*>(a.out) + off;
-        const uint32_t lo = f32_to_bf16(o.x) | (static_cast<uint32_t>(f32_to_bf16(o.y)) << 16);
-        const uint32_t hi = f32_to_bf16(o.z) | (static_cast<uint32_t>(f32_to_bf16(o.w)) << 16);
-        *reinterpret_cast<u32x2*>(op) = u32x2{lo, hi};
-      } else {
-        *reinterpret_cast<float4*>(static_cast<float*>(a.out) + off) = o;
-      }
-    } else {
-      const int64_t sp = (static_cast<int64_t>(s) * a.Hq + h) * a.max_parts + part;
-      *reinterpret_cast<float4*>(a.ws_o + sp * D + d) = o;
-      if (d == 0) {
-        a.ws_ml[2 * sp] = M;
-        a.ws_ml[2 * sp + 1] = lsum;
-      }
-    }
+    attr_set = true;
   }
+  kern<<<grid, dim3(kThreads), lds, stream>>>(a);
+  return check_launch("paged attention (bf16)");
 }
 
 template <int D, int B>
 int launch(const AttnArgs& a, hipStream_t stream) {
   const int G = a.Hq / a.Hkv;
   const int chunks = (G + 15) / 16;
-  dim3 grid(a.max_parts, a.Hkv * chunks, a.S);
-  attention_bf16_kernel<D, B><<<grid, dim3(kThreads), 0, stream>>>(a);
-  return check_launch("paged attention (bf16)");
+  const int HG = bf16_heads_per_group(a.Hkv);
+  dim3 grid((a.max_parts + a.parts_per_wg - 1) / a.parts_per_wg, (a.Hkv / HG) * chunks, a.S);
+  const size_t lds = bf16_lds_bytes(a.parts_per_wg / (4 / HG), G, D);
+  if (lds > bf16_lds_limit()) {
+    set_error("paged attention (bf16): %zu bytes of LDS needed", lds);
+    return PKV_ERR_UNSUPPORTED;
+  }
+  const bool nt = a.nontemporal != 0;
+  if (HG == 4)
+    return nt ? launch_one<D, B, 4, true>(a, grid, lds, stream) : launch_one<D, B, 4, false>(a, grid, lds, stream);
+  if (HG == 2)
+    return nt ? launch_one<D, B, 2, true>(a, grid, lds, stream) : launch_one<D, B, 2, false>(a, grid, lds, stream);
+  return nt ? launch_one<D, B, 1, true>(a, grid, lds, stream) : launch_one<D, B, 1, false>(a, grid, lds, stream);
 }
 
 }  // namespace

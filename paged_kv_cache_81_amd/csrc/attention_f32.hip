@@ -21,6 +21,7 @@ __global__ void __launch_bounds__(64) attention_f32_kernel(AttnArgs a) {
   constexpr int PER = D / 64;  // output dims per lane
   __shared__ float s_q[kMaxHeads][D];
   __shared__ float s_p[kMaxHeads][kMaxPart];
+  __shared__ int s_phys[kMaxPart];  // physical block of each token of the partition
 
   const int lane = threadIdx.x;
   const int G = a.Hq / a.Hkv;
@@ -57,6 +58,7 @@ __global__ void __launch_bounds__(64) attention_f32_kernel(AttnArgs a) {
   for (int i = lane; i < n; i += 64) {
     const int t = t_begin + i;
     const int phys = trow[t / B];
+    s_phys[i] = phys;
     float dot[kMaxHeads];
 #pragma unroll
     for (int h = 0; h < kMaxHeads; ++h) dot[h] = 0.f;
@@ -112,21 +114,33 @@ __global__ void __launch_bounds__(64) attention_f32_kernel(AttnArgs a) {
   for (int h = 0; h < kMaxHeads; ++h)
 #pragma unroll
     for (int e = 0; e < PER; ++e) acc[h][e] = 0.f;
-  for (int i = 0; i < n; ++i) {
-    const int t = t_begin + i;
-    const int phys = trow[t / B];
-    if (phys < 0 || phys >= a.NB) continue;  // flagged in phase 1
-    const float* vr = vbase + (static_cast<int64_t>(phys) * B + t % B) * row + lane * PER;
-    float v[PER];
+  // 16 tokens per batch: their value loads are all in flight together
+  constexpr int kBatch = 16;
+  for (int i0 = 0; i0 < n; i0 += kBatch) {
+    float v[kBatch][PER];
 #pragma unroll
-    for (int e = 0; e < PER; ++e) v[e] = vr[e];
+    for (int k = 0; k < kBatch; ++k) {
+      const int i = i0 + k;
+      const int phys = i < n ? s_phys[i] : -1;
 #pragma unroll
-    for (int h = 0; h < kMaxHeads; ++h)
-      if (h < nh) {
-        const float p = s_p[h][i];
+      for (int e = 0; e < PER; ++e) v[k][e] = 0.f;
+      if (phys >= 0 && phys < a.NB) {  // a bad block was flagged in phase 1
+        const float* vr = vbase + (static_cast<int64_t>(phys) * B + (t_begin + i) % B) * row + lane * PER;
 #pragma unroll
-        for (int e = 0; e < PER; ++e) acc[h][e] = fmaf(p, v[e], acc[h][e]);
+        for (int e = 0; e < PER; ++e) v[k][e] = vr[e];
       }
+    }
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) {
+      if (i0 + k >= n) break;
+#pragma unroll
+      for (int h = 0; h < kMaxHeads; ++h)
+        if (h < nh) {
+          const float p = s_p[h][i0 + k];
+#pragma unroll
+          for (int e = 0; e < PER; ++e) acc[h][e] = fmaf(p, v[k][e], acc[h][e]);
+        }
+    }
   }
 
   // any lane that saw a bad block poisons the whole work item
@@ -149,7 +163,7 @@ __global__ void __launch_bounds__(64) attention_f32_kernel(AttnArgs a) {
         else
           static_cast<float*>(a.out)[off] = o;
       } else {
-        const int64_t sp = (static_cast<int64_t>(s) * a.Hq + hq) * a.max_parts + part;
+        const int64_t sp = (static_cast<int64_t>(s) * a.max_parts + part) * a.Hq + hq;
         a.ws_o[sp * D + d] = o;
         if (d == 0) {
           a.ws_ml[2 * sp] = bad ? NAN : m[h];

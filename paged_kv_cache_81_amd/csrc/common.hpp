@@ -62,8 +62,8 @@ int launch_gather(void* k_out, void* v_out, const void* kv, const int32_t* table
 
 struct AttnArgs {
   void* out;          // [S][Hq][D] fp32 or bf16
-  float* ws_o;        // [S][Hq][max_parts][D]   (split path only)
-  float* ws_ml;       // [S][Hq][max_parts][2]   (m in log2 units, l)
+  float* ws_o;        // [S][max_parts][Hq][D]   (split path only)
+  float* ws_ml;       // [S][max_parts][Hq][2]   (m in log2 units, l)
   const void* query;  // [S][Hq][D]
   const void* kv;     // [2][NB][B][Hkv][D]
   const int32_t* tables;
@@ -73,7 +73,25 @@ struct AttnArgs {
   int max_parts;      // partitions the grid covers per sequence
   float scale_log2;   // scale * log2(e)
   int out_bf16;
+  int nontemporal;    // stream K/V past the caches
+  int parts_per_wg;   // partitions one workgroup covers (bf16 path)
 };
+
+// kv heads per bf16 workgroup: 4 when they divide Hkv, else 2, else 1
+inline int bf16_heads_per_group(int Hkv) { return Hkv % 4 == 0 ? 4 : (Hkv % 2 == 0 ? 2 : 1); }
+
+// LDS of one bf16 workgroup: for each of its 4 waves, pps partition slots of
+// min(16, G) head rows (D + 4 floats), then an (m, l) pair per row, padded
+// to a multiple of 4 floats so every wave's area stays 16-byte aligned.
+__host__ __device__ inline int bf16_lds_wave_floats(int pps, int G, int D) {
+  const int nhs = G < 16 ? G : 16;
+  return pps * nhs * (D + 4) + (pps * nhs * 2 + 3) / 4 * 4;
+}
+inline size_t bf16_lds_bytes(int pps, int G, int D) {
+  return static_cast<size_t>(4) * bf16_lds_wave_floats(pps, G, D) * sizeof(float);
+}
+// at most this much, so that two workgroups fit in a CU's 160 KB
+inline size_t bf16_lds_limit() { return 76 * 1024; }
 
 int launch_attention_bf16(const AttnArgs& a, hipStream_t stream);
 int launch_attention_f32(const AttnArgs& a, hipStream_t stream);

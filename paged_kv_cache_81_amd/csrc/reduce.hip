@@ -1,7 +1,8 @@
 // Log-sum-exp merge of context partitions.
 //
 // For each (sequence, query head) split into n > 1 partitions with statistics
-// (m_p, l_p, o_p) -- m in log2 units, o normalised -- the output is
+// (m_p, l_p, o_p) -- m in log2 units, o normalised, stored in the workspace
+// as rows [s][p][h] -- the output is
 //     M = max_p m_p,  w_p = l_p * 2^(m_p - M),  out = sum_p w_p o_p / sum_p w_p.
 // One wave per (sequence, head); sequences held in one partition were written
 // by the attention kernel directly and are skipped here.
@@ -31,15 +32,19 @@ __global__ void __launch_bounds__(64) reduce_kernel(AttnArgs a) {
 #pragma unroll
     for (int e = 0; e < PER; ++e) res[e] = NAN;
   } else {
-    const float* ml = a.ws_ml + static_cast<int64_t>(sh) * a.max_parts * 2;
-    const float* o = a.ws_o + static_cast<int64_t>(sh) * a.max_parts * D + lane * PER;
+    // workspace rows are [s][p][h]: partition p of (s, h) is row (s*P + p)*Hq + h
+    const int h = sh - s * a.Hq;
+    const int64_t pstride = a.Hq;  // rows between consecutive partitions
+    const int64_t row0 = static_cast<int64_t>(s) * a.max_parts * a.Hq + h;
+    const float* ml = a.ws_ml + 2 * row0;
+    const float* o = a.ws_o + row0 * D + lane * PER;
     float M = -INFINITY;
-    for (int p = lane; p < n; p += 64) M = fmaxf(M, ml[2 * p]);
+    for (int p = lane; p < n; p += 64) M = fmaxf(M, ml[2 * pstride * p]);
     M = wave_max(M);
     const float Mu = (M == -INFINITY) ? 0.f : M;
     float den = 0.f;
     for (int p = lane; p < n; p += 64) {
-      const float w = ml[2 * p + 1] * __builtin_amdgcn_exp2f(ml[2 * p] - Mu);
+      const float w = ml[2 * pstride * p + 1] * __builtin_amdgcn_exp2f(ml[2 * pstride * p] - Mu);
       s_w[p] = w;
       den += w;
     }
@@ -54,13 +59,13 @@ __global__ void __launch_bounds__(64) reduce_kernel(AttnArgs a) {
       for (int k = 0; k < 4; ++k) {
         const float w = s_w[p + k];
 #pragma unroll
-        for (int e = 0; e < PER; ++e) acc[e] = fmaf(w, o[static_cast<int64_t>(p + k) * D + e], acc[e]);
+        for (int e = 0; e < PER; ++e) acc[e] = fmaf(w, o[(p + k) * pstride * D + e], acc[e]);
       }
     }
     for (; p < n; ++p) {
       const float w = s_w[p];
 #pragma unroll
-      for (int e = 0; e < PER; ++e) acc[e] = fmaf(w, o[static_cast<int64_t>(p) * D + e], acc[e]);
+      for (int e = 0; e < PER; ++e) acc[e] = fmaf(w, o[p * pstride * D + e], acc[e]);
     }
     const float inv = 1.f / den;
 #pragma unroll

@@ -90,11 +90,15 @@ def run_write_step(st: DeviceStep) -> None:
     pkv.write(st.new_k, st.new_v, st.kv, st.new_slots)
 
 
-def attend(st: DeviceStep, partition_size=None, out_dtype=torch.float32) -> torch.Tensor:
+def attend(st: DeviceStep, partition_size=None, out_dtype=torch.float32,
+           shared_blocks=None) -> torch.Tensor:
+    """Decode attention over the device step; workloads that alias blocks
+    across sequences read K/V through the caches unless told otherwise."""
     w = st.w
     P = w.partition_size if partition_size is None else partition_size
+    shared = bool(w.meta.get("forks")) if shared_blocks is None else shared_blocks
     return pkv.attention_decode(st.query, st.kv, st.tables, st.lens, w.scale, w.max_context_len,
-                                partition_size=P, out_dtype=out_dtype)
+                                partition_size=P, out_dtype=out_dtype, shared_blocks=shared)
 
 
 def row_rel_err(got: np.ndarray, ref: np.ndarray) -> np.ndarray:

@@ -50,10 +50,16 @@ def lib():
 
 def test_partition_choice(lib):
     F32, BF16 = 0, 1
-    # automatic: one partition for short contexts, 512 tokens otherwise
+    # automatic: one partition for short contexts, 256 tokens otherwise ...
     assert lib.paged_attention_partition_size(4, 8, 2, 128, 16, 100, 0, BF16) == 128
-    assert lib.paged_attention_partition_size(4, 8, 2, 128, 16, 32768, 0, BF16) == 512
+    assert lib.paged_attention_partition_size(4, 8, 2, 128, 16, 32768, 0, BF16) == 256
     assert lib.paged_attention_partition_size(4, 8, 2, 128, 16, 0, 0, BF16) == 32
+    # ... unless the batch alone has enough (sequence, kv-head group) work
+    # units to fill the GPU: 64 sequences x 10 groups of 4 kv heads
+    assert lib.paged_attention_partition_size(64, 40, 40, 128, 16, 2034, 0, BF16) == 2048
+    assert lib.paged_attention_partition_size(8, 40, 40, 128, 16, 2034, 0, BF16) == 256
+    assert lib.paged_attention_partition_size(4, 8, 2, 64, 16, 1000, 0, F32) == 64
+    assert lib.paged_attention_partition_size(4, 8, 2, 64, 48, 1000, 0, F32) == 96
     # requests must be whole 32-token steps and whole blocks
     assert lib.paged_attention_partition_size(4, 8, 2, 128, 16, 9999, 96, BF16) == 96
     assert lib.paged_attention_partition_size(4, 8, 2, 128, 64, 9999, 96, BF16) == -1
@@ -78,14 +84,14 @@ def test_host_checks_reject_bad_arguments(lib):
     BF16 = 1
     args = dict(out=p, out_dtype=0, query=p, kv=p, tables=p, width=4, lens=p, S=2, Hq=8, Hkv=2,
                 D=128, B=16, NB=10, scale=0.1, max_len=64, P=0, ws=None, ws_bytes=0, dtype=BF16,
-                stream=None)
+                flags=0, stream=None)
 
     def call(**kw):
         a = dict(args, **kw)
         return lib.paged_attention_decode(a["out"], a["out_dtype"], a["query"], a["kv"], a["tables"],
                                           a["width"], a["lens"], a["S"], a["Hq"], a["Hkv"], a["D"],
                                           a["B"], a["NB"], a["scale"], a["max_len"], a["P"], a["ws"],
-                                          a["ws_bytes"], a["dtype"], a["stream"])
+                                          a["ws_bytes"], a["dtype"], a["flags"], a["stream"])
     assert call(D=96) == -2
     assert call(B=8) == -2                      # bf16 blocks of 8 are not built
     assert call(Hq=7) == -1
@@ -94,6 +100,7 @@ def test_host_checks_reject_bad_arguments(lib):
     assert call(P=48) == -1
     assert call(scale=float("nan")) == -1
     assert call(max_len=4096, P=512) == -3      # needs a workspace
+    assert call(flags=2) == -1                  # unknown flag
     assert call(S=0) == 0                        # nothing to do
     assert b"workspace" in lib.pkv_last_error() or lib.pkv_last_error() == b""
     assert lib.paged_kv_write(p, p, p, p, 0, 10, 16, 2, 128, BF16, None) == 0

@@ -242,6 +242,28 @@ def test_shared_prefix_aliasing_is_bit_identical():
     assert np.array_equal(shared.view(np.uint32), private.view(np.uint32))
 
 
+@pytest.mark.parametrize("name", ["shared_prefix", "qwen2_gqa"])
+def test_cached_and_streamed_loads_agree_bit_for_bit(name):
+    w = SMALL[name]()
+    st = H.upload(w)
+    a = H.attend(st, shared_blocks=False).cpu().numpy()
+    b = H.attend(st, shared_blocks=True).cpu().numpy()
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+def test_result_does_not_depend_on_work_split():
+    """The same partition size with a different number of partitions per
+    workgroup gives identical rows: 16 sequences of 16384 tokens make the
+    launcher give each wave two 512-token partitions, one sequence alone one."""
+    w = workloads.long_context(num_seqs=16, context_len=16384, partition_size=512)
+    st = H.upload(w)
+    two = H.attend(st).cpu().numpy()
+    one = pkv.attention_decode(st.query[:1].contiguous(), st.kv, st.tables[:1].contiguous(),
+                               st.lens[:1].contiguous(), w.scale, w.max_context_len,
+                               partition_size=512).cpu().numpy()
+    assert np.array_equal(one[0].view(np.uint32), two[0].view(np.uint32))
+
+
 def test_bf16_output_is_rounded_fp32_output():
     w = workloads.long_context(num_seqs=2, context_len=2000)
     st = H.upload(w)
