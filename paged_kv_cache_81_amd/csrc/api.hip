@@ -86,13 +86,13 @@ int resolve_partition(int S, int Hq, int Hkv, int D, int B, int max_len, int req
 // per wave, since its lengths may be ragged and a long run on its longest
 // sequence would become the critical path.  Capped by what the waves can hold
 // in LDS until they write it.
-int bf16_parts_per_wg(int S, int Hq, int Hkv, int D, int max_parts) {
+int bf16_parts_per_wg(int S, int Hq, int Hkv, int D, int max_parts, bool k_tile) {
   const int nslot = 4 / bf16_heads_per_group(Hkv);
   const int64_t units = bf16_units(S, Hq, Hkv);
   if (S > 32) return nslot;
   int64_t pps = units * max_parts / (static_cast<int64_t>(kResidentGroups) * nslot);
   pps = std::max<int64_t>(1, std::min<int64_t>(pps, cdiv64(max_parts, nslot)));
-  while (pps > 1 && bf16_lds_bytes(static_cast<int>(pps), Hq / Hkv, D) > bf16_lds_limit()) --pps;
+  while (pps > 1 && bf16_lds_bytes(static_cast<int>(pps), Hq / Hkv, D, k_tile) > bf16_lds_limit()) --pps;
   return static_cast<int>(pps) * nslot;
 }
 
@@ -277,8 +277,19 @@ int decode_impl(int phases, void* out, pkv_dtype out_dtype, const void* query,
   a.scale_log2 = scale * 1.4426950408889634f;
   a.out_bf16 = out_dtype == PKV_BF16 ? 1 : 0;
   a.nontemporal = (flags & PKV_ATTN_CACHED_KV) ? 0 : 1;
+  // Longest sequences first, so the longest work starts earliest and short
+  // sequences fill the tail -- except when blocks are shared: sequences that
+  // share blocks come adjacent in a batch and should run together to hit in
+  // the caches.  Each workgroup ranks the lengths itself, so only for small
+  // batches.
+  a.longest_first = !(flags & PKV_ATTN_CACHED_KV) && num_seqs <= kMaxRankedSeqs;
+  // Keys take the LDS path when a token's row across all kv heads is long
+  // (>= 4 KB): one head's 64-byte pieces of such rows stream poorly, while
+  // for short rows the direct MFMA-layout load is faster.
+  a.k_via_lds = static_cast<int64_t>(num_kv_heads) * head_size * elem_bytes(dtype) >= 4096;
   a.parts_per_wg = dtype == PKV_BF16
-                       ? bf16_parts_per_wg(num_seqs, num_q_heads, num_kv_heads, head_size, a.max_parts)
+                       ? bf16_parts_per_wg(num_seqs, num_q_heads, num_kv_heads, head_size, a.max_parts,
+                                           a.k_via_lds != 0)
                        : 1;
   if (parts > 1) {
     const size_t need = paged_attention_workspace_bytes(num_seqs, num_q_heads, num_kv_heads,

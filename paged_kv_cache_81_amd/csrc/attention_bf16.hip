@@ -82,13 +82,15 @@ __device__ __forceinline__ bf16x8 load_bf16x8(const uint16_t* p) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-template <int D, int B, int HG, bool NT>
+template <int D, int B, int HG, bool NT, bool KL>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
 attention_bf16_kernel(AttnArgs a) {
   constexpr int QC = D / 32;  // score MFMAs per tile (32 dims each)
   constexpr int NV = D / 16;  // output blocks of 16 rows; dims per lane per V token
   constexpr int NW = NV / 2;  // 32-bit words per lane per V token
   constexpr int NSLOT = kWaves / HG;  // waves per kv head, each on its own partitions
+  constexpr int NCH = D / 8;          // 16-byte chunks per K row
+  auto kskew = [](int t) { return (t * NCH / 16) % NCH; };
 
   // Finished partitions stay in LDS until the wave has read its last K/V:
   // a global store issued between the loads would make the following waits
@@ -106,9 +108,31 @@ attention_bf16_kernel(AttnArgs a) {
 
   const int G = a.Hq / a.Hkv;
   const int chunks = (G + 15) >> 4;
+  // grid: x = run of partitions, y = (kv-head group, query-head chunk),
+  // z = sequence: all work of a sequence is dispatched together
   const int hg = blockIdx.y / chunks;
   const int chunk = blockIdx.y - hg * chunks;
-  const int s = blockIdx.z;
+  // Longest sequences first: workgroups are dispatched in blockIdx order, so
+  // the workgroups of z take the z-th longest sequence (ties by index).  Long
+  // sequences then start first and short ones fill the tail.
+  int s = blockIdx.z;
+  if (a.longest_first) {
+    __shared__ int s_len[kMaxRankedSeqs];
+    __shared__ int s_pick;
+    for (int i = threadIdx.x; i < a.S; i += kThreads) s_len[i] = a.lens[i];
+    __syncthreads();
+    for (int c = threadIdx.x; c < a.S; c += kThreads) {
+      const int lc = s_len[c];
+      int rank = 0;
+      for (int t = 0; t < a.S; ++t) {
+        const int lt = s_len[t];
+        rank += (lt > lc || (lt == lc && t < c)) ? 1 : 0;
+      }
+      if (rank == static_cast<int>(blockIdx.z)) s_pick = c;
+    }
+    __syncthreads();
+    s = s_pick;
+  }
   const int kvh = hg * HG + hi;
   const int nh = min(16, G - chunk * 16);
   const int h0 = kvh * G + chunk * 16;
@@ -125,9 +149,12 @@ attention_bf16_kernel(AttnArgs a) {
   const int p_first = blockIdx.x * a.parts_per_wg + slot * pps;
   if (p_first >= nparts) return;  // (partition 0 always exists)
 
-  // LDS of this wave: rows [i][hh][SROW] for its i-th partition, then (m, l)
+  // LDS of this wave: the current step's K tile (32 tokens x D bf16), then
+  // rows [i][hh][SROW] of its i-th finished partition, then their (m, l)
   const int nhs = min(16, G);  // head rows per partition slot
-  float* stage = s_dyn + static_cast<int64_t>(wv) * bf16_lds_wave_floats(pps, G, D);
+  float* wave_lds = s_dyn + static_cast<int64_t>(wv) * bf16_lds_wave_floats(pps, G, D, KL);
+  char* k_lds = reinterpret_cast<char*>(wave_lds);
+  float* stage = wave_lds + (KL ? bf16_lds_k_floats(D) : 0);
   float* stage_ml = stage + pps * nhs * SROW;  // 16-byte aligned: SROW % 4 == 0
 
   // Write partition p_first + i of heads h0 .. h0+nh-1 from the wave's LDS:
@@ -187,12 +214,16 @@ attention_bf16_kernel(AttnArgs a) {
   const uint16_t* kbase = static_cast<const uint16_t*>(a.kv) + static_cast<int64_t>(kvh) * D;
   const uint16_t* vbase = kbase + static_cast<int64_t>(a.NB) * B * row;
   const int32_t* trow = a.tables + static_cast<int64_t>(s) * a.width;
-  // per-lane byte offsets inside a 16-token tile (unsigned 32-bit, so a load is
-  // scalar base + vector offset)
-  const uint32_t koff = (j * static_cast<uint32_t>(row) + 8 * g) * 2u;
+  // Per-lane byte offsets inside a 16-token tile (unsigned 32-bit, so a load is
+  // scalar base + vector offset).  Keys and values are read alike: one load
+  // instruction covers 4 rows of D*2 contiguous bytes (lane (j, g): row
+  // 4g + r, bytes 2*NV*j ..), the shape that streams at full rate; a load
+  // giving each lane its MFMA row directly (16 rows of 64 bytes) streams ~30%
+  // slower.  Keys are then rearranged through LDS for the score MFMA.
   uint32_t voff[4];
 #pragma unroll
   for (int r = 0; r < 4; ++r) voff[r] = ((4 * g + r) * static_cast<uint32_t>(row) + NV * j) * 2u;
+  const uint32_t koff = (j * static_cast<uint32_t>(row) + 8 * g) * 2u;
 
   // Block-table window: lane l holds the physical block of tile (l & 1) of
   // step q0 + (l >> 1), so 32 steps need one load; per step the entries are
@@ -205,8 +236,12 @@ attention_bf16_kernel(AttnArgs a) {
   int win = load_window(0);
   asm volatile("" ::"v"(win));
 
+  // K arrives either row-wise like V and is rearranged through LDS (KL), or
+  // straight in MFMA layout (token j, dims 32c + 8g: 16 rows of 64 bytes per
+  // load instruction)
   struct Step {
-    bf16x8 k[2][QC];
+    Words<NW> k[2][4];  // KL: token 4g + r of tile u, dims NV*j ..
+    bf16x8 kd[2][QC];   // !KL: token j of tile u, dims 32c + 8g ..
     Words<NW> v[2][4];
     bool bad;  // a table entry of this step is out of range
   };
@@ -237,9 +272,15 @@ attention_bf16_kernel(AttnArgs a) {
       const int64_t base = (static_cast<int64_t>(blk) * B + (tt % B)) * row;
       const char* kp = reinterpret_cast<const char*>(kbase + base);
       const char* vp = reinterpret_cast<const char*>(vbase + base);
+      if constexpr (KL) {
 #pragma unroll
-      for (int c = 0; c < QC; ++c)
-        d.k[u][c] = load_bf16x8<NT>(reinterpret_cast<const uint16_t*>(kp + koff + 64 * c));
+        for (int r = 0; r < 4; ++r)
+          d.k[u][r] = load_words<NW, NT>(reinterpret_cast<const uint16_t*>(kp + voff[r]));
+      } else {
+#pragma unroll
+        for (int c = 0; c < QC; ++c)
+          d.kd[u][c] = load_bf16x8<NT>(reinterpret_cast<const uint16_t*>(kp + koff + 64 * c));
+      }
 #pragma unroll
       for (int r = 0; r < 4; ++r)
         d.v[u][r] = load_words<NW, NT>(reinterpret_cast<const uint16_t*>(vp + voff[r]));
@@ -288,14 +329,43 @@ attention_bf16_kernel(AttnArgs a) {
     bad_blk = bad_blk || d.bad;
     const int lim = tw_end - ts;  // valid tokens in this step (>= 1)
 
+    // K tile through LDS: token t of the step is a row of 2D bytes; its
+    // 16-byte chunk ch sits at chunk position (ch + skew(t)) mod NCH, so both
+    // the row-wise writes and the MFMA-layout reads (token j, chunk 4c + g)
+    // hit distinct banks within each 16-lane pass
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        if constexpr (!KL) break;
+        const int t = 16 * u + 4 * g + r;
+        const int pb = NW * 4;                 // bytes of this lane's piece
+        const int ch = (j * pb) >> 4;          // its 16-byte chunk
+        const int pos = t * (2 * D) + 16 * ((ch + kskew(t)) % NCH) + ((j * pb) & 15);
+        if constexpr (NW == 4) {
+          *reinterpret_cast<u32x4*>(k_lds + pos) = u32x4{d.k[u][r].w[0], d.k[u][r].w[1], d.k[u][r].w[2], d.k[u][r].w[3]};
+        } else {
+          *reinterpret_cast<u32x2*>(k_lds + pos) = u32x2{d.k[u][r].w[0], d.k[u][r].w[1]};
+        }
+      }
+
     // scores
     float x[2][4];
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       f32x4 sc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int c = 0; c < QC; ++c)
-        sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(d.k[u][c], qf[c], sc, 0, 0, 0);
+      for (int c = 0; c < QC; ++c) {
+        bf16x8 kf;
+        if constexpr (KL) {
+          const int t = 16 * u + j;
+          const int pos = t * (2 * D) + 16 * ((4 * c + g + kskew(t)) % NCH);
+          kf = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(k_lds + pos));
+        } else {
+          kf = d.kd[u][c];
+        }
+        sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[c], sc, 0, 0, 0);
+      }
 #pragma unroll
       for (int r = 0; r < 4; ++r) x[u][r] = sc[r] * a.scale_log2;
     }
@@ -374,9 +444,9 @@ attention_bf16_kernel(AttnArgs a) {
   for (int i = 0; i <= p_last - p_first; ++i) store_rows(i);
 }
 
-template <int D, int B, int HG, bool NT>
+template <int D, int B, int HG, bool NT, bool KL>
 int launch_one(const AttnArgs& a, dim3 grid, size_t lds, hipStream_t stream) {
-  auto kern = attention_bf16_kernel<D, B, HG, NT>;
+  auto kern = attention_bf16_kernel<D, B, HG, NT, KL>;
   static bool attr_set = false;  // allow dynamic LDS up to the per-workgroup maximum
   if (!attr_set) {
     if (hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -391,23 +461,29 @@ int launch_one(const AttnArgs& a, dim3 grid, size_t lds, hipStream_t stream) {
   return check_launch("paged attention (bf16)");
 }
 
+template <int D, int B, int HG>
+int launch_hg(const AttnArgs& a, dim3 grid, size_t lds, hipStream_t stream) {
+  const bool nt = a.nontemporal != 0, kl = a.k_via_lds != 0;
+  if (nt) return kl ? launch_one<D, B, HG, true, true>(a, grid, lds, stream)
+                    : launch_one<D, B, HG, true, false>(a, grid, lds, stream);
+  return kl ? launch_one<D, B, HG, false, true>(a, grid, lds, stream)
+            : launch_one<D, B, HG, false, false>(a, grid, lds, stream);
+}
+
 template <int D, int B>
 int launch(const AttnArgs& a, hipStream_t stream) {
   const int G = a.Hq / a.Hkv;
   const int chunks = (G + 15) / 16;
   const int HG = bf16_heads_per_group(a.Hkv);
   dim3 grid((a.max_parts + a.parts_per_wg - 1) / a.parts_per_wg, (a.Hkv / HG) * chunks, a.S);
-  const size_t lds = bf16_lds_bytes(a.parts_per_wg / (4 / HG), G, D);
+  const size_t lds = bf16_lds_bytes(a.parts_per_wg / (4 / HG), G, D, a.k_via_lds != 0);
   if (lds > bf16_lds_limit()) {
     set_error("paged attention (bf16): %zu bytes of LDS needed", lds);
     return PKV_ERR_UNSUPPORTED;
   }
-  const bool nt = a.nontemporal != 0;
-  if (HG == 4)
-    return nt ? launch_one<D, B, 4, true>(a, grid, lds, stream) : launch_one<D, B, 4, false>(a, grid, lds, stream);
-  if (HG == 2)
-    return nt ? launch_one<D, B, 2, true>(a, grid, lds, stream) : launch_one<D, B, 2, false>(a, grid, lds, stream);
-  return nt ? launch_one<D, B, 1, true>(a, grid, lds, stream) : launch_one<D, B, 1, false>(a, grid, lds, stream);
+  if (HG == 4) return launch_hg<D, B, 4>(a, grid, lds, stream);
+  if (HG == 2) return launch_hg<D, B, 2>(a, grid, lds, stream);
+  return launch_hg<D, B, 1>(a, grid, lds, stream);
 }
 
 }  // namespace

@@ -75,23 +75,31 @@ struct AttnArgs {
   int out_bf16;
   int nontemporal;    // stream K/V past the caches
   int parts_per_wg;   // partitions one workgroup covers (bf16 path)
+  int longest_first;  // map workgroups to sequences in decreasing length
+  int k_via_lds;      // load keys row-wise and rearrange them through LDS
 };
+
+// largest batch whose bf16 workgroups rank the sequences by length
+constexpr int kMaxRankedSeqs = 128;
 
 // kv heads per bf16 workgroup: 4 when they divide Hkv, else 2, else 1
 inline int bf16_heads_per_group(int Hkv) { return Hkv % 4 == 0 ? 4 : (Hkv % 2 == 0 ? 2 : 1); }
 
-// LDS of one bf16 workgroup: for each of its 4 waves, pps partition slots of
-// min(16, G) head rows (D + 4 floats), then an (m, l) pair per row, padded
-// to a multiple of 4 floats so every wave's area stays 16-byte aligned.
-__host__ __device__ inline int bf16_lds_wave_floats(int pps, int G, int D) {
+// LDS of one bf16 workgroup: for each of its 4 waves, a 32-token K tile
+// (32 x D bf16), then pps partition slots of min(16, G) head rows (D + 4
+// floats), then an (m, l) pair per row, padded to a multiple of 4 floats so
+// every wave's area stays 16-byte aligned.
+__host__ __device__ inline int bf16_lds_k_floats(int D) { return 16 * D; }
+__host__ __device__ inline int bf16_lds_wave_floats(int pps, int G, int D, bool k_tile) {
   const int nhs = G < 16 ? G : 16;
-  return pps * nhs * (D + 4) + (pps * nhs * 2 + 3) / 4 * 4;
+  return (k_tile ? bf16_lds_k_floats(D) : 0) + pps * nhs * (D + 4) + (pps * nhs * 2 + 3) / 4 * 4;
 }
-inline size_t bf16_lds_bytes(int pps, int G, int D) {
-  return static_cast<size_t>(4) * bf16_lds_wave_floats(pps, G, D) * sizeof(float);
+inline size_t bf16_lds_bytes(int pps, int G, int D, bool k_tile) {
+  return static_cast<size_t>(4) * bf16_lds_wave_floats(pps, G, D, k_tile) * sizeof(float);
 }
-// at most this much, so that two workgroups fit in a CU's 160 KB
-inline size_t bf16_lds_limit() { return 76 * 1024; }
+// at most this much (plus ~1 KB of static LDS), so that two workgroups fit
+// in a CU's 160 KB
+inline size_t bf16_lds_limit() { return 78 * 1024; }
 
 int launch_attention_bf16(const AttnArgs& a, hipStream_t stream);
 int launch_attention_f32(const AttnArgs& a, hipStream_t stream);
