@@ -291,6 +291,13 @@ int decode_impl(int phases, void* out, pkv_dtype out_dtype, const void* query,
                        ? bf16_parts_per_wg(num_seqs, num_q_heads, num_kv_heads, head_size, a.max_parts,
                                            a.k_via_lds != 0)
                        : 1;
+  // When contexts are split into several workgroup runs, a ragged batch
+  // leaves most of a grid sized by the longest context empty, and dispatching
+  // the empty workgroups takes longer than the work: workgroups then number
+  // the real work items themselves and walk that list instead.
+  a.compact = dtype == PKV_BF16 && num_seqs <= kMaxCompactSeqs &&
+              cdiv64(a.max_parts, a.parts_per_wg) > 1;
+  if (a.compact) a.longest_first = 0;
   if (parts > 1) {
     const size_t need = paged_attention_workspace_bytes(num_seqs, num_q_heads, num_kv_heads,
                                                         head_size, block_size, max_context_len,

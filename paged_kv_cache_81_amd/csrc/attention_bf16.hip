@@ -35,7 +35,9 @@
 //    (max score, exponent sum, normalised partial output) for the merge kernel.
 #include "common.hpp"
 
+#include <algorithm>
 #include <cmath>
+#include <mutex>
 
 namespace pkv {
 namespace {
@@ -108,340 +110,423 @@ attention_bf16_kernel(AttnArgs a) {
 
   const int G = a.Hq / a.Hkv;
   const int chunks = (G + 15) >> 4;
-  // grid: x = run of partitions, y = (kv-head group, query-head chunk),
-  // z = sequence: all work of a sequence is dispatched together
-  const int hg = blockIdx.y / chunks;
-  const int chunk = blockIdx.y - hg * chunks;
-  // Longest sequences first: workgroups are dispatched in blockIdx order, so
-  // the workgroups of z take the z-th longest sequence (ties by index).  Long
-  // sequences then start first and short ones fill the tail.
-  int s = blockIdx.z;
-  if (a.longest_first) {
-    __shared__ int s_len[kMaxRankedSeqs];
+  const int Y = (a.Hkv / HG) * chunks;  // (kv-head group, query-head chunk) pairs
+  const int P = a.partition;
+
+  // Work items are (sequence, pair y, run of partitions).  Dense grid: x =
+  // run, y = pair, z = sequence, so all work of a sequence is dispatched
+  // together; workgroups past a sequence's last partition exit at once.
+  // Compact list (split contexts of a ragged batch, where most of the dense
+  // grid would be such empty workgroups): the items of all sequences are
+  // numbered consecutively -- sequence, then pair, then run -- and workgroup b
+  // takes items b, b + gridDim.x, ...
+  // compact list: first item of each sequence; dense grid: the lengths
+  __shared__ int s_seq[kMaxCompactSeqs + 1];
+  __shared__ int s_wsum[kWaves];
+  int total = 1;
+  if (a.compact) {
+    auto runs_of = [&](int L) {
+      const int np = L > 0 ? (L + P - 1) / P : 1;
+      const bool bad = L < 0 || (L + B - 1) / B > a.width || np > a.max_parts;
+      return bad ? 1 : (np + a.parts_per_wg - 1) / a.parts_per_wg;
+    };
+    const int i0 = 2 * threadIdx.x;
+    const int c0 = i0 < a.S ? Y * runs_of(a.lens[i0]) : 0;
+    const int c1 = i0 + 1 < a.S ? Y * runs_of(a.lens[i0 + 1]) : 0;
+    int v = c0 + c1;  // inclusive scan over the wave's lanes
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int t = __shfl_up(v, d, 64);
+      if (lane >= d) v += t;
+    }
+    if (lane == 63) s_wsum[wv] = v;
+    __syncthreads();
+    int before = 0;
+    total = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      before += w < wv ? s_wsum[w] : 0;
+      total += s_wsum[w];
+    }
+    const int excl = before + v - c0 - c1;
+    if (i0 < a.S) s_seq[i0] = excl;
+    if (i0 + 1 < a.S) s_seq[i0 + 1] = excl + c0;
+    if (threadIdx.x == 0) s_seq[a.S] = total;
+    __syncthreads();
+  }
+
+  // Longest sequences first (dense grid): workgroups are dispatched in
+  // blockIdx order, so the workgroups of z take the z-th longest sequence
+  // (ties by index).  Long sequences then start first and short ones fill
+  // the tail.
+  int s_dense = blockIdx.z;
+  if (!a.compact && a.longest_first) {
     __shared__ int s_pick;
-    for (int i = threadIdx.x; i < a.S; i += kThreads) s_len[i] = a.lens[i];
+    for (int i = threadIdx.x; i < a.S; i += kThreads) s_seq[i] = a.lens[i];
     __syncthreads();
     for (int c = threadIdx.x; c < a.S; c += kThreads) {
-      const int lc = s_len[c];
+      const int lc = s_seq[c];
       int rank = 0;
       for (int t = 0; t < a.S; ++t) {
-        const int lt = s_len[t];
+        const int lt = s_seq[t];
         rank += (lt > lc || (lt == lc && t < c)) ? 1 : 0;
       }
       if (rank == static_cast<int>(blockIdx.z)) s_pick = c;
     }
     __syncthreads();
-    s = s_pick;
+    s_dense = s_pick;
   }
-  const int kvh = hg * HG + hi;
-  const int nh = min(16, G - chunk * 16);
-  const int h0 = kvh * G + chunk * 16;
 
-  const int L = a.lens[s];
-  const int P = a.partition;
-  const int nparts = L > 0 ? (L + P - 1) / P : 1;
-  const bool bad_seq = L < 0 || (L + B - 1) / B > a.width || nparts > a.max_parts;
-  // without a workspace (one partition per sequence) results always go to out
-  const bool single = nparts == 1 || a.max_parts == 1;
-  // this workgroup covers partitions [p_first, p_first + parts_per_wg); the
-  // wave covers a contiguous run of pps of them, i.e. one token range
-  const int pps = a.parts_per_wg / NSLOT;
-  const int p_first = blockIdx.x * a.parts_per_wg + slot * pps;
-  if (p_first >= nparts) return;  // (partition 0 always exists)
+  // one work item: sequence s, pair yy, partition run xr
+  auto item = [&](const int s, const int yy, const int xr) {
+    const int hg = yy / chunks;
+    const int chunk = yy - hg * chunks;
+    const int kvh = hg * HG + hi;
+    const int nh = min(16, G - chunk * 16);
+    const int h0 = kvh * G + chunk * 16;
 
-  // LDS of this wave: the current step's K tile (32 tokens x D bf16), then
-  // rows [i][hh][SROW] of its i-th finished partition, then their (m, l)
-  const int nhs = min(16, G);  // head rows per partition slot
-  float* wave_lds = s_dyn + static_cast<int64_t>(wv) * bf16_lds_wave_floats(pps, G, D, KL);
-  char* k_lds = reinterpret_cast<char*>(wave_lds);
-  float* stage = wave_lds + (KL ? bf16_lds_k_floats(D) : 0);
-  float* stage_ml = stage + pps * nhs * SROW;  // 16-byte aligned: SROW % 4 == 0
+    const int L = a.lens[s];
+    const int nparts = L > 0 ? (L + P - 1) / P : 1;
+    const bool bad_seq = L < 0 || (L + B - 1) / B > a.width || nparts > a.max_parts;
+    // without a workspace (one partition per sequence) results always go to out
+    const bool single = nparts == 1 || a.max_parts == 1;
+    // this workgroup covers partitions [p_first, p_first + parts_per_wg); the
+    // wave covers a contiguous run of pps of them, i.e. one token range
+    const int pps = a.parts_per_wg / NSLOT;
+    const int p_first = xr * a.parts_per_wg + slot * pps;
+    if (p_first >= nparts) return;  // (partition 0 always exists)
 
-  // Write partition p_first + i of heads h0 .. h0+nh-1 from the wave's LDS:
-  // the normalised output (single partition) into out, else the partial
-  // output and (m, l) into the workspace, whose layout [s][p][h][D] keeps a
-  // wave's heads adjacent.  Each store instruction covers 64 consecutive
-  // 16-byte pieces.
-  auto store_rows = [&](int i) {
-    const int p = p_first + i;
-    const float* src = stage + i * nhs * SROW;
-    constexpr int D4 = D / 4;
-    const int64_t row0 = single ? static_cast<int64_t>(s) * a.Hq + h0
-                                : (static_cast<int64_t>(s) * a.max_parts + p) * a.Hq + h0;
-    for (int e = lane; e < nh * D4; e += 64) {
-      const int hh = e / D4;
-      const int d = (e - hh * D4) * 4;
-      const float4 o = *reinterpret_cast<const float4*>(src + hh * SROW + d);
-      const int64_t off = row0 * D + static_cast<int64_t>(e) * 4;
-      if (single && a.out_bf16) {
-        const uint32_t lo = f32_to_bf16(o.x) | (static_cast<uint32_t>(f32_to_bf16(o.y)) << 16);
-        const uint32_t hi2 = f32_to_bf16(o.z) | (static_cast<uint32_t>(f32_to_bf16(o.w)) << 16);
-        *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(a.out) + off) = u32x2{lo, hi2};
-      } else {
-        *reinterpret_cast<float4*>((single ? static_cast<float*>(a.out) : a.ws_o) + off) = o;
+    // LDS of this wave: the current step's K tile (32 tokens x D bf16), then
+    // rows [i][hh][SROW] of its i-th finished partition, then their (m, l)
+    const int nhs = min(16, G);  // head rows per partition slot
+    float* wave_lds = s_dyn + static_cast<int64_t>(wv) * bf16_lds_wave_floats(pps, G, D, KL);
+    char* k_lds = reinterpret_cast<char*>(wave_lds);
+    float* stage = wave_lds + (KL ? bf16_lds_k_floats(D) : 0);
+    float* stage_ml = stage + pps * nhs * SROW;  // 16-byte aligned: SROW % 4 == 0
+
+    // Write partition p_first + i of heads h0 .. h0+nh-1 from the wave's LDS:
+    // the normalised output (single partition) into out, else the partial
+    // output and (m, l) into the workspace, whose layout [s][p][h][D] keeps a
+    // wave's heads adjacent.  Each store instruction covers 64 consecutive
+    // 16-byte pieces.
+    auto store_rows = [&](int i) {
+      const int p = p_first + i;
+      const float* src = stage + i * nhs * SROW;
+      constexpr int D4 = D / 4;
+      const int64_t row0 = single ? static_cast<int64_t>(s) * a.Hq + h0
+                                  : (static_cast<int64_t>(s) * a.max_parts + p) * a.Hq + h0;
+      for (int e = lane; e < nh * D4; e += 64) {
+        const int hh = e / D4;
+        const int d = (e - hh * D4) * 4;
+        const float4 o = *reinterpret_cast<const float4*>(src + hh * SROW + d);
+        const int64_t off = row0 * D + static_cast<int64_t>(e) * 4;
+        if (single && a.out_bf16) {
+          const uint32_t lo = f32_to_bf16(o.x) | (static_cast<uint32_t>(f32_to_bf16(o.y)) << 16);
+          const uint32_t hi2 = f32_to_bf16(o.z) | (static_cast<uint32_t>(f32_to_bf16(o.w)) << 16);
+          *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(a.out) + off) = u32x2{lo, hi2};
+        } else {
+          *reinterpret_cast<float4*>((single ? static_cast<float*>(a.out) : a.ws_o) + off) = o;
+        }
       }
+      if (!single && lane < nh)
+        *reinterpret_cast<float2*>(a.ws_ml + 2 * (row0 + lane)) =
+            *reinterpret_cast<const float2*>(stage_ml + 2 * (i * nhs + lane));
+    };
+
+    if (bad_seq) {
+      // the merge kernel poisons split sequences itself
+      if (single) {
+        for (int i = lane; i < nh * SROW; i += 64) stage[i] = NAN;
+        __builtin_amdgcn_wave_barrier();
+        store_rows(0);
+      }
+      return;
     }
-    if (!single && lane < nh)
-      *reinterpret_cast<float2*>(a.ws_ml + 2 * (row0 + lane)) =
-          *reinterpret_cast<const float2*>(stage_ml + 2 * (i * nhs + lane));
-  };
 
-  if (bad_seq) {
-    // the merge kernel poisons split sequences itself
-    if (single) {
-      for (int i = lane; i < nh * SROW; i += 64) stage[i] = NAN;
-      __builtin_amdgcn_wave_barrier();
-      store_rows(0);
+    // query fragments: q[s][h0 + j][32c + 8g .. +8]
+    bf16x8 qf[QC];
+    {
+      const uint16_t* qp = static_cast<const uint16_t*>(a.query) +
+                           (static_cast<int64_t>(s) * a.Hq + h0 + j) * D + 8 * g;
+#pragma unroll
+      for (int c = 0; c < QC; ++c)
+        qf[c] = (j < nh) ? load_bf16x8<false>(qp + 32 * c) : bf16x8{};
     }
-    return;
-  }
 
-  // query fragments: q[s][h0 + j][32c + 8g .. +8]
-  bf16x8 qf[QC];
-  {
-    const uint16_t* qp = static_cast<const uint16_t*>(a.query) +
-                         (static_cast<int64_t>(s) * a.Hq + h0 + j) * D + 8 * g;
+    const int tw_begin = p_first * P;
+    const int tw_end = min(L, (p_first + pps) * P);
+    const int my_steps = (tw_end - tw_begin + kStep - 1) / kStep;  // 0 only when L == 0
+
+    const int64_t row = static_cast<int64_t>(a.Hkv) * D;  // elements between slots
+    const uint16_t* kbase = static_cast<const uint16_t*>(a.kv) + static_cast<int64_t>(kvh) * D;
+    const uint16_t* vbase = kbase + static_cast<int64_t>(a.NB) * B * row;
+    const int32_t* trow = a.tables + static_cast<int64_t>(s) * a.width;
+    // Per-lane byte offsets inside a 16-token tile (unsigned 32-bit, so a load is
+    // scalar base + vector offset).  Keys and values are read alike: one load
+    // instruction covers 4 rows of D*2 contiguous bytes (lane (j, g): row
+    // 4g + r, bytes 2*NV*j ..), the shape that streams at full rate; a load
+    // giving each lane its MFMA row directly (16 rows of 64 bytes) streams ~30%
+    // slower.  Keys are then rearranged through LDS for the score MFMA.
+    uint32_t voff[4];
 #pragma unroll
-    for (int c = 0; c < QC; ++c)
-      qf[c] = (j < nh) ? load_bf16x8<false>(qp + 32 * c) : bf16x8{};
-  }
+    for (int r = 0; r < 4; ++r) voff[r] = ((4 * g + r) * static_cast<uint32_t>(row) + NV * j) * 2u;
+    const uint32_t koff = (j * static_cast<uint32_t>(row) + 8 * g) * 2u;
 
-  const int tw_begin = p_first * P;
-  const int tw_end = min(L, (p_first + pps) * P);
-  const int my_steps = (tw_end - tw_begin + kStep - 1) / kStep;  // 0 only when L == 0
+    // Block-table window: lane l holds the physical block of tile (l & 1) of
+    // step q0 + (l >> 1), so 32 steps need one load; per step the entries are
+    // read back as scalars.
+    auto load_window = [&](int q0) -> int {
+      const int tt = tw_begin + (q0 + (lane >> 1)) * kStep + 16 * (lane & 1);
+      return tt < tw_end ? trow[tt / B] : -1;
+    };
+    int win_q0 = 0;
+    int win = load_window(0);
+    asm volatile("" ::"v"(win));
 
-  const int64_t row = static_cast<int64_t>(a.Hkv) * D;  // elements between slots
-  const uint16_t* kbase = static_cast<const uint16_t*>(a.kv) + static_cast<int64_t>(kvh) * D;
-  const uint16_t* vbase = kbase + static_cast<int64_t>(a.NB) * B * row;
-  const int32_t* trow = a.tables + static_cast<int64_t>(s) * a.width;
-  // Per-lane byte offsets inside a 16-token tile (unsigned 32-bit, so a load is
-  // scalar base + vector offset).  Keys and values are read alike: one load
-  // instruction covers 4 rows of D*2 contiguous bytes (lane (j, g): row
-  // 4g + r, bytes 2*NV*j ..), the shape that streams at full rate; a load
-  // giving each lane its MFMA row directly (16 rows of 64 bytes) streams ~30%
-  // slower.  Keys are then rearranged through LDS for the score MFMA.
-  uint32_t voff[4];
+    // K arrives either row-wise like V and is rearranged through LDS (KL), or
+    // straight in MFMA layout (token j, dims 32c + 8g: 16 rows of 64 bytes per
+    // load instruction)
+    struct Step {
+      Words<NW> k[2][4];  // KL: token 4g + r of tile u, dims NV*j ..
+      bf16x8 kd[2][QC];   // !KL: token j of tile u, dims 32c + 8g ..
+      Words<NW> v[2][4];
+      bool bad;  // a table entry of this step is out of range
+    };
+    bool bad_blk = false;  // ... of some step of the current partition
+
+    // issue the loads of step q (tokens tw_begin + 32q ..).  The same 16 loads
+    // are issued on every path, so the compiler can wait for exactly one
+    // buffer's loads: a tile past the end of the run, or whose table entry is
+    // out of range, reads block 0 instead (always in the pool); its scores are
+    // masked and its values zeroed in compute(), or its partition poisoned.
+    auto issue = [&](Step& d, int q) {
+      if (q - win_q0 >= 32) {
+        win_q0 = q;
+        win = load_window(q);
+        // wait for the entries here: a load still pending where the paths join
+        // would make every step wait for all outstanding K/V loads
+        asm volatile("" ::"v"(win));
+      }
+      const int ts = tw_begin + q * kStep;
+      d.bad = false;
 #pragma unroll
-  for (int r = 0; r < 4; ++r) voff[r] = ((4 * g + r) * static_cast<uint32_t>(row) + NV * j) * 2u;
-  const uint32_t koff = (j * static_cast<uint32_t>(row) + 8 * g) * 2u;
-
-  // Block-table window: lane l holds the physical block of tile (l & 1) of
-  // step q0 + (l >> 1), so 32 steps need one load; per step the entries are
-  // read back as scalars.
-  auto load_window = [&](int q0) -> int {
-    const int tt = tw_begin + (q0 + (lane >> 1)) * kStep + 16 * (lane & 1);
-    return tt < tw_end ? trow[tt / B] : -1;
-  };
-  int win_q0 = 0;
-  int win = load_window(0);
-  asm volatile("" ::"v"(win));
-
-  // K arrives either row-wise like V and is rearranged through LDS (KL), or
-  // straight in MFMA layout (token j, dims 32c + 8g: 16 rows of 64 bytes per
-  // load instruction)
-  struct Step {
-    Words<NW> k[2][4];  // KL: token 4g + r of tile u, dims NV*j ..
-    bf16x8 kd[2][QC];   // !KL: token j of tile u, dims 32c + 8g ..
-    Words<NW> v[2][4];
-    bool bad;  // a table entry of this step is out of range
-  };
-  bool bad_blk = false;  // ... of some step of the current partition
-
-  // issue the loads of step q (tokens tw_begin + 32q ..).  The same 16 loads
-  // are issued on every path, so the compiler can wait for exactly one
-  // buffer's loads: a tile past the end of the run, or whose table entry is
-  // out of range, reads block 0 instead (always in the pool); its scores are
-  // masked and its values zeroed in compute(), or its partition poisoned.
-  auto issue = [&](Step& d, int q) {
-    if (q - win_q0 >= 32) {
-      win_q0 = q;
-      win = load_window(q);
-      // wait for the entries here: a load still pending where the paths join
-      // would make every step wait for all outstanding K/V loads
-      asm volatile("" ::"v"(win));
-    }
-    const int ts = tw_begin + q * kStep;
-    d.bad = false;
+      for (int u = 0; u < 2; ++u) {
+        const int tt = ts + 16 * u;
+        const int phys = __builtin_amdgcn_readlane(win, 2 * (q - win_q0) + u);
+        const bool in_range = phys >= 0 && phys < a.NB;
+        d.bad = d.bad || (tt < tw_end && !in_range);
+        const int blk = (tt < tw_end && in_range) ? phys : 0;
+        const int64_t base = (static_cast<int64_t>(blk) * B + (tt % B)) * row;
+        const char* kp = reinterpret_cast<const char*>(kbase + base);
+        const char* vp = reinterpret_cast<const char*>(vbase + base);
+        if constexpr (KL) {
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int tt = ts + 16 * u;
-      const int phys = __builtin_amdgcn_readlane(win, 2 * (q - win_q0) + u);
-      const bool in_range = phys >= 0 && phys < a.NB;
-      d.bad = d.bad || (tt < tw_end && !in_range);
-      const int blk = (tt < tw_end && in_range) ? phys : 0;
-      const int64_t base = (static_cast<int64_t>(blk) * B + (tt % B)) * row;
-      const char* kp = reinterpret_cast<const char*>(kbase + base);
-      const char* vp = reinterpret_cast<const char*>(vbase + base);
-      if constexpr (KL) {
+          for (int r = 0; r < 4; ++r)
+            d.k[u][r] = load_words<NW, NT>(reinterpret_cast<const uint16_t*>(kp + voff[r]));
+        } else {
+#pragma unroll
+          for (int c = 0; c < QC; ++c)
+            d.kd[u][c] = load_bf16x8<NT>(reinterpret_cast<const uint16_t*>(kp + koff + 64 * c));
+        }
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-          d.k[u][r] = load_words<NW, NT>(reinterpret_cast<const uint16_t*>(kp + voff[r]));
-      } else {
-#pragma unroll
-        for (int c = 0; c < QC; ++c)
-          d.kd[u][c] = load_bf16x8<NT>(reinterpret_cast<const uint16_t*>(kp + koff + 64 * c));
+          d.v[u][r] = load_words<NW, NT>(reinterpret_cast<const uint16_t*>(vp + voff[r]));
       }
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        d.v[u][r] = load_words<NW, NT>(reinterpret_cast<const uint16_t*>(vp + voff[r]));
-    }
-  };
+    };
 
-  float m_run = -INFINITY;
-  float l_run = 0.f;
-  f32x4 acc[NV];
-#pragma unroll
-  for (int n = 0; n < NV; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  // keep partition p's result in LDS and start the next partition afresh.
-  // lane (j, g) holds head j, dims NV*(4g + r) + n
-  auto finalize = [&](int p) {
-    float lsum = l_run + __shfl_xor(l_run, 16, 64);
-    lsum += __shfl_xor(lsum, 32, 64);
-    const bool bad = bad_blk;
-    const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
-    const int i = p - p_first;
-    if (j < nh) {
-      float* dst = stage + (i * nhs + j) * SROW;
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-#pragma unroll
-        for (int n0 = 0; n0 < NV; n0 += 4) {
-          float4 o = make_float4(acc[n0][r] * inv, acc[n0 + 1][r] * inv, acc[n0 + 2][r] * inv,
-                                 acc[n0 + 3][r] * inv);
-          if (bad) o = make_float4(NAN, NAN, NAN, NAN);
-          *reinterpret_cast<float4*>(dst + NV * (4 * g + r) + n0) = o;
-        }
-      if (g == 0)
-        *reinterpret_cast<float2*>(stage_ml + 2 * (i * nhs + j)) =
-            make_float2(bad ? NAN : m_run, bad ? NAN : lsum);
-    }
-    m_run = -INFINITY;
-    l_run = 0.f;
+    float m_run = -INFINITY;
+    float l_run = 0.f;
+    f32x4 acc[NV];
 #pragma unroll
     for (int n = 0; n < NV; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
-    bad_blk = false;
-  };
 
-  auto compute = [&](Step& d, int q) {
-    const int ts = tw_begin + q * kStep;
-    if (q > 0 && ts % P == 0) finalize(ts / P - 1);  // a new partition starts here
-    bad_blk = bad_blk || d.bad;
-    const int lim = tw_end - ts;  // valid tokens in this step (>= 1)
-
-    // K tile through LDS: token t of the step is a row of 2D bytes; its
-    // 16-byte chunk ch sits at chunk position (ch + skew(t)) mod NCH, so both
-    // the row-wise writes and the MFMA-layout reads (token j, chunk 4c + g)
-    // hit distinct banks within each 16-lane pass
+    // keep partition p's result in LDS and start the next partition afresh.
+    // lane (j, g) holds head j, dims NV*(4g + r) + n
+    auto finalize = [&](int p) {
+      float lsum = l_run + __shfl_xor(l_run, 16, 64);
+      lsum += __shfl_xor(lsum, 32, 64);
+      const bool bad = bad_blk;
+      const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+      const int i = p - p_first;
+      if (j < nh) {
+        float* dst = stage + (i * nhs + j) * SROW;
 #pragma unroll
-    for (int u = 0; u < 2; ++u)
+        for (int r = 0; r < 4; ++r)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        if constexpr (!KL) break;
-        const int t = 16 * u + 4 * g + r;
-        const int pb = NW * 4;                 // bytes of this lane's piece
-        const int ch = (j * pb) >> 4;          // its 16-byte chunk
-        const int pos = t * (2 * D) + 16 * ((ch + kskew(t)) % NCH) + ((j * pb) & 15);
-        if constexpr (NW == 4) {
-          *reinterpret_cast<u32x4*>(k_lds + pos) = u32x4{d.k[u][r].w[0], d.k[u][r].w[1], d.k[u][r].w[2], d.k[u][r].w[3]};
-        } else {
-          *reinterpret_cast<u32x2*>(k_lds + pos) = u32x2{d.k[u][r].w[0], d.k[u][r].w[1]};
-        }
+          for (int n0 = 0; n0 < NV; n0 += 4) {
+            float4 o = make_float4(acc[n0][r] * inv, acc[n0 + 1][r] * inv, acc[n0 + 2][r] * inv,
+                                   acc[n0 + 3][r] * inv);
+            if (bad) o = make_float4(NAN, NAN, NAN, NAN);
+            *reinterpret_cast<float4*>(dst + NV * (4 * g + r) + n0) = o;
+          }
+        if (g == 0)
+          *reinterpret_cast<float2*>(stage_ml + 2 * (i * nhs + j)) =
+              make_float2(bad ? NAN : m_run, bad ? NAN : lsum);
       }
+      m_run = -INFINITY;
+      l_run = 0.f;
+#pragma unroll
+      for (int n = 0; n < NV; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+      bad_blk = false;
+    };
 
-    // scores
-    float x[2][4];
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      f32x4 sc = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int c = 0; c < QC; ++c) {
-        bf16x8 kf;
-        if constexpr (KL) {
-          const int t = 16 * u + j;
-          const int pos = t * (2 * D) + 16 * ((4 * c + g + kskew(t)) % NCH);
-          kf = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(k_lds + pos));
-        } else {
-          kf = d.kd[u][c];
-        }
-        sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[c], sc, 0, 0, 0);
-      }
-#pragma unroll
-      for (int r = 0; r < 4; ++r) x[u][r] = sc[r] * a.scale_log2;
-    }
-    if (lim < kStep) {  // the sequence ends inside this step: mask scores, zero values
+    auto compute = [&](Step& d, int q) {
+      const int ts = tw_begin + q * kStep;
+      if (q > 0 && ts % P == 0) finalize(ts / P - 1);  // a new partition starts here
+      bad_blk = bad_blk || d.bad;
+      const int lim = tw_end - ts;  // valid tokens in this step (>= 1)
+
+      // K tile through LDS: token t of the step is a row of 2D bytes; its
+      // 16-byte chunk ch sits at chunk position (ch + skew(t)) mod NCH, so both
+      // the row-wise writes and the MFMA-layout reads (token j, chunk 4c + g)
+      // hit distinct banks within each 16-lane pass
 #pragma unroll
       for (int u = 0; u < 2; ++u)
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-          if (16 * u + 4 * g + r >= lim) {
-            x[u][r] = -INFINITY;
-#pragma unroll
-            for (int w = 0; w < NW; ++w) d.v[u][r].w[w] = 0u;
+        for (int r = 0; r < 4; ++r) {
+          if constexpr (!KL) break;
+          const int t = 16 * u + 4 * g + r;
+          const int pb = NW * 4;                 // bytes of this lane's piece
+          const int ch = (j * pb) >> 4;          // its 16-byte chunk
+          const int pos = t * (2 * D) + 16 * ((ch + kskew(t)) % NCH) + ((j * pb) & 15);
+          if constexpr (NW == 4) {
+            *reinterpret_cast<u32x4*>(k_lds + pos) = u32x4{d.k[u][r].w[0], d.k[u][r].w[1], d.k[u][r].w[2], d.k[u][r].w[3]};
+          } else {
+            *reinterpret_cast<u32x2*>(k_lds + pos) = u32x2{d.k[u][r].w[0], d.k[u][r].w[1]};
           }
-    }
+        }
 
-    // online softmax (log2 domain), per head j
-    float mx = x[0][0];
+      // scores
+      float x[2][4];
 #pragma unroll
-    for (int u = 0; u < 2; ++u)
+      for (int u = 0; u < 2; ++u) {
+        f32x4 sc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int r = 0; r < 4; ++r) mx = fmaxf(mx, x[u][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float m_new = fmaxf(m_run, mx);
-    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-    const float alpha = fast_exp2(m_run - m_use);
-    m_run = m_new;
-
-    bf16x8 phi, plo;
-    float psum = 0.f;
+        for (int c = 0; c < QC; ++c) {
+          bf16x8 kf;
+          if constexpr (KL) {
+            const int t = 16 * u + j;
+            const int pos = t * (2 * D) + 16 * ((4 * c + g + kskew(t)) % NCH);
+            kf = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(k_lds + pos));
+          } else {
+            kf = d.kd[u][c];
+          }
+          sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[c], sc, 0, 0, 0);
+        }
 #pragma unroll
-    for (int u = 0; u < 2; ++u)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float pv = fast_exp2(x[u][r] - m_use);
-        psum += pv;
-        const __bf16 hb = static_cast<__bf16>(pv);
-        phi[4 * u + r] = hb;
-        plo[4 * u + r] = static_cast<__bf16>(pv - static_cast<float>(hb));
+        for (int r = 0; r < 4; ++r) x[u][r] = sc[r] * a.scale_log2;
       }
-    l_run = l_run * alpha + psum;
-
-    // V^T operand for output block n: the 8 tokens' value of dim NV*j + n
+      if (lim < kStep) {  // the sequence ends inside this step: mask scores, zero values
 #pragma unroll
-    for (int n = 0; n < NV; ++n) {
-      const uint32_t sel = (n & 1) ? 0x07060302u : 0x05040100u;
-      u32x4 va;
+        for (int u = 0; u < 2; ++u)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int e0 = 2 * e, e1 = 2 * e + 1;  // token slots (u = e/4, r = e%4)
-        va[e] = __builtin_amdgcn_perm(d.v[e1 >> 2][e1 & 3].w[n >> 1], d.v[e0 >> 2][e0 & 3].w[n >> 1], sel);
+          for (int r = 0; r < 4; ++r)
+            if (16 * u + 4 * g + r >= lim) {
+              x[u][r] = -INFINITY;
+#pragma unroll
+              for (int w = 0; w < NW; ++w) d.v[u][r].w[w] = 0u;
+            }
       }
-      const bf16x8 vb = __builtin_bit_cast(bf16x8, va);
-      f32x4 o = acc[n] * alpha;
-      o = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vb, phi, o, 0, 0, 0);
-      o = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vb, plo, o, 0, 0, 0);
-      acc[n] = o;
-    }
-  };
 
-  // two register buffers: the next step's loads are in flight while the
-  // current step computes (also across partition boundaries)
-  Step bufA, bufB;
-  if (my_steps > 0) issue(bufA, 0);
-  for (int q = 0; q < my_steps; q += 2) {
-    if (q + 1 < my_steps) issue(bufB, q + 1);
-    compute(bufA, q);
-    if (q + 1 >= my_steps) break;
-    if (q + 2 < my_steps) issue(bufA, q + 2);
-    compute(bufB, q + 1);
+      // online softmax (log2 domain), per head j
+      float mx = x[0][0];
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) mx = fmaxf(mx, x[u][r]);
+      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      const float m_new = fmaxf(m_run, mx);
+      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+      const float alpha = fast_exp2(m_run - m_use);
+      m_run = m_new;
+
+      bf16x8 phi, plo;
+      float psum = 0.f;
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float pv = fast_exp2(x[u][r] - m_use);
+          psum += pv;
+          const __bf16 hb = static_cast<__bf16>(pv);
+          phi[4 * u + r] = hb;
+          plo[4 * u + r] = static_cast<__bf16>(pv - static_cast<float>(hb));
+        }
+      l_run = l_run * alpha + psum;
+
+      // V^T operand for output block n: the 8 tokens' value of dim NV*j + n
+#pragma unroll
+      for (int n = 0; n < NV; ++n) {
+        const uint32_t sel = (n & 1) ? 0x07060302u : 0x05040100u;
+        u32x4 va;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int e0 = 2 * e, e1 = 2 * e + 1;  // token slots (u = e/4, r = e%4)
+          va[e] = __builtin_amdgcn_perm(d.v[e1 >> 2][e1 & 3].w[n >> 1], d.v[e0 >> 2][e0 & 3].w[n >> 1], sel);
+        }
+        const bf16x8 vb = __builtin_bit_cast(bf16x8, va);
+        f32x4 o = acc[n] * alpha;
+        o = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vb, phi, o, 0, 0, 0);
+        o = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vb, plo, o, 0, 0, 0);
+        acc[n] = o;
+      }
+    };
+
+    // two register buffers: the next step's loads are in flight while the
+    // current step computes (also across partition boundaries)
+    Step bufA, bufB;
+    if (my_steps > 0) issue(bufA, 0);
+    for (int q = 0; q < my_steps; q += 2) {
+      if (q + 1 < my_steps) issue(bufB, q + 1);
+      compute(bufA, q);
+      if (q + 1 >= my_steps) break;
+      if (q + 2 < my_steps) issue(bufA, q + 2);
+      compute(bufB, q + 1);
+    }
+    // the last partition (or, for an empty sequence, its zero output)
+    const int p_last = my_steps > 0 ? (tw_begin + (my_steps - 1) * kStep) / P : p_first;
+    finalize(p_last);
+    __builtin_amdgcn_wave_barrier();
+    for (int i = 0; i <= p_last - p_first; ++i) store_rows(i);
+  };  // item
+
+  if (!a.compact) {
+    item(s_dense, blockIdx.y, blockIdx.x);
+    return;
   }
-  // the last partition (or, for an empty sequence, its zero output)
-  const int p_last = my_steps > 0 ? (tw_begin + (my_steps - 1) * kStep) / P : p_first;
-  finalize(p_last);
-  __builtin_amdgcn_wave_barrier();
-  for (int i = 0; i <= p_last - p_first; ++i) store_rows(i);
+  for (int it = blockIdx.x; it < total; it += gridDim.x) {
+    // the sequence whose items contain it: the last s with s_seq[s] <= it
+    int lo = 0, hi2 = a.S - 1;
+    while (lo < hi2) {
+      const int mid = (lo + hi2 + 1) >> 1;
+      if (s_seq[mid] <= it) lo = mid; else hi2 = mid - 1;
+    }
+    const int nruns = (s_seq[lo + 1] - s_seq[lo]) / Y;
+    const int local = it - s_seq[lo];
+    const int yy = local / nruns;
+    item(lo, yy, local - yy * nruns);
+    // the wave's LDS is reused by the next item: finish reading it first
+    __builtin_amdgcn_wave_barrier();
+  }
+}
+
+// Workgroups of this kernel that one CU holds with `lds` bytes of dynamic LDS.
+template <typename K>
+int resident_per_cu(K kern, size_t lds) {
+  static std::mutex mu;
+  static size_t cached_lds = 0;
+  static int cached = 0;
+  std::lock_guard<std::mutex> lock(mu);
+  if (cached == 0 || cached_lds != lds) {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, reinterpret_cast<const void*>(kern), kThreads,
+                                                     lds) != hipSuccess || n <= 0)
+      n = 1;
+    cached = n;
+    cached_lds = lds;
+  }
+  return cached;
 }
 
 template <int D, int B, int HG, bool NT, bool KL>
@@ -456,6 +541,19 @@ int launch_one(const AttnArgs& a, dim3 grid, size_t lds, hipStream_t stream) {
       return PKV_ERR_HIP;
     }
     attr_set = true;
+  }
+  if (a.compact) {
+    // one round of resident workgroups walks the item list (never more
+    // workgroups than the dense grid has)
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) {
+      set_error("paged attention (bf16): cannot query the device");
+      return PKV_ERR_HIP;
+    }
+    const int64_t dense = static_cast<int64_t>(grid.x) * grid.y * grid.z;
+    grid = dim3(static_cast<unsigned>(std::min<int64_t>(dense, static_cast<int64_t>(cus) *
+                                                                   resident_per_cu(kern, lds))));
   }
   kern<<<grid, dim3(kThreads), lds, stream>>>(a);
   return check_launch("paged attention (bf16)");

@@ -77,10 +77,13 @@ struct AttnArgs {
   int parts_per_wg;   // partitions one workgroup covers (bf16 path)
   int longest_first;  // map workgroups to sequences in decreasing length
   int k_via_lds;      // load keys row-wise and rearrange them through LDS
+  int compact;        // bf16: workgroups walk a compact list of work items
 };
 
 // largest batch whose bf16 workgroups rank the sequences by length
 constexpr int kMaxRankedSeqs = 128;
+// largest batch whose bf16 workgroups can number the work items themselves
+constexpr int kMaxCompactSeqs = 512;
 
 // kv heads per bf16 workgroup: 4 when they divide Hkv, else 2, else 1
 inline int bf16_heads_per_group(int Hkv) { return Hkv % 4 == 0 ? 4 : (Hkv % 2 == 0 ? 2 : 1); }
@@ -97,9 +100,9 @@ __host__ __device__ inline int bf16_lds_wave_floats(int pps, int G, int D, bool 
 inline size_t bf16_lds_bytes(int pps, int G, int D, bool k_tile) {
   return static_cast<size_t>(4) * bf16_lds_wave_floats(pps, G, D, k_tile) * sizeof(float);
 }
-// at most this much (plus ~1 KB of static LDS), so that two workgroups fit
+// at most this much (plus ~2 KB of static LDS), so that two workgroups fit
 // in a CU's 160 KB
-inline size_t bf16_lds_limit() { return 78 * 1024; }
+inline size_t bf16_lds_limit() { return 77 * 1024; }
 
 int launch_attention_bf16(const AttnArgs& a, hipStream_t stream);
 int launch_attention_f32(const AttnArgs& a, hipStream_t stream);

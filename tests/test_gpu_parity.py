@@ -264,6 +264,32 @@ def test_result_does_not_depend_on_work_split():
     assert np.array_equal(one[0].view(np.uint32), two[0].view(np.uint32))
 
 
+def test_compact_item_list_matches_dense_grid_bit_for_bit():
+    """A batch of at most 512 sequences whose contexts span several workgroup
+    runs walks a compact list of work items; a larger one uses the dense grid.
+    The first 64 sequences of a 600-sequence batch give the same bits either
+    way -- also with 32-token partitions, where each workgroup of the compact
+    launch takes many items -- and agree with the oracle."""
+    rng = np.random.default_rng(12)
+    lens = rng.integers(16, 1200, 600)
+    w = workloads.custom(13, lens, dtype="bf16", num_q_heads=8, num_kv_heads=2, head_size=128,
+                         block_size=16)
+    st = H.upload(w)
+    n = 64
+    sub = [t[:n].contiguous() for t in (st.query, st.tables, st.lens)]
+    for P in (32, 256):
+        say(f"[compact] P={P}")
+        dense = H.attend(st, partition_size=P).cpu().numpy()[:n]
+        compact = pkv.attention_decode(*sub[:1], st.kv, *sub[1:], w.scale, int(lens[:n].max()),
+                                       partition_size=P).cpu().numpy()
+        assert np.array_equal(dense.view(np.uint32), compact.view(np.uint32)), f"P={P}"
+    for s in (0, int(np.argmax(lens[:n])), int(np.argmin(lens[:n])), 40):
+        k, v = w.logical_kv(s)
+        ref = oracle.attention_ref(oracle.to_f64(w.query[s], "bf16"), oracle.to_f64(k, "bf16"),
+                                   oracle.to_f64(v, "bf16"), w.scale)
+        _check_rows(compact[s], ref, 2e-3, f"compact seq {s} (L={lens[s]})")
+
+
 def test_bf16_output_is_rounded_fp32_output():
     w = workloads.long_context(num_seqs=2, context_len=2000)
     st = H.upload(w)
