@@ -133,12 +133,13 @@ int paged_kv_gather(void* k_out, void* v_out, const void* kv_cache, const int32_
                     pkv_dtype dtype, hipStream_t stream);
 
 /*
- * Partition size the decode kernel will use for these arguments: a request of
- * 0 selects one from the shapes (bf16: whole sequences when the batch has
- * enough (sequence, kv-head group) work items to fill the GPU, else 512
- * tokens; fp32: 64 tokens); otherwise the request is returned if it is a
- * positive multiple of 32 and of block_size (fp32: at most 512), else -1.
- * Host only.
+ * Partition size the decode kernel will use for these arguments.  A request
+ * of 0 selects the split automatically.  bf16: whole sequences when the batch
+ * has enough (sequence, kv-head group) work items to fill the GPU; otherwise
+ * 0, the stream schedule: each wave of a persistent grid reads an equal share
+ * of the batch's K/V, cutting contexts wherever the shares end.  fp32: 64
+ * tokens.  A positive request is returned if it is a multiple of 32 and of
+ * block_size (fp32: at most 512), else -1.  Host only.
  */
 int paged_attention_partition_size(int num_seqs, int num_q_heads, int num_kv_heads, int head_size,
                                    int block_size, int max_context_len, int partition_size,
@@ -146,7 +147,9 @@ int paged_attention_partition_size(int num_seqs, int num_q_heads, int num_kv_hea
 
 /*
  * Workspace bytes paged_attention_decode needs for these arguments (0 when
- * every sequence fits in one partition).  Host only.
+ * every sequence fits in one partition).  The stream schedule always needs
+ * one, sized for the current device's compute units: query it on the device
+ * the call will run on.  Host only.
  */
 size_t paged_attention_workspace_bytes(int num_seqs, int num_q_heads, int num_kv_heads,
                                        int head_size, int block_size, int max_context_len,
@@ -168,9 +171,11 @@ size_t paged_attention_workspace_bytes(int num_seqs, int num_q_heads, int num_kv
  * where K_s[t] = kv_cache[0][table[s][t / B]][t % B] and V_s likewise.
  * context_lens[s] counts every token attended, including the one written this
  * step; a sequence of length 0 gets zeros.  Long contexts are split into
- * partitions of `partition_size` tokens whose softmax statistics are merged by
- * the log-sum-exp rule; the result does not depend on the split beyond
- * rounding.  Accumulation is fp32.
+ * partitions -- of `partition_size` tokens, or, under the stream schedule,
+ * wherever one wave's share of the batch ends -- whose softmax statistics are
+ * merged by the log-sum-exp rule; the result does not depend on the split
+ * beyond rounding, and repeated calls on the same GPU model give identical
+ * bits.  Accumulation is fp32.
  *
  *   out           out_dtype [num_seqs][num_q_heads][head_size]      (output)
  *   query         dtype [num_seqs][num_q_heads][head_size]
@@ -178,8 +183,10 @@ size_t paged_attention_workspace_bytes(int num_seqs, int num_q_heads, int num_kv
  *   block_tables  int32 [num_seqs][table_width]; entries past a sequence's
  *                 last block are never read
  *   context_lens  int32 [num_seqs], 0 <= L <= min(max_context_len, table_width*B)
- *   max_context_len  host int, an upper bound of context_lens (sizes the grid)
- *   partition_size   0 = chosen by the library, else a multiple of 32 and of B
+ *   max_context_len  host int, an upper bound of context_lens (sizes the grid
+ *                 of fixed partitions)
+ *   partition_size   0 = chosen by the library (see
+ *                 paged_attention_partition_size), else a multiple of 32 and of B
  *   flags         0 or PKV_ATTN_CACHED_KV
  *   workspace     device scratch of at least paged_attention_workspace_bytes()
  *                 bytes (may be NULL when that is 0), 256-byte aligned

@@ -2,6 +2,7 @@
 // dispatch to the kernels.  Nothing here touches device memory contents.
 #include "common.hpp"
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <string>
@@ -96,6 +97,50 @@ int bf16_parts_per_wg(int S, int Hq, int Hkv, int D, int max_parts, bool k_tile)
   return static_cast<int>(pps) * nslot;
 }
 
+// The stream schedule serves bf16 caches with automatic partitioning when
+// the batch has too few (sequence, kv-head group) work units to fill the GPU
+// with whole sequences -- ragged batches, long contexts -- and every
+// sequence's length fits its scan.
+bool uses_stream(int S, int Hq, int Hkv, int max_len, int req, pkv_dtype dtype) {
+  if (dtype != PKV_BF16 || req != 0 || S > kMaxStreamSeqs) return false;
+  // whole sequences when the batch alone fills the GPU (no merge pass)
+  if (bf16_units(S, Hq, Hkv) >= kResidentGroups) return false;
+  // stream steps are counted in 32-bit integers
+  const int G = Hq / Hkv;
+  const int64_t steps = static_cast<int64_t>(S) * Hkv * ((G + 15) / 16) * (max_len / 32 + 1);
+  return steps < (int64_t{1} << 31);
+}
+
+// Waves of the stream schedule's persistent grid on the current device.
+int stream_waves(int D) {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus <= 0)
+    return 0;
+  return cus * stream_wgs_per_cu(D) * 4;
+}
+
+// Workspace of the stream schedule: one partial-result slot (nhs rows of D
+// floats and their (m, l)) per wave and per (sequence, kv head, query-head
+// chunk) -- a piece of the stream is named by piece + pair, so that many
+// slots cover every piece -- then the scan of the lengths, which tells the
+// merge where each unit was cut.
+struct StreamLayout {
+  int64_t ml_off, pref_off, bytes;
+};
+StreamLayout stream_layout(int S, int Hq, int Hkv, int D, int waves) {
+  const int G = Hq / Hkv;
+  const int64_t units = static_cast<int64_t>(S) * Hkv * ((G + 15) / 16);
+  const int64_t rows = (static_cast<int64_t>(waves) + units) * std::min(16, G);
+  auto up256 = [](int64_t b) { return (b + 255) / 256 * 256; };
+  StreamLayout l;
+  l.ml_off = up256(rows * D * 4);
+  l.pref_off = l.ml_off + up256(rows * 2 * 4);
+  l.bytes = l.pref_off + up256(static_cast<int64_t>(S + 1) * 4);
+  return l;
+}
+
 }  // namespace
 }  // namespace pkv
 
@@ -178,6 +223,8 @@ int paged_attention_partition_size(int num_seqs, int num_q_heads, int num_kv_hea
   clear_error();
   if (!shape_ok(num_seqs, num_q_heads, num_kv_heads, head_size, block_size, max_context_len, dtype))
     return -1;
+  if (uses_stream(num_seqs, num_q_heads, num_kv_heads, max_context_len, partition_size, dtype))
+    return 0;
   const int P = resolve_partition(num_seqs, num_q_heads, num_kv_heads, head_size, block_size,
                                   max_context_len, partition_size, dtype);
   if (P < 0) set_error("partition_size %d is not a positive multiple of %d (fp32: at most 512)",
@@ -190,6 +237,12 @@ size_t paged_attention_workspace_bytes(int num_seqs, int num_q_heads, int num_kv
                                        int partition_size, pkv_dtype dtype) {
   const int P = paged_attention_partition_size(num_seqs, num_q_heads, num_kv_heads, head_size,
                                                block_size, max_context_len, partition_size, dtype);
+  if (P == 0 && num_seqs > 0) {
+    const int waves = stream_waves(head_size);
+    return waves > 0 ? static_cast<size_t>(
+                           stream_layout(num_seqs, num_q_heads, num_kv_heads, head_size, waves).bytes)
+                     : 0;
+  }
   if (P <= 0) return 0;
   const int64_t parts = cdiv64(std::max(max_context_len, 1), P);
   if (parts <= 1) return 0;
@@ -203,6 +256,62 @@ size_t paged_attention_workspace_bytes(int num_seqs, int num_q_heads, int num_kv
 namespace {
 
 enum Phase { kAttend = 1, kMerge = 2 };
+
+// The stream schedule (arguments already checked).
+int decode_stream(int phases, void* out, pkv_dtype out_dtype, const void* query,
+                  const void* kv_cache, const int32_t* block_tables, int table_width,
+                  const int32_t* context_lens, int num_seqs, int num_q_heads, int num_kv_heads,
+                  int head_size, int block_size, int num_blocks, float scale, int max_context_len,
+                  void* workspace, size_t workspace_bytes, pkv_dtype dtype, unsigned flags,
+                  hipStream_t stream) {
+  const int waves = stream_waves(head_size);
+  if (waves <= 0) {
+    set_error("cannot query the current device");
+    return PKV_ERR_HIP;
+  }
+  const StreamLayout lay = stream_layout(num_seqs, num_q_heads, num_kv_heads, head_size, waves);
+  if (!workspace || workspace_bytes < static_cast<size_t>(lay.bytes)) {
+    set_error("workspace of %zu bytes is smaller than the %lld needed", workspace_bytes,
+              static_cast<long long>(lay.bytes));
+    return PKV_ERR_WORKSPACE;
+  }
+  if (reinterpret_cast<uintptr_t>(workspace) & 255u) {
+    set_error("workspace must be 256-byte aligned");
+    return PKV_ERR_INVALID;
+  }
+  AttnArgs a{};
+  a.out = out;
+  a.query = query;
+  a.kv = kv_cache;
+  a.tables = block_tables;
+  a.lens = context_lens;
+  a.width = table_width;
+  a.S = num_seqs;
+  a.Hq = num_q_heads;
+  a.Hkv = num_kv_heads;
+  a.D = head_size;
+  a.B = block_size;
+  a.NB = num_blocks;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.out_bf16 = out_dtype == PKV_BF16 ? 1 : 0;
+  a.nontemporal = (flags & PKV_ATTN_CACHED_KV) ? 0 : 1;
+  a.k_via_lds = static_cast<int64_t>(num_kv_heads) * head_size * elem_bytes(dtype) >= 4096;
+  a.max_len = max_context_len;
+  a.stream = 1;
+  a.stream_waves = waves;
+  stream_lds_plan(num_q_heads / num_kv_heads, head_size, a.k_via_lds != 0, &a.stream_slots,
+                  &a.stream_wave_floats);
+  char* ws = static_cast<char*>(workspace);
+  a.ws_o = reinterpret_cast<float*>(ws);
+  a.ws_ml = reinterpret_cast<float*>(ws + lay.ml_off);
+  a.ws_pref = reinterpret_cast<int*>(ws + lay.pref_off);
+  if (phases & kAttend) {
+    const int rc = launch_attention_bf16(a, stream);
+    if (rc != PKV_OK) return rc;
+  }
+  if (phases & kMerge) return launch_reduce(a, stream);
+  return PKV_OK;
+}
 
 int decode_impl(int phases, void* out, pkv_dtype out_dtype, const void* query,
                 const void* kv_cache, const int32_t* block_tables, int table_width,
@@ -246,6 +355,11 @@ int decode_impl(int phases, void* out, pkv_dtype out_dtype, const void* query,
     set_error("out, query and kv_cache must be 16-byte aligned");
     return PKV_ERR_INVALID;
   }
+  if (uses_stream(num_seqs, num_q_heads, num_kv_heads, max_context_len, partition_size, dtype))
+    return decode_stream(phases, out, out_dtype, query, kv_cache, block_tables, table_width,
+                         context_lens, num_seqs, num_q_heads, num_kv_heads, head_size, block_size,
+                         num_blocks, scale, max_context_len, workspace, workspace_bytes, dtype,
+                         flags, stream);
   const int P = resolve_partition(num_seqs, num_q_heads, num_kv_heads, head_size, block_size,
                                   max_context_len, partition_size, dtype);
   if (P <= 0) {

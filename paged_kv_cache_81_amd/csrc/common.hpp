@@ -78,15 +78,37 @@ struct AttnArgs {
   int longest_first;  // map workgroups to sequences in decreasing length
   int k_via_lds;      // load keys row-wise and rearrange them through LDS
   int compact;        // bf16: workgroups walk a compact list of work items
+  // stream schedule (bf16, automatic partitioning)
+  int stream;              // use it
+  int stream_waves;        // waves of the persistent grid (a multiple of 4)
+  int stream_slots;        // finished results a wave keeps in LDS before storing
+  int stream_wave_floats;  // LDS floats of one wave
+  int* ws_pref;            // [S + 1] first stream step of each sequence
+  int max_len;             // longest valid context (longer ones give NaN)
 };
+
+// Stream schedule: wave w of W reads stream steps [start(w), start(w + 1))
+// of the T in the batch.  With T >= W every piece has floor(T/W) or one more
+// steps; with fewer steps than waves, wave w < T gets step w alone and the
+// rest none -- never an empty piece between two others.
+__host__ __device__ inline int stream_piece_start(int64_t w, int64_t T, int64_t W) {
+  return static_cast<int>(T >= W ? w * T / W : (w < T ? w : T));
+}
+// The wave whose piece holds step x (0 <= x < T).
+__host__ __device__ inline int64_t stream_wave_of(int64_t x, int64_t T, int64_t W) {
+  return T >= W ? ((x + 1) * W - 1) / T : x;
+}
 
 // largest batch whose bf16 workgroups rank the sequences by length
 constexpr int kMaxRankedSeqs = 128;
 // largest batch whose bf16 workgroups can number the work items themselves
 constexpr int kMaxCompactSeqs = 512;
+// largest batch the stream schedule takes (its workgroups scan the lengths);
+// it serves batches of fewer than 512 (sequence, kv-head group) units
+constexpr int kMaxStreamSeqs = 512;
 
 // kv heads per bf16 workgroup: 4 when they divide Hkv, else 2, else 1
-inline int bf16_heads_per_group(int Hkv) { return Hkv % 4 == 0 ? 4 : (Hkv % 2 == 0 ? 2 : 1); }
+__host__ __device__ inline int bf16_heads_per_group(int Hkv) { return Hkv % 4 == 0 ? 4 : (Hkv % 2 == 0 ? 2 : 1); }
 
 // LDS of one bf16 workgroup: for each of its 4 waves, a 32-token K tile
 // (32 x D bf16), then pps partition slots of min(16, G) head rows (D + 4
@@ -103,6 +125,32 @@ inline size_t bf16_lds_bytes(int pps, int G, int D, bool k_tile) {
 // at most this much (plus ~2 KB of static LDS), so that two workgroups fit
 // in a CU's 160 KB
 inline size_t bf16_lds_limit() { return 77 * 1024; }
+
+// Stream schedule: workgroups per CU of the persistent grid (what the
+// kernel's registers allow: 3 for head size 64, 2 for 128).
+inline int stream_wgs_per_cu(int D) { return D == 64 ? 3 : 2; }
+// Ints describing where a stream result slot goes.
+constexpr int kStreamMeta = 3;
+// LDS floats per result slot: nhs rows of D + 4, their (m, l), and the
+// slot's description.
+inline int stream_slot_floats(int G, int D) {
+  const int nhs = G < 16 ? G : 16;
+  return nhs * (D + 4) + 2 * nhs + kStreamMeta;
+}
+// Result slots per wave and LDS floats per wave: what is left of the CU's
+// 160 KB, shared by the resident workgroups, after the static scan array and
+// the K tile; at most 16 slots.
+inline void stream_lds_plan(int G, int D, bool k_tile, int* slots, int* wave_floats) {
+  const size_t static_bytes = (kMaxStreamSeqs + 1 + 4) * sizeof(int) + 256;
+  size_t per_wg = 160 * 1024 / stream_wgs_per_cu(D) - static_bytes;
+  if (per_wg > bf16_lds_limit()) per_wg = bf16_lds_limit();
+  const int per_wave = static_cast<int>(per_wg / 4 / sizeof(float));
+  const int tile = k_tile ? 16 * D : 0;
+  int k = (per_wave - tile) / stream_slot_floats(G, D);
+  k = k < 1 ? 1 : (k > 16 ? 16 : k);
+  *slots = k;
+  *wave_floats = (tile + k * stream_slot_floats(G, D) + 3) / 4 * 4;
+}
 
 int launch_attention_bf16(const AttnArgs& a, hipStream_t stream);
 int launch_attention_f32(const AttnArgs& a, hipStream_t stream);

@@ -1,11 +1,11 @@
 // Log-sum-exp merge of context partitions.
 //
-// For each (sequence, query head) split into n > 1 partitions with statistics
-// (m_p, l_p, o_p) -- m in log2 units, o normalised, stored in the workspace
-// as rows [s][p][h] -- the output is
+// For each (sequence, query head) whose context was split into n > 1 parts
+// with statistics (m_p, l_p, o_p) -- m in log2 units, o normalised -- the
+// output is
 //     M = max_p m_p,  w_p = l_p * 2^(m_p - M),  out = sum_p w_p o_p / sum_p w_p.
-// One wave per (sequence, head); sequences held in one partition were written
-// by the attention kernel directly and are skipped here.
+// One wave per (sequence, query head); heads whose context was read in one
+// part were written by the attention kernel directly and are skipped here.
 #include "common.hpp"
 
 #include <cmath>
@@ -13,86 +13,194 @@
 namespace pkv {
 namespace {
 
+constexpr int kWaves = 4;
+
+// Merge the np parts of one (sequence, head): statistics (m, l) at
+// ml[2 * stride * p] and ml[2 * stride * p + 1], normalised rows at
+// o[stride * D * p]; the result goes to out at out_off.  Lane (g, d4) covers
+// dims 4*d4 .. 4*d4+3 of parts p = g, g + NG, ...: the rows of the first 64
+// parts are loaded in one round together with their statistics (lane p holds
+// part p's), whose weights then reach the row lanes by shuffles; further
+// parts follow eight loads at a time.  The NG row groups are combined across
+// lanes.  A poisoned part (NaN statistics) poisons the row.
 template <int D>
-__global__ void __launch_bounds__(64) reduce_kernel(AttnArgs a) {
-  constexpr int PER = D / 64;
-  extern __shared__ float s_w[];
-  const int sh = blockIdx.x;
-  const int s = sh / a.Hq;
-  const int lane = threadIdx.x;
+__device__ __forceinline__ void merge_parts(const AttnArgs& a, const float* ml, const float* o,
+                                            int64_t stride, int np, int64_t out_off) {
+  constexpr int G4 = D / 4;    // lanes per row
+  constexpr int NG = 64 / G4;  // rows per load instruction
+  constexpr int U = 64 / NG;   // first-round rows per lane: parts 0 .. 63
+  const int lane = threadIdx.x & 63;
+  const int g = lane / G4;
+  const int d4 = lane - g * G4;
+  const float4 zero = make_float4(0.f, 0.f, 0.f, 0.f);
+
+  // rows past the last part repeat it (with weight 0), so that within the
+  // rounds that hold a part every lane loads
+  float4 v[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    if (NG * u < np) {
+      const int p = min(g + NG * u, np - 1);
+      v[u] = *reinterpret_cast<const float4*>(o + stride * D * p + 4 * d4);
+    } else {
+      v[u] = zero;
+    }
+  }
+  float m0 = -INFINITY, l0 = 0.f;  // statistics of part `lane`
+  if (lane < np) {
+    m0 = ml[2 * stride * lane];
+    l0 = ml[2 * stride * lane + 1];
+  }
+  // running (max, sum) of the lane's parts lane, lane + 64, ..., rescaled as
+  // the max grows; then the lanes are combined
+  float m_l = m0, d_l = l0;
+  for (int p = lane + 64; p < np; p += 64) {
+    const float m = ml[2 * stride * p];
+    const float l = ml[2 * stride * p + 1];
+    if (m > m_l) {
+      d_l = d_l * __builtin_amdgcn_exp2f(m_l - m) + l;
+      m_l = m;
+    } else {
+      d_l += l * __builtin_amdgcn_exp2f(m - m_l);
+    }
+  }
+  const float M = wave_max(m_l);
+  const float Mu = (M == -INFINITY) ? 0.f : M;
+  const float den = wave_sum(m_l == -INFINITY ? d_l : d_l * __builtin_amdgcn_exp2f(m_l - Mu));
+
+  const float w_lane = lane < np ? l0 * __builtin_amdgcn_exp2f(m0 - Mu) : 0.f;
+  float4 acc = zero;
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const float w = __shfl(w_lane, g + NG * u, 64);
+    acc.x = fmaf(w, v[u].x, acc.x);
+    acc.y = fmaf(w, v[u].y, acc.y);
+    acc.z = fmaf(w, v[u].z, acc.z);
+    acc.w = fmaf(w, v[u].w, acc.w);
+  }
+  constexpr int U2 = 8;
+  for (int p0 = 64 + g; p0 < np; p0 += NG * U2) {
+    float4 r[U2];
+    float w[U2];
+#pragma unroll
+    for (int u = 0; u < U2; ++u) {
+      const int p = min(p0 + NG * u, np - 1);
+      r[u] = *reinterpret_cast<const float4*>(o + stride * D * p + 4 * d4);
+      w[u] = p0 + NG * u < np
+                 ? ml[2 * stride * p + 1] * __builtin_amdgcn_exp2f(ml[2 * stride * p] - Mu)
+                 : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < U2; ++u) {
+      acc.x = fmaf(w[u], r[u].x, acc.x);
+      acc.y = fmaf(w[u], r[u].y, acc.y);
+      acc.z = fmaf(w[u], r[u].z, acc.z);
+      acc.w = fmaf(w[u], r[u].w, acc.w);
+    }
+  }
+#pragma unroll
+  for (int m = G4; m < 64; m <<= 1) {
+    acc.x += __shfl_xor(acc.x, m, 64);
+    acc.y += __shfl_xor(acc.y, m, 64);
+    acc.z += __shfl_xor(acc.z, m, 64);
+    acc.w += __shfl_xor(acc.w, m, 64);
+  }
+  if (g == 0) {
+    const float inv = 1.f / den;
+    const float4 r = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+    const int64_t off = out_off + 4 * d4;
+    if (a.out_bf16) {
+      const uint32_t lo = f32_to_bf16(r.x) | (static_cast<uint32_t>(f32_to_bf16(r.y)) << 16);
+      const uint32_t hi = f32_to_bf16(r.z) | (static_cast<uint32_t>(f32_to_bf16(r.w)) << 16);
+      *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + off) = make_uint2(lo, hi);
+    } else {
+      *reinterpret_cast<float4*>(static_cast<float*>(a.out) + off) = r;
+    }
+  }
+}
+
+// Fixed partitions: partition p of (s, h) is workspace row (s*P + p)*Hq + h.
+template <int D>
+__global__ void __launch_bounds__(64 * kWaves) reduce_kernel(AttnArgs a) {
+  const int wv = threadIdx.x >> 6;
+  const int64_t sh = static_cast<int64_t>(blockIdx.x) * kWaves + wv;
+  if (sh >= static_cast<int64_t>(a.S) * a.Hq) return;
+  const int s = static_cast<int>(sh / a.Hq);
+  const int h = static_cast<int>(sh - static_cast<int64_t>(s) * a.Hq);
+  const int lane = threadIdx.x & 63;
   const int L = a.lens[s];
   const int P = a.partition;
   const int n = L > 0 ? (L + P - 1) / P : 1;
   const bool bad = L < 0 || (L + a.B - 1) / a.B > a.width || n > a.max_parts;
-  const int64_t out_off = static_cast<int64_t>(sh) * D + lane * PER;
   if (!bad && n <= 1) return;
-
-  float res[PER];
   if (bad) {
-#pragma unroll
-    for (int e = 0; e < PER; ++e) res[e] = NAN;
-  } else {
-    // workspace rows are [s][p][h]: partition p of (s, h) is row (s*P + p)*Hq + h
-    const int h = sh - s * a.Hq;
-    const int64_t pstride = a.Hq;  // rows between consecutive partitions
-    const int64_t row0 = static_cast<int64_t>(s) * a.max_parts * a.Hq + h;
-    const float* ml = a.ws_ml + 2 * row0;
-    const float* o = a.ws_o + row0 * D + lane * PER;
-    float M = -INFINITY;
-    for (int p = lane; p < n; p += 64) M = fmaxf(M, ml[2 * pstride * p]);
-    M = wave_max(M);
-    const float Mu = (M == -INFINITY) ? 0.f : M;
-    float den = 0.f;
-    for (int p = lane; p < n; p += 64) {
-      const float w = ml[2 * pstride * p + 1] * __builtin_amdgcn_exp2f(ml[2 * pstride * p] - Mu);
-      s_w[p] = w;
-      den += w;
+    for (int d = lane; d < D; d += 64) {
+      if (a.out_bf16)
+        static_cast<uint16_t*>(a.out)[sh * D + d] = f32_to_bf16(NAN);
+      else
+        static_cast<float*>(a.out)[sh * D + d] = NAN;
     }
-    den = wave_sum(den);
-    __syncthreads();
-    float acc[PER];
-#pragma unroll
-    for (int e = 0; e < PER; ++e) acc[e] = 0.f;
-    int p = 0;
-    for (; p + 4 <= n; p += 4) {
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const float w = s_w[p + k];
-#pragma unroll
-        for (int e = 0; e < PER; ++e) acc[e] = fmaf(w, o[(p + k) * pstride * D + e], acc[e]);
-      }
-    }
-    for (; p < n; ++p) {
-      const float w = s_w[p];
-#pragma unroll
-      for (int e = 0; e < PER; ++e) acc[e] = fmaf(w, o[p * pstride * D + e], acc[e]);
-    }
-    const float inv = 1.f / den;
-#pragma unroll
-    for (int e = 0; e < PER; ++e) res[e] = acc[e] * inv;
+    return;
   }
-#pragma unroll
-  for (int e = 0; e < PER; ++e) {
-    if (a.out_bf16)
-      static_cast<uint16_t*>(a.out)[out_off + e] = f32_to_bf16(res[e]);
-    else
-      static_cast<float*>(a.out)[out_off + e] = res[e];
-  }
+  const int64_t row0 = static_cast<int64_t>(s) * a.max_parts * a.Hq + h;
+  merge_parts<D>(a, a.ws_ml + 2 * row0, a.ws_o + row0 * D, a.Hq, n, sh * D);
+}
+
+// Stream schedule: unit r = (sequence s, group of HG kv heads, query-head
+// chunk) covers stream steps [g0, g0 + n).  The pieces holding its first and
+// last steps are w0 and w1 (stream_wave_of).  If they are the same piece the
+// unit was finished there; else each piece w0 .. w1 read a non-empty part of
+// it and left a partial result in workspace slot w + r, rows [kv head in
+// the group][query head].
+template <int D>
+__global__ void __launch_bounds__(64 * kWaves) reduce_stream_kernel(AttnArgs a) {
+  const int wv = threadIdx.x >> 6;
+  const int64_t sh = static_cast<int64_t>(blockIdx.x) * kWaves + wv;
+  if (sh >= static_cast<int64_t>(a.S) * a.Hq) return;
+  const int s = static_cast<int>(sh / a.Hq);
+  const int h = static_cast<int>(sh - static_cast<int64_t>(s) * a.Hq);
+  const int G = a.Hq / a.Hkv;
+  const int chunks = (G + 15) >> 4;
+  const int HG = bf16_heads_per_group(a.Hkv);
+  const int Y = (a.Hkv / HG) * chunks;
+  const int nhs = min(16, G);
+  const int kvh = h / G;
+  const int jh = h - kvh * G;  // query head inside the kv head's group
+  const int chunk = jh >> 4;
+  const int hh = jh & 15;
+  const int hg = kvh / HG;
+  const int hi = kvh - hg * HG;
+  const int y = hg * chunks + chunk;
+  const int64_t r = static_cast<int64_t>(s) * Y + y;
+
+  const int64_t T = a.ws_pref[a.S];
+  const int64_t W = a.stream_waves / HG;  // pieces of the attention launch
+  const int n = (a.ws_pref[s + 1] - a.ws_pref[s]) / Y;
+  const int64_t g0 = a.ws_pref[s] + static_cast<int64_t>(y) * n;
+  const int64_t w0 = stream_wave_of(g0, T, W);
+  const int64_t w1 = stream_wave_of(g0 + n - 1, T, W);
+  if (w0 == w1) return;
+  const int64_t row0 = ((w0 + r) * HG + hi) * nhs + hh;
+  merge_parts<D>(a, a.ws_ml + 2 * row0, a.ws_o + row0 * D, static_cast<int64_t>(HG) * nhs,
+                 static_cast<int>(w1 - w0 + 1), sh * D);
 }
 
 }  // namespace
 
 int launch_reduce(const AttnArgs& a, hipStream_t stream) {
-  if (a.S == 0 || a.max_parts <= 1) return PKV_OK;
-  const dim3 grid(static_cast<unsigned>(a.S) * a.Hq);
-  const size_t lds = static_cast<size_t>(a.max_parts) * sizeof(float);
-  if (a.D == 64) {
-    reduce_kernel<64><<<grid, dim3(64), lds, stream>>>(a);
-  } else if (a.D == 128) {
-    reduce_kernel<128><<<grid, dim3(64), lds, stream>>>(a);
-  } else {
+  if (a.S == 0 || (!a.stream && a.max_parts <= 1)) return PKV_OK;
+  const int64_t waves = static_cast<int64_t>(a.S) * a.Hq;
+  const dim3 grid(static_cast<unsigned>((waves + kWaves - 1) / kWaves));
+  if (a.D != 64 && a.D != 128) {
     set_error("partition merge: head_size %d is not built", a.D);
     return PKV_ERR_UNSUPPORTED;
+  }
+  if (a.stream) {
+    if (a.D == 64) reduce_stream_kernel<64><<<grid, dim3(64 * kWaves), 0, stream>>>(a);
+    else reduce_stream_kernel<128><<<grid, dim3(64 * kWaves), 0, stream>>>(a);
+  } else {
+    if (a.D == 64) reduce_kernel<64><<<grid, dim3(64 * kWaves), 0, stream>>>(a);
+    else reduce_kernel<128><<<grid, dim3(64 * kWaves), 0, stream>>>(a);
   }
   return check_launch("partition merge");
 }

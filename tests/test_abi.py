@@ -50,14 +50,14 @@ def lib():
 
 def test_partition_choice(lib):
     F32, BF16 = 0, 1
-    # automatic: one partition for short contexts, 256 tokens otherwise ...
-    assert lib.paged_attention_partition_size(4, 8, 2, 128, 16, 100, 0, BF16) == 128
-    assert lib.paged_attention_partition_size(4, 8, 2, 128, 16, 32768, 0, BF16) == 256
-    assert lib.paged_attention_partition_size(4, 8, 2, 128, 16, 0, 0, BF16) == 32
-    # ... unless the batch alone has enough (sequence, kv-head group) work
-    # units to fill the GPU: 64 sequences x 10 groups of 4 kv heads
+    # automatic, bf16: whole sequences when the batch has enough (sequence,
+    # kv-head group) work units to fill the GPU -- 64 sequences x 10 groups
+    # of 4 kv heads --
     assert lib.paged_attention_partition_size(64, 40, 40, 128, 16, 2034, 0, BF16) == 2048
-    assert lib.paged_attention_partition_size(8, 40, 40, 128, 16, 2034, 0, BF16) == 256
+    assert lib.paged_attention_partition_size(2000, 8, 2, 64, 16, 100, 0, BF16) == 128
+    # ... else the stream schedule (0)
+    for S, L in ((4, 100), (4, 32768), (4, 0), (8, 2034), (511, 5000)):
+        assert lib.paged_attention_partition_size(S, 8, 2, 128, 16, L, 0, BF16) == 0
     assert lib.paged_attention_partition_size(4, 8, 2, 64, 16, 1000, 0, F32) == 64
     assert lib.paged_attention_partition_size(4, 8, 2, 64, 48, 1000, 0, F32) == 96
     # requests must be whole 32-token steps and whole blocks

@@ -191,6 +191,98 @@ def test_attention_head_groupings(hq, hkv):
     _check_rows(H.attend(st, partition_size=256).cpu().numpy(), ref, 2e-3, f"Hq={hq} Hkv={hkv}")
 
 
+def _oracle_rows(w, seqs):
+    out = {}
+    for s in seqs:
+        k, v = w.logical_kv(s)
+        out[s] = oracle.attention_ref(oracle.to_f64(w.query[s], w.dtype), oracle.to_f64(k, w.dtype),
+                                      oracle.to_f64(v, w.dtype), w.scale)
+    return out
+
+
+@pytest.mark.parametrize("lens,hq,hkv,D", [
+    ([100], 8, 1, 128),               # fewer stream steps than waves: one step per wave
+    ([5000], 4, 4, 64),               # one sequence cut into hundreds of pieces
+    ([3, 0, 40000, 17, 600], 32, 8, 128),  # a long context among short ones
+])
+def test_stream_schedule_cuts_and_merges(lens, hq, hkv, D):
+    """The stream schedule (automatic partitioning) gives each wave an equal
+    share of the batch's steps, so single contexts are cut into many pieces
+    and merged; the rows agree with the oracle and repeat bit for bit."""
+    w = workloads.custom(61 + len(lens), lens, dtype="bf16", num_q_heads=hq, num_kv_heads=hkv,
+                         head_size=D, block_size=16)
+    st = H.upload(w)
+    assert pkv.partition_size(w.num_seqs, hq, hkv, D, 16, w.max_context_len) == 0
+    got = H.attend(st, partition_size=0).cpu().numpy()
+    again = H.attend(st, partition_size=0).cpu().numpy()
+    assert np.array_equal(got.view(np.uint32), again.view(np.uint32))
+    for s, ref in _oracle_rows(w, [s for s in range(w.num_seqs) if lens[s] > 0]).items():
+        _check_rows(got[s], ref, 2e-3, f"stream seq {s} (L={lens[s]})")
+    for s in range(w.num_seqs):
+        if lens[s] == 0:
+            assert not got[s].any()
+
+
+def test_stream_schedule_full_batch_of_short_sequences():
+    """511 sequences (the largest batch the stream schedule takes for one
+    group of kv heads) of 1 to 80 tokens, GQA 14/2, head size 64."""
+    rng = np.random.default_rng(21)
+    lens = rng.integers(1, 81, 511)
+    w = workloads.custom(22, lens, dtype="bf16", num_q_heads=14, num_kv_heads=2, head_size=64,
+                         block_size=16)
+    st = H.upload(w)
+    assert pkv.partition_size(w.num_seqs, 14, 2, 64, 16, w.max_context_len) == 0
+    got = H.attend(st, partition_size=0).cpu().numpy()
+    ref_kv, _, _ = oracle_pool(w)
+    ref = oracle.paged_attention_ref(w.query, ref_kv, w.block_tables, w.context_lens, w.scale, w.dtype)
+    _check_rows(got, ref, 2e-3, "511 short sequences")
+
+
+def test_stream_schedule_bad_sequences_and_bf16_output():
+    w = workloads.custom(23, [40, 300, 700, 2], dtype="bf16", num_q_heads=8, num_kv_heads=2,
+                         head_size=128, block_size=16)
+    st = H.upload(w)
+    clean = H.attend(st, partition_size=0).cpu().numpy()
+    b16 = H.attend(st, partition_size=0, out_dtype=torch.bfloat16)
+    f32 = H.attend(st, partition_size=0)
+    assert torch.equal(f32.to(torch.bfloat16).view(torch.int16), b16.view(torch.int16))
+    st.tables[1, 3] = w.num_blocks + 5     # outside the pool: the kernel must not read it
+    bad = H.attend(st, partition_size=0).cpu().numpy()
+    assert np.isnan(bad[1]).all()
+    assert np.array_equal(bad[[0, 2, 3]].view(np.uint32), clean[[0, 2, 3]].view(np.uint32))
+    st.lens[2] = w.table_width * 16 + 1     # longer than its table
+    bad = H.attend(st, partition_size=0).cpu().numpy()
+    assert np.isnan(bad[2]).all() and np.array_equal(bad[0], clean[0])
+
+
+def test_stream_workspace_needs_no_clearing():
+    """The stream schedule writes every workspace byte it later reads: a
+    workspace full of garbage, or last used for another shape, gives the
+    same bits as a zeroed one."""
+    dev = torch.device("cuda:0")
+    a = workloads.custom(71, [3000, 17, 900], dtype="bf16", num_q_heads=16, num_kv_heads=4,
+                         head_size=128, block_size=16)
+    b = workloads.custom(72, [5000, 2, 64, 1200, 333], dtype="bf16", num_q_heads=14,
+                         num_kv_heads=2, head_size=64, block_size=32)
+    sa, sb = H.upload(a), H.upload(b)
+    need = max(pkv.workspace_bytes(w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_size,
+                                   w.block_size, w.max_context_len) for w in (a, b))
+    clean = torch.zeros(need, dtype=torch.uint8, device=dev)
+    junk = torch.randint(0, 256, (need,), dtype=torch.uint8, device=dev)
+
+    def run(st, ws):
+        w = st.w
+        return pkv.attention_decode(st.query, st.kv, st.tables, st.lens, w.scale, w.max_context_len,
+                                    workspace=ws).cpu().numpy()
+
+    ref_a, ref_b = run(sa, clean.clone()), run(sb, clean.clone())
+    for st, ref in ((sa, ref_a), (sb, ref_b), (sa, ref_a), (sa, ref_a), (sb, ref_b)):
+        got = run(st, junk)
+        assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
+    for s, r in _oracle_rows(b, [0, 3]).items():
+        _check_rows(ref_b[s], r, 2e-3, f"stream seq {s}")
+
+
 def test_many_partitions():
     w = workloads.custom(5, [16384, 9000], dtype="bf16", num_q_heads=8, num_kv_heads=1,
                          head_size=128, block_size=32)
