@@ -98,13 +98,21 @@ int bf16_parts_per_wg(int S, int Hq, int Hkv, int D, int max_parts, bool k_tile)
 }
 
 // The stream schedule serves bf16 caches with automatic partitioning when
-// the batch has too few (sequence, kv-head group) work units to fill the GPU
-// with whole sequences -- ragged batches, long contexts -- and every
-// sequence's length fits its scan.
+// whole sequences would leave the GPU partly idle -- too few (sequence,
+// kv-head group) work units to fill it, or a partial last round of them --
+// and every sequence's length fits its scan.
 bool uses_stream(int S, int Hq, int Hkv, int max_len, int req, pkv_dtype dtype) {
   if (dtype != PKV_BF16 || req != 0 || S > kMaxStreamSeqs) return false;
-  // whole sequences when the batch alone fills the GPU (no merge pass)
-  if (bf16_units(S, Hq, Hkv) >= kResidentGroups) return false;
+  // Whole sequences (no merge pass) when the batch fills the GPU in whole
+  // rounds of resident workgroups, or in enough rounds that dispatch order
+  // evens out the lengths, or when the merge would have many rows; the
+  // stream otherwise -- a partial last round of whole sequences leaves most
+  // of the GPU idle at the end.
+  const int64_t units = bf16_units(S, Hq, Hkv);
+  if (units >= kResidentGroups &&
+      (units % kResidentGroups == 0 || units >= 4 * kResidentGroups ||
+       static_cast<int64_t>(S) * Hq > 4096))
+    return false;
   // stream steps are counted in 32-bit integers
   const int G = Hq / Hkv;
   const int64_t steps = static_cast<int64_t>(S) * Hkv * ((G + 15) / 16) * (max_len / 32 + 1);

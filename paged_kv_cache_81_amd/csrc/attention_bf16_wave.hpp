@@ -110,7 +110,8 @@ struct Wave {
   const char* vbase;
   const int32_t* trow;
   int t_begin, t_end;
-  int win, win_q0;  // block-table window (see load_window)
+  int win, win_q0;  // block-table window of steps [win_q0, win_q0 + 32) (see load_window)
+  int win_next;     // ... and of the 32 steps after it
   bf16x8 qf[QC];
 
   // running softmax state of the current partition
@@ -169,20 +170,23 @@ struct Wave {
     win_q0 = 0;
     win = load_window(0);
     asm volatile("" ::"v"(win));
+    win_next = load_window(32);
   }
 
-  // Issue the loads of step q (tokens t_begin + 32q ..).  The same loads are
-  // issued on every path, so the compiler can wait for exactly one buffer's
-  // loads: a tile past the end of the run, or whose table entry is out of
-  // range, reads block 0 instead (always in the pool); its scores are masked
-  // and its values zeroed in compute(), or its partition poisoned.
+  // Issue the loads of step q (tokens t_begin + 32q ..), steps in order.
+  // The same K/V loads are issued on every path, so the compiler can wait
+  // for exactly one buffer's loads: a tile past the end of the run, or whose
+  // table entry is out of range, reads block 0 instead (always in the pool);
+  // its scores are masked and its values zeroed in compute(), or its
+  // partition poisoned.  Table windows are loaded one window ahead: when the
+  // steps reach the prefetched window it becomes current and the next one
+  // is requested (ahead of this step's K/V, so waiting for it later costs
+  // nothing extra).
   __device__ __forceinline__ void issue(Step& d, int q) {
     if (q - win_q0 >= 32) {
-      win_q0 = q;
-      win = load_window(q);
-      // wait for the entries here: a load still pending where the paths join
-      // would make every step wait for all outstanding K/V loads
-      asm volatile("" ::"v"(win));
+      win = win_next;
+      win_q0 += 32;
+      win_next = load_window(win_q0 + 32);
     }
     const int ts = t_begin + q * kStep;
     d.bad = false;
@@ -210,7 +214,9 @@ struct Wave {
 
   static __device__ __forceinline__ int kskew(int t) { return (t * NCH / 16) % NCH; }
 
-  // Fold step q (loaded into d) into the running partition.
+  // Fold step q (loaded into d) into the running partition.  MASK: the run
+  // may end inside this step.
+  template <bool MASK>
   __device__ __forceinline__ void compute(Step& d, int q) {
     const int ts = t_begin + q * kStep;
     bad_blk = bad_blk || d.bad;
@@ -258,7 +264,7 @@ struct Wave {
 #pragma unroll
       for (int r = 0; r < 4; ++r) x[u][r] = sc[r] * scale_log2;
     }
-    if (lim < kStep) {  // the run ends inside this step: mask scores, zero values
+    if (MASK && lim < kStep) {  // the run ends inside this step: mask scores, zero values
 #pragma unroll
       for (int u = 0; u < 2; ++u)
 #pragma unroll
@@ -317,7 +323,9 @@ struct Wave {
   }
 
   // Steps 0 .. nsteps-1 of the run, two register buffers deep: the next
-  // step's loads are in flight while the current step computes.
+  // step's loads are in flight while the current step computes (many waves
+  // per CU keep the memory system busy; a repeated last step to make every
+  // issue unconditional measured slower on short runs).
   // at_step(q) runs before step q is folded in (partition boundaries).
   template <typename F>
   __device__ __forceinline__ void run(int nsteps, F&& at_step) {
@@ -326,11 +334,11 @@ struct Wave {
     for (int q = 0; q < nsteps; q += 2) {
       if (q + 1 < nsteps) issue(bufB, q + 1);
       at_step(q);
-      compute(bufA, q);
+      compute<true>(bufA, q);
       if (q + 1 >= nsteps) break;
       if (q + 2 < nsteps) issue(bufA, q + 2);
       at_step(q + 1);
-      compute(bufB, q + 1);
+      compute<true>(bufB, q + 1);
     }
   }
 

@@ -153,6 +153,7 @@ inline void stream_lds_plan(int G, int D, bool k_tile, int* slots, int* wave_flo
 }
 
 int launch_attention_bf16(const AttnArgs& a, hipStream_t stream);
+int launch_attention_bf16_stream(const AttnArgs& a, hipStream_t stream);
 int launch_attention_f32(const AttnArgs& a, hipStream_t stream);
 int launch_reduce(const AttnArgs& a, hipStream_t stream);
 

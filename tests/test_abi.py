@@ -50,14 +50,19 @@ def lib():
 
 def test_partition_choice(lib):
     F32, BF16 = 0, 1
-    # automatic, bf16: whole sequences when the batch has enough (sequence,
-    # kv-head group) work units to fill the GPU -- 64 sequences x 10 groups
-    # of 4 kv heads --
-    assert lib.paged_attention_partition_size(64, 40, 40, 128, 16, 2034, 0, BF16) == 2048
+    # automatic, bf16: whole sequences when the batch fills the GPU with
+    # (sequence, kv-head group) work units in whole rounds of 512 -- 256
+    # sequences x 2 groups of 4 kv heads --, in 4 rounds or more, or when a
+    # merge would have more than 4096 rows ...
+    assert lib.paged_attention_partition_size(256, 32, 8, 128, 16, 1280, 0, BF16) == 1280
     assert lib.paged_attention_partition_size(2000, 8, 2, 64, 16, 100, 0, BF16) == 128
-    # ... else the stream schedule (0)
+    assert lib.paged_attention_partition_size(256, 40, 40, 128, 16, 2034, 0, BF16) == 2048
+    assert lib.paged_attention_partition_size(160, 40, 40, 128, 16, 2034, 0, BF16) == 2048
+    # ... else the stream schedule (0): too few units, or 64 sequences x 10
+    # groups = 1.25 rounds with a 2560-row merge
     for S, L in ((4, 100), (4, 32768), (4, 0), (8, 2034), (511, 5000)):
         assert lib.paged_attention_partition_size(S, 8, 2, 128, 16, L, 0, BF16) == 0
+    assert lib.paged_attention_partition_size(64, 40, 40, 128, 16, 2034, 0, BF16) == 0
     assert lib.paged_attention_partition_size(4, 8, 2, 64, 16, 1000, 0, F32) == 64
     assert lib.paged_attention_partition_size(4, 8, 2, 64, 48, 1000, 0, F32) == 96
     # requests must be whole 32-token steps and whole blocks
