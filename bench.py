@@ -40,7 +40,12 @@ DEFAULT_WORKLOAD = "opt13b_mha"
 # hold several times the 256 MB memory-side cache
 DEFAULT_LAYERS = {"opt13b_mha": 40, "qwen2_gqa": 24, "shared_prefix": 8, "long_context": 4,
                   "tiny": 1}
-KERNEL_SOURCES = ["paged_kv_cache_81_amd/csrc/attention_bf16.hip",
+# the sources that decide what the attention launch does (the counter
+# summary in profiles/ holds for this set only)
+KERNEL_SOURCES = ["paged_kv_cache_81_amd/csrc/api.hip",
+                  "paged_kv_cache_81_amd/csrc/attention_bf16.hip",
+                  "paged_kv_cache_81_amd/csrc/attention_bf16_stream.hip",
+                  "paged_kv_cache_81_amd/csrc/attention_bf16_wave.hpp",
                   "paged_kv_cache_81_amd/csrc/attention_f32.hip",
                   "paged_kv_cache_81_amd/csrc/common.hpp"]
 
@@ -82,6 +87,60 @@ def measured_traffic(workload: str):
     if not rec or rec.get("kernel_source_sha") != kernel_source_sha():
         return None
     return rec.get("hbm_bytes_per_launch")
+
+
+def _counter_means(path: str, kernel_part: str, min_value: float = 0.0):
+    """Mean Counter_Value (KiB per dispatch) of the dispatches whose kernel
+    name contains kernel_part (and whose value is at least min_value)."""
+    import csv
+    vals, name = [], None
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            if kernel_part in r["Kernel_Name"] and float(r["Counter_Value"]) >= min_value:
+                vals.append(float(r["Counter_Value"]))
+                name = r["Kernel_Name"]
+    if not vals:
+        raise SystemExit(f"no dispatch of {kernel_part!r} in {path}")
+    return sum(vals) / len(vals), len(vals), name
+
+
+def summarize_counters(d: str, workload: str) -> int:
+    """HBM bytes per attention launch from rocprofv3 counter passes, scaled
+    by what the same counters read for a 1 GiB copy."""
+    import workloads
+
+    csv_of = lambda c: os.path.join(d, c, "run_counter_collection.csv")
+    fetch, n, kname = _counter_means(csv_of("FETCH_SIZE"), "attention_bf16")
+    write, _, _ = _counter_means(csv_of("WRITE_SIZE"), "attention_bf16")
+    # the 1 GiB copies (smaller copies of the same kernel in the run are ignored)
+    cfetch, _, _ = _counter_means(csv_of("cal_FETCH_SIZE"), "copyBuffer", 1e5)
+    cwrite, _, _ = _counter_means(csv_of("cal_WRITE_SIZE"), "copyBuffer", 1e5)
+    fscale, wscale = (1 << 30) / (cfetch * 1024), (1 << 30) / (cwrite * 1024)
+    w = workloads.make(workload)
+    rec = {
+        "kernel": kname,
+        "kernel_source_sha": kernel_source_sha(),
+        "fetch_size_kib_per_launch": round(fetch, 2),
+        "write_size_kib_per_launch": round(write, 2),
+        "copy_fetch_size_kib": round(cfetch, 3),
+        "copy_write_size_kib": round(cwrite, 3),
+        "fetch_scale": round(fscale, 6),
+        "write_scale": round(wscale, 6),
+        "hbm_read_bytes_per_launch": round(fetch * 1024 * fscale),
+        "hbm_write_bytes_per_launch": round(write * 1024 * wscale),
+        "hbm_bytes_per_launch": round(fetch * 1024 * fscale + write * 1024 * wscale),
+        "algorithmic_kv_bytes_per_launch": unique_kv_bytes(w),
+        "logical_kv_bytes_per_launch": kv_bytes(w),
+        "launches_counted": n,
+    }
+    path = os.path.join(ROOT, "profiles", "attention_traffic.json")
+    table = json.load(open(path)) if os.path.exists(path) else {}
+    table[workload] = rec
+    with open(path, "w") as f:
+        json.dump(table, f, indent=1)
+        f.write("\n")
+    print(json.dumps(rec, indent=1))
+    return 0
 
 
 def cpu_baseline(w, seconds: float) -> dict:
@@ -138,13 +197,20 @@ def main() -> int:
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (known bytes), for "
                          "scaling hardware byte counters")
+    ap.add_argument("--summarize-counters", metavar="DIR",
+                    help="no GPU: turn rocprofv3 FETCH_SIZE / WRITE_SIZE passes of this workload "
+                         "and of --copy-calibration (DIR/{FETCH_SIZE,WRITE_SIZE,cal_FETCH_SIZE,"
+                         "cal_WRITE_SIZE}) into HBM bytes per attention launch in "
+                         "profiles/attention_traffic.json")
     args = ap.parse_args()
+
+    if args.summarize_counters:
+        return summarize_counters(args.summarize_counters, args.workload)
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}): "
-              "this build runs the decode path on a single MI355X; see the design notes for how "
-              "it would shard.", file=sys.stderr)
+              "the decode path runs on a single MI355X.", file=sys.stderr)
         return 2
 
     import numpy as np
@@ -301,7 +367,8 @@ def main() -> int:
     # by several sequences can hit in the caches, and a logical rate above the
     # HBM peak would not be a fraction of it
     attn_gbps = ukvb / (kernel_us["attention"] * 1e-6) / 1e9
-    kname = f"attention_bf16_kernel<{D},{B}>" if dt else f"attention_f32_kernel<{D}>"
+    kname = (f"attention_f32_kernel<{D}>" if not dt else
+             f"attention_bf16_stream_kernel<{D},{B}>" if P == 0 else f"attention_bf16_kernel<{D},{B}>")
     traffic = measured_traffic(w.name)
 
     result = {

@@ -405,6 +405,9 @@ int decode_impl(int phases, void* out, pkv_dtype out_dtype, const void* query,
   // the caches.  Each workgroup ranks the lengths itself, so only for small
   // batches.
   a.longest_first = !(flags & PKV_ATTN_CACHED_KV) && num_seqs <= kMaxRankedSeqs;
+  // Shared blocks are read once per L2 when the sequences sharing them run
+  // on one XCD.
+  a.xcd_blocked = (flags & PKV_ATTN_CACHED_KV) ? 1 : 0;
   // Keys take the LDS path when a token's row across all kv heads is long
   // (>= 4 KB): one head's 64-byte pieces of such rows stream poorly, while
   // for short rows the direct MFMA-layout load is faster.

@@ -20,6 +20,7 @@ namespace {
 
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
+constexpr int kXcds = 8;  // accelerator complexes (each with its own L2) of an MI355X
 using wave::kStep;
 
 // ---------------------------------------------------------------- fixed partitions
@@ -87,6 +88,22 @@ attention_bf16_kernel(AttnArgs a) {
   // (ties by index).  Long sequences then start first and short ones fill
   // the tail.
   int s_dense = blockIdx.z;
+  int y_dense = blockIdx.y;
+  int x_dense = blockIdx.x;
+  if (!CMP && a.xcd_blocked) {
+    // Workgroup b (in dispatch order) runs on XCD b mod 8: renumber so that
+    // XCD i takes the i-th contiguous eighth of the (sequence, pair, run)
+    // items, and sequences adjacent in the batch -- forks that share a
+    // prompt's blocks -- read them through one L2.
+    const int64_t n = static_cast<int64_t>(gridDim.x) * gridDim.y * gridDim.z;
+    const int64_t b = blockIdx.x + static_cast<int64_t>(gridDim.x) * (blockIdx.y + static_cast<int64_t>(gridDim.y) * blockIdx.z);
+    const int64_t q = n / kXcds, r = n % kXcds;
+    const int64_t xcd = b % kXcds;
+    const int64_t item = xcd * q + min(xcd, r) + b / kXcds;
+    x_dense = static_cast<int>(item % gridDim.x);
+    y_dense = static_cast<int>((item / gridDim.x) % gridDim.y);
+    s_dense = static_cast<int>(item / (static_cast<int64_t>(gridDim.x) * gridDim.y));
+  }
   if (!CMP && a.longest_first) {
     __shared__ int s_pick;
     for (int i = threadIdx.x; i < a.S; i += kThreads) s_seq[i] = a.lens[i];
@@ -98,7 +115,7 @@ attention_bf16_kernel(AttnArgs a) {
         const int lt = s_seq[t];
         rank += (lt > lc || (lt == lc && t < c)) ? 1 : 0;
       }
-      if (rank == static_cast<int>(blockIdx.z)) s_pick = c;
+      if (rank == s_dense) s_pick = c;
     }
     __syncthreads();
     s_dense = s_pick;
@@ -171,7 +188,7 @@ attention_bf16_kernel(AttnArgs a) {
   };
 
   if constexpr (!CMP) {
-    item(s_dense, blockIdx.y, blockIdx.x);
+    item(s_dense, y_dense, x_dense);
     return;
   }
   for (int it = blockIdx.x; it < total; it += gridDim.x) {

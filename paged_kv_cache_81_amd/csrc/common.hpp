@@ -78,6 +78,7 @@ struct AttnArgs {
   int longest_first;  // map workgroups to sequences in decreasing length
   int k_via_lds;      // load keys row-wise and rearrange them through LDS
   int compact;        // bf16: workgroups walk a compact list of work items
+  int xcd_blocked;    // bf16 dense grid: each XCD takes a contiguous eighth of the items
   // stream schedule (bf16, automatic partitioning)
   int stream;              // use it
   int stream_waves;        // waves of the persistent grid (a multiple of 4)
