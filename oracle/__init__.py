@@ -34,3 +34,10 @@ from .paged_attention import (  # noqa: F401
     to_f64,
     write_ref,
 )
+from .block_manager import (  # noqa: F401,E402
+    NONE_HASH,
+    OutOfBlocks,
+    RefBlockManager,
+    block_hash,
+    copy_blocks_ref,
+)

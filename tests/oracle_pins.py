@@ -348,6 +348,226 @@ def pin_split_merge(o) -> None:
         assert np.abs(l0 - np.exp(z - z.max(axis=1, keepdims=True)).sum(axis=1)).max() < 1e-12
 
 
+# ------------------------------------------------------------------ block manager
+
+def _free_order(n, head):
+    return list(head) + [b for b in range(n) if b not in head]
+
+
+def _cached_blocks(m):
+    return sorted(m.cache.values())
+
+
+def pin_cow_parallel_samples(o) -> None:
+    """Two samples of one prompt share its blocks; the first writer of a
+    shared block copies it, the last one writes in place ([review] worked
+    example, tests/golden/cow_parallel_samples.json)."""
+    g = golden("cow_parallel_samples.json")
+    m = o.RefBlockManager(g["num_blocks"], g["block_size"],
+                          free_order=_free_order(g["num_blocks"], g["free_order_head"]))
+    m.allocate(1, g["prompt"])
+    m.fork(1, 2)
+    e = g["after_prefill_and_fork"]
+    assert m.table(1) == e["table"] and m.table(2) == e["table"]
+    assert all(m.ref[int(b)] == r for b, r in e["ref"].items())
+    for sid, key in ((1, "A1_writes"), (2, "A2_writes")):
+        e = g[key]
+        slots, copies = m.append(sid, [e["token"]])
+        assert slots == [e["slot"]], (key, slots)
+        assert [list(c) for c in copies] == e["copies"], (key, copies)
+        assert m.table(sid) == e["table"]
+        assert all(m.ref[int(b)] == r for b, r in e["ref"].items())
+
+
+def pin_prefix_cache_timeline(o) -> None:
+    """Times 1-6 of [walkthrough]'s prefix-cache timeline: hits, the free
+    queue order after reverse-order frees, eviction of reused cached blocks
+    (tests/golden/prefix_cache_timeline.json)."""
+    g = golden("prefix_cache_timeline.json")
+    m = o.RefBlockManager(g["num_blocks"], g["block_size"])
+    for st in g["steps"]:
+        if st["op"] == "allocate":
+            assert m.allocate(st["seq"], st["tokens"]) == st["cached_tokens"], st["time"]
+        elif st["op"] == "append":
+            m.append(st["seq"], st["tokens"])
+        else:
+            m.free_seq(st["seq"])
+        if "table" in st:
+            assert m.table(st["seq"]) == st["table"], (st["time"], m.table(st["seq"]))
+        if "free_queue" in st:
+            assert m.free == st["free_queue"], (st["time"], m.free)
+        if "cached_blocks" in st:
+            assert _cached_blocks(m) == st["cached_blocks"], (st["time"], _cached_blocks(m))
+        if "still_cached" in st:
+            assert set(st["still_cached"]) <= set(_cached_blocks(m)), st["time"]
+    # time 6 reused block 3, so its old content is no longer a hit
+    assert 3 not in [m.cache.get(h) for h in m.cache if m.cache[h] == 3 and m.hash_of[3] is not None] or \
+        m.hash_of[3] is None
+
+
+def pin_prefix_hit_table_50(o) -> None:
+    """[walkthrough] 'ブロック割当のロジック': 50 tokens at B = 16 get table
+    [10, 21, 45, 67] with the first two blocks from the prefix cache; token 64
+    takes block 89 (tests/golden/prefix_hit_table_50.json)."""
+    g = golden("prefix_hit_table_50.json")
+    m = o.RefBlockManager(g["num_blocks"], g["block_size"],
+                          free_order=_free_order(g["num_blocks"], g["free_order_head"]))
+    m.allocate(7, g["earlier_request"])
+    m.free_seq(7)
+    assert m.allocate(8, g["request"]) == g["cached_tokens"]
+    assert m.table(8) == g["table"]
+    slots, copies = m.append(8, g["decode_tokens"])
+    assert m.table(8) == g["table_after_decode"] and not copies
+    first = g["first_token_in_89"]
+    assert slots[first - len(g["request"])] == 89 * g["block_size"]
+    # the same 32 tokens again: hits are looked up over num_tokens - 1 tokens
+    # (find_longest_cache_hit's max_length), so the last block is computed
+    assert m.allocate(9, g["earlier_request"]) == g["block_size"]
+
+
+def pin_block_hash_chain(o) -> None:
+    """A block's hash depends on every earlier token and on nothing else:
+    equal prefixes hash equally, any earlier change changes every later hash."""
+    rng = np.random.default_rng(5)
+    toks = rng.integers(0, 1000, 64).tolist()
+
+    def chain(t):
+        out, h = [], o.NONE_HASH
+        for i in range(len(t) // 16):
+            h = o.block_hash(h, t[16 * i:16 * (i + 1)])
+            out.append(h)
+        return out
+
+    base = chain(toks)
+    assert len(set(base)) == 4 and all(len(h) == 32 for h in base)
+    assert chain(list(toks)) == base
+    for pos in (0, 17, 63):
+        t2 = list(toks)
+        t2[pos] += 1
+        c2 = chain(t2)
+        b = pos // 16
+        assert c2[:b] == base[:b] and all(x != y for x, y in zip(c2[b:], base[b:]))
+    # the same 16 tokens under another parent hash differently
+    assert o.block_hash(o.NONE_HASH, toks[16:32]) != base[1]
+
+
+def _simulate(o, seed, N=24, B=4, ncpu=24, steps=300):
+    """Random allocate / append / fork / free / swap sequences on a small pool,
+    with the pool's contents modelled as token ids per slot (copy-on-write and
+    swap copies applied as the manager asks).  After every operation: reading
+    each sequence through its table gives its own tokens; reference counts
+    equal the table entries pointing at each block; the free queue is exactly
+    the unreferenced blocks; a refused operation changed nothing."""
+    rng = np.random.default_rng(seed)
+    m = o.RefBlockManager(N, B, num_cpu_blocks=ncpu)
+    gpu = np.full(N * B, -1, dtype=np.int64)
+    cpu = np.full(ncpu * B, -1, dtype=np.int64)
+    toks = {}
+    nxt = 0
+    vocab = [list(rng.integers(0, 50, 40)) for _ in range(3)]  # shared prompt stems
+
+    def check():
+        for sid, t in toks.items():
+            s = m.seqs[sid]
+            pool = cpu if s.swapped else gpu
+            got = [int(pool[s.table[p // B] * B + p % B]) for p in range(len(t))]
+            assert got == t, (sid, got, t)
+            assert len(s.table) == -(-len(t) // B)
+        refs = [0] * N
+        for s in m.seqs.values():
+            if not s.swapped:
+                for b in s.table:
+                    refs[b] += 1
+        assert refs == m.ref, (refs, m.ref)
+        assert sorted(m.free) == [b for b in range(N) if refs[b] == 0]
+        for h, b in m.cache.items():
+            assert m.hash_of[b] == h
+
+    def state():
+        return (list(m.ref), list(m.hash_of), dict(m.cache), list(m.free), list(m.cpu_free),
+                list(m.cpu_ref), {i: (list(s.table), list(s.tokens), list(s.hashes), s.swapped)
+                                  for i, s in m.seqs.items()})
+
+    for _ in range(steps):
+        snap = state()
+        op = rng.integers(0, 6)
+        live = [i for i in toks if not m.seqs[i].swapped]
+        try:
+            if op == 0 or not toks:
+                stem = vocab[rng.integers(0, 3)]
+                n = int(rng.integers(1, 20))
+                t = [int(x) for x in stem[:rng.integers(0, n + 1)]]
+                t += [int(x) for x in rng.integers(100, 200, n - len(t))]
+                sid = nxt
+                nxt += 1
+                cached = m.allocate(sid, t)
+                # whole cached blocks, and the last token is always computed
+                assert cached % B == 0 and (cached < len(t) or not t)
+                for p in range(cached, len(t)):
+                    gpu[m.table(sid)[p // B] * B + p % B] = t[p]
+                toks[sid] = t
+            elif op == 1 and live:
+                sid = live[rng.integers(0, len(live))]
+                new = [int(x) for x in rng.integers(100, 200, rng.integers(1, 6))]
+                slots, copies = m.append(sid, new)
+                for s_, d_ in copies:
+                    gpu[d_ * B:(d_ + 1) * B] = gpu[s_ * B:(s_ + 1) * B]
+                for sl, tk in zip(slots, new):
+                    assert m.ref[sl // B] == 1  # nobody else sees the written block
+                    gpu[sl] = tk
+                toks[sid] = toks[sid] + new
+            elif op == 2 and live:
+                sid = live[rng.integers(0, len(live))]
+                m.fork(sid, nxt)
+                toks[nxt] = list(toks[sid])
+                nxt += 1
+            elif op == 3:
+                sid = list(toks)[rng.integers(0, len(toks))]
+                m.free_seq(sid)
+                del toks[sid]
+            elif op == 4 and live:
+                # a sequence and everything sharing blocks with it
+                sid = live[rng.integers(0, len(live))]
+                group = {sid}
+                grew = True
+                while grew:
+                    blocks = {b for i in group for b in m.seqs[i].table}
+                    more = {i for i in live if set(m.seqs[i].table) & blocks}
+                    grew = not more <= group
+                    group |= more
+                for g_, c_ in m.swap_out(sorted(group)):
+                    cpu[c_ * B:(c_ + 1) * B] = gpu[g_ * B:(g_ + 1) * B]
+            elif op == 5:
+                swapped = [i for i in toks if m.seqs[i].swapped]
+                if swapped:
+                    sid = swapped[0]
+                    cblocks = set(m.seqs[sid].table)
+                    group = sorted(i for i in swapped if set(m.seqs[i].table) & cblocks)
+                    for c_, g_ in m.swap_in(group):
+                        gpu[g_ * B:(g_ + 1) * B] = cpu[c_ * B:(c_ + 1) * B]
+        except o.OutOfBlocks:
+            assert state() == snap, "a refused operation changed the state"
+        check()
+
+
+def pin_block_manager_invariants(o) -> None:
+    for seed in range(4):
+        _simulate(o, seed)
+
+
+def pin_copy_blocks(o) -> None:
+    """Block copies move whole blocks (keys and values) and nothing else."""
+    rng = np.random.default_rng(9)
+    kv = rng.standard_normal((2, 6, 4, 2, 3))
+    before = kv.copy()
+    o.copy_blocks_ref(kv, [(1, 4), (5, 0)])
+    assert np.array_equal(kv[:, 4], before[:, 1]) and np.array_equal(kv[:, 0], before[:, 5])
+    assert np.array_equal(kv[:, [1, 2, 3, 5]], before[:, [1, 2, 3, 5]])
+    host = np.zeros((2, 3, 4, 2, 3))
+    o.copy_blocks_ref(before, [(2, 1)], dst=host)
+    assert np.array_equal(host[:, 1], before[:, 2]) and not host[:, [0, 2]].any()
+
+
 ALL_PINS = [
     pin_block_counts,
     pin_waste_bound,
@@ -361,4 +581,10 @@ ALL_PINS = [
     pin_attention_closed_forms,
     pin_paged_invariants,
     pin_split_merge,
+    pin_cow_parallel_samples,
+    pin_prefix_cache_timeline,
+    pin_prefix_hit_table_50,
+    pin_block_hash_chain,
+    pin_block_manager_invariants,
+    pin_copy_blocks,
 ]

@@ -103,7 +103,124 @@ def _last_fill_wrong(n, B):
     return n % B
 
 
+from oracle import block_manager as bm
+
+
+class _FreeForward(bm.RefBlockManager):
+    """Returns a finished request's blocks first block first."""
+    def free_seq(self, sid):
+        s = self._seq(sid)
+        for b in s.table:
+            self._release(b)
+        del self.seqs[sid]
+
+
+class _NoEviction(bm.RefBlockManager):
+    """Keeps a reused block's old cache entry."""
+    def _take(self):
+        b = self.free.pop(0)
+        self.hash_of[b] = None
+        self.ref[b] = 1
+        return b
+
+
+class _CowKeepsRef(bm.RefBlockManager):
+    """Copy-on-write without dropping the old block's count."""
+    def append(self, sid, tokens):
+        s = self._seq(sid)
+        shared = [b for b in s.table if self.ref[b] > 1]
+        slots, copies = super().append(sid, tokens)
+        for src_, _ in copies:
+            if src_ in shared:
+                self.ref[src_] += 1
+        return slots, copies
+
+
+class _ForkNoRef(bm.RefBlockManager):
+    """Fork shares the blocks without counting the new references."""
+    def fork(self, parent, child):
+        super().fork(parent, child)
+        for b in self.seqs[child].table:
+            self.ref[b] -= 1
+
+
+class _HitsUpToFullLength(bm.RefBlockManager):
+    """Prefix hits may cover every token, the last one included."""
+    def allocate(self, sid, tokens):
+        n = len(tokens)
+        if n and n % self.B == 0 and self.prefix_caching:
+            parent, hits = bm.NONE_HASH, 0
+            for i in range(n // self.B):
+                parent = bm.block_hash(parent, tokens[i * self.B:(i + 1) * self.B])
+                if parent not in self.cache:
+                    break
+                hits += 1
+            if hits == n // self.B:
+                cached = super().allocate(sid, tokens)
+                return n
+        return super().allocate(sid, tokens)
+
+
+class _HitsPastMiss(bm.RefBlockManager):
+    """Keeps looking for hits after the first miss."""
+    def allocate(self, sid, tokens):
+        if sid in self.seqs:
+            raise KeyError(sid)
+        n = len(tokens)
+        need = -(-n // self.B)
+        hits, parent = [], bm.NONE_HASH
+        for i in range((n - 1) // self.B if n > 0 else 0):
+            h = bm.block_hash(parent, tokens[i * self.B:(i + 1) * self.B])
+            if h in self.cache:
+                hits.append(self.cache[h])
+            parent = h
+        in_queue = sum(1 for b in hits if self.ref[b] == 0)
+        if len(self.free) - in_queue < need - len(hits):
+            raise bm.OutOfBlocks()
+        s = bm._Seq()
+        for b in hits:
+            self._touch(b)
+        s.table = hits + [self._take() for _ in range(need - len(hits))]
+        s.tokens = list(tokens)
+        self.seqs[sid] = s
+        self._cache_full(s)
+        return len(hits) * self.B
+
+
+class _CachePartial(bm.RefBlockManager):
+    """Also registers the partly filled last block."""
+    def _cache_full(self, s):
+        super()._cache_full(s)
+        if self.prefix_caching and len(s.tokens) % self.B and s.table:
+            parent = s.hashes[-1] if s.hashes else bm.NONE_HASH
+            h = bm.block_hash(parent, s.tokens[len(s.hashes) * self.B:])
+            b = s.table[len(s.hashes)]
+            self.cache.setdefault(h, b)
+            if self.hash_of[b] is None:
+                self.hash_of[b] = h
+
+
+def _hash_no_parent(parent, tokens):
+    return bm.block_hash(bm.NONE_HASH, tokens)
+
+
+def _copy_blocks_keys_only(kv, pairs, dst=None):
+    out = kv if dst is None else dst
+    for s, d in pairs:
+        out[0, d] = kv[0, s]
+    return out
+
+
 MUTANTS = {
+    "bm_free_forward": dict(RefBlockManager=_FreeForward),
+    "bm_no_eviction": dict(RefBlockManager=_NoEviction),
+    "bm_cow_keeps_ref": dict(RefBlockManager=_CowKeepsRef),
+    "bm_fork_no_ref": dict(RefBlockManager=_ForkNoRef),
+    "bm_hits_full_length": dict(RefBlockManager=_HitsUpToFullLength),
+    "bm_hits_past_miss": dict(RefBlockManager=_HitsPastMiss),
+    "bm_cache_partial": dict(RefBlockManager=_CachePartial),
+    "hash_no_parent": dict(block_hash=_hash_no_parent),
+    "copy_keys_only": dict(copy_blocks_ref=_copy_blocks_keys_only),
     "blocks_floor": dict(blocks_needed=_floor_blocks),
     "slot_swapped_axes": dict(slot_of=_slot_swapped),
     "slot_off_by_one": dict(slot_of=_slot_off_by_one),
