@@ -252,10 +252,14 @@ class RefBlockManager:
         if not all(s.swapped for s in group):
             raise KeyError("not swapped")
         blocks: List[int] = []
+        uses: Dict[int, int] = {}
         for s in group:
             for b in s.table:
-                if b not in blocks:
+                if b not in uses:
                     blocks.append(b)
+                uses[b] = uses.get(b, 0) + 1
+        if any(self.cpu_ref[b] != uses[b] for b in blocks):
+            raise KeyError("blocks shared outside the group")
         if len(blocks) > len(self.free):
             raise OutOfBlocks()
         to_gpu = {b: self._take() for b in blocks}

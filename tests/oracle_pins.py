@@ -540,9 +540,13 @@ def _simulate(o, seed, N=24, B=4, ncpu=24, steps=300):
             elif op == 5:
                 swapped = [i for i in toks if m.seqs[i].swapped]
                 if swapped:
-                    sid = swapped[0]
-                    cblocks = set(m.seqs[sid].table)
-                    group = sorted(i for i in swapped if set(m.seqs[i].table) & cblocks)
+                    group, grew = {swapped[0]}, True
+                    while grew:
+                        blocks = {b for i in group for b in m.seqs[i].table}
+                        more = {i for i in swapped if set(m.seqs[i].table) & blocks}
+                        grew = not more <= group
+                        group |= more
+                    group = sorted(group)
                     for c_, g_ in m.swap_in(group):
                         gpu[g_ * B:(g_ + 1) * B] = cpu[c_ * B:(c_ + 1) * B]
         except o.OutOfBlocks:
