@@ -17,12 +17,14 @@
  * physical_block * block_size + offset.
  *
  * Conventions for every entry point:
- *  - Pointers are DEVICE pointers unless stated otherwise; arrays are
- *    row-major and contiguous in the shapes given.
+ *  - Pointers are DEVICE pointers unless stated otherwise (the block manager
+ *    functions, pkv_bm_*, take host pointers); arrays are row-major and
+ *    contiguous in the shapes given.
  *  - The caller allocates and owns every buffer (cache, tables, slots, query,
- *    output, workspace).  The library allocates nothing, keeps no pointer
- *    after returning, and has no global mutable state except a thread-local
- *    error message.
+ *    output, workspace).  The library allocates no device memory, keeps no
+ *    pointer after returning, and has no global mutable state except a
+ *    thread-local error message; the only host memory it holds is inside
+ *    block managers the caller creates and destroys.
  *  - All work is enqueued asynchronously on `stream` (0 = the null stream);
  *    the library never synchronises.  Argument errors are found on the host
  *    before anything is enqueued; the return value is a pkv_status and, when
@@ -62,7 +64,9 @@ typedef enum {
   PKV_ERR_INVALID = -1,     /* bad argument (null pointer, size, alignment)   */
   PKV_ERR_UNSUPPORTED = -2, /* valid but not built (head size, block size...) */
   PKV_ERR_WORKSPACE = -3,   /* workspace missing or too small                 */
-  PKV_ERR_HIP = -4          /* the HIP runtime refused a launch               */
+  PKV_ERR_HIP = -4,         /* the HIP runtime refused a launch               */
+  PKV_ERR_NO_BLOCKS = -5    /* block manager: not enough free blocks; nothing
+                               was changed                                    */
 } pkv_status;
 
 /* Message describing the last failed call on this thread ("" if none).  The
@@ -227,6 +231,126 @@ int paged_attention_merge(void* out, pkv_dtype out_dtype, const void* query,
                           float scale, int max_context_len, int partition_size, void* workspace,
                           size_t workspace_bytes, pkv_dtype dtype, unsigned flags,
                           hipStream_t stream);
+
+/*
+ * paged_kv_copy_blocks -- copy whole blocks (keys and values) between two
+ * pools of the same geometry: dst_cache[:, dst_blocks[i]] =
+ * src_cache[:, src_blocks[i]] for every i.
+ *
+ * Serves copy-on-write (dst_cache == src_cache: a forked sample about to
+ * write into a shared block first copies it to its own; studying-code.tistory.com
+ * vLLM review, "생성 단계에서의 Copy-on-Write", and "메모리 복사 오버헤드의
+ * 최적화": only that one block is copied) and swapping (one pool in device
+ * memory, the other in pinned host memory from hipHostMalloc, which the
+ * kernel reads or writes over PCIe).  Bit-exact copy.  Each pointer is
+ * checked with hipPointerGetAttributes: pinned host memory is used through
+ * its mapped device address, and pageable host memory gives PKV_ERR_INVALID
+ * before anything is launched.
+ *
+ *   dst_cache    dtype [2][dst_num_blocks][block_size][num_kv_heads][head_size]
+ *   src_cache    dtype [2][src_num_blocks][block_size][num_kv_heads][head_size]
+ *   src_blocks, dst_blocks  int32 [num_copies], device or pinned host memory;
+ *                a pair with an id out of its pool's range is skipped
+ * The copies are independent: no destination may also be a source, and no
+ * block may be a destination twice (the block manager's copy lists obey this).
+ * Supported: head_size * element bytes a multiple of 16; pools 16-byte aligned.
+ */
+int paged_kv_copy_blocks(void* dst_cache, int dst_num_blocks, const void* src_cache,
+                         int src_num_blocks, const int32_t* src_blocks, const int32_t* dst_blocks,
+                         int num_copies, int block_size, int num_kv_heads, int head_size,
+                         pkv_dtype dtype, hipStream_t stream);
+
+/*
+ * Block manager (host).  Hands out the block tables and slots the kernels
+ * above consume, for one pool of num_blocks physical blocks of block_size
+ * tokens (every layer's cache uses the same table):
+ *
+ *  - each physical block has a reference count, one per logical block that
+ *    maps to it (studying-code.tistory.com vLLM review, "요청 완료 후 메모리
+ *    관리": two samples share blocks 7 and 1, counts 2);
+ *  - free blocks wait in a queue: allocation takes its head, a freed sequence
+ *    returns the blocks whose count reaches zero to its tail, last block first
+ *    (itan.pw walk-through, "プレイフィックスキャッシュの詳細", times 4-6);
+ *  - a prompt of n tokens takes ceil(n / block_size) blocks; decoding fills
+ *    the last block and takes a new one when it is full (the walk-through,
+ *    overall allocation flow and "ブロック割当のロジック");
+ *  - fork shares every block of the parent (counts + 1); writing a token
+ *    into a block whose count is above 1 first moves the writer to a fresh
+ *    block and reports the copy the caller must make with
+ *    paged_kv_copy_blocks before the write (the review, "생성 단계에서의
+ *    Copy-on-Write"; tech.blogsailing.com explainer, section 3);
+ *  - with prefix caching, every full block is registered under the chain hash
+ *    SHA-256(previous block's hash, or 32 zero bytes, || its token ids as
+ *    little-endian int32); a new request reuses the cached blocks of its
+ *    leading full blocks, at most (n - 1) / block_size of them, up to the
+ *    first miss; a cached block taken from the free queue for other data
+ *    loses its entry (the walk-through, "プレイフィックスキャッシュの詳細");
+ *  - a group of sequences (every sequence sharing a block with another must
+ *    be in it) is swapped out to, and back in from, a pool of num_cpu_blocks
+ *    host blocks, all or nothing; the caller makes the reported copies.
+ *
+ * A request the pool cannot satisfy returns PKV_ERR_NO_BLOCKS and changes
+ * nothing.  Sequences are named by caller-chosen int64 ids.  A manager is not
+ * thread-safe.  All pointers here are host pointers.
+ */
+typedef struct pkv_block_manager pkv_block_manager;
+
+/* NULL on bad sizes.  prefix_caching: 0 or 1. */
+pkv_block_manager* pkv_bm_create(int num_blocks, int block_size, int prefix_caching,
+                                 int num_cpu_blocks);
+void pkv_bm_destroy(pkv_block_manager* bm);
+
+/* Replace the initial free-queue order (a permutation of all blocks) of a
+ * manager that has no sequence yet. */
+int pkv_bm_set_free_order(pkv_block_manager* bm, const int32_t* order, int n);
+
+/* Admit sequence `seq` with its prompt tokens[num_tokens]; *num_cached_tokens
+ * receives how many leading tokens came from the prefix cache (their K/V are
+ * already in the pool; the caller writes positions from there on). */
+int pkv_bm_allocate(pkv_block_manager* bm, int64_t seq, const int32_t* tokens, int num_tokens,
+                    int* num_cached_tokens);
+
+/* Append n generated tokens to `seq`.  slots[n] receives each token's slot
+ * (for paged_kv_slot_mapping's consumers: paged_kv_write); copy_src[n] and
+ * copy_dst[n] receive *num_copies copy-on-write block copies to make first. */
+int pkv_bm_append(pkv_block_manager* bm, int64_t seq, const int32_t* tokens, int n,
+                  int64_t* slots, int32_t* copy_src, int32_t* copy_dst, int* num_copies);
+
+/* `child` shares every block of `parent`. */
+int pkv_bm_fork(pkv_block_manager* bm, int64_t parent, int64_t child);
+
+/* Release a sequence (swapped out or not). */
+int pkv_bm_free(pkv_block_manager* bm, int64_t seq);
+
+/* Swap the group seqs[num_seqs] out to host blocks (gpu_blocks[i] ->
+ * cpu_blocks[i], *num_copies pairs, at most `capacity`), or back in
+ * (cpu_blocks[i] -> gpu_blocks[i]). */
+int pkv_bm_swap_out(pkv_block_manager* bm, const int64_t* seqs, int num_seqs, int32_t* gpu_blocks,
+                    int32_t* cpu_blocks, int capacity, int* num_copies);
+int pkv_bm_swap_in(pkv_block_manager* bm, const int64_t* seqs, int num_seqs, int32_t* cpu_blocks,
+                   int32_t* gpu_blocks, int capacity, int* num_copies);
+
+/* Views.  Counts are returned (>= 0) or a negative status. */
+int pkv_bm_num_tokens(pkv_block_manager* bm, int64_t seq);
+int pkv_bm_is_swapped(pkv_block_manager* bm, int64_t seq);
+/* the sequence's block ids (CPU block ids while swapped out); returns the
+ * count and fills at most `capacity` entries */
+int pkv_bm_block_table(pkv_block_manager* bm, int64_t seq, int32_t* out, int capacity);
+/* slots of positions [begin, end) of a resident sequence */
+int pkv_bm_slots(pkv_block_manager* bm, int64_t seq, int begin, int end, int64_t* out);
+/* block tables [num_seqs][table_width] (INT32_MIN past each sequence's last
+ * block) and context lengths [num_seqs] of resident sequences, for the
+ * attention entry points (copy them to the device) */
+int pkv_bm_batch_tables(pkv_block_manager* bm, const int64_t* seqs, int num_seqs, int32_t* tables,
+                        int table_width, int32_t* context_lens);
+int pkv_bm_ref_count(pkv_block_manager* bm, int block);
+int pkv_bm_num_free(pkv_block_manager* bm);
+/* the free queue, head first; returns its length, fills at most `capacity` */
+int pkv_bm_free_queue(pkv_block_manager* bm, int32_t* out, int capacity);
+/* 1 and the block's 32-byte chain hash in out, or 0 when it has none */
+int pkv_bm_block_hash(pkv_block_manager* bm, int block, uint8_t* out);
+/* 1 when the prefix cache maps the block's hash to this block */
+int pkv_bm_is_cached(pkv_block_manager* bm, int block);
 
 #ifdef __cplusplus
 }

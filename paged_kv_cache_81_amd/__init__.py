@@ -16,7 +16,7 @@ import torch
 
 from ._lib import PKV_ATTN_CACHED_KV, PKV_BF16, PKV_F32, PagedKVError, check, lib
 
-__all__ = ["slot_mapping", "write", "gather", "partition_size", "workspace_bytes",
+__all__ = ["slot_mapping", "write", "gather", "copy_blocks", "partition_size", "workspace_bytes",
            "attention_decode", "attention_partitions", "attention_merge", "PagedKVError"]
 
 _DTYPES = {torch.float32: PKV_F32, torch.bfloat16: PKV_BF16}
@@ -118,6 +118,46 @@ def gather(kv_cache: torch.Tensor, block_tables: torch.Tensor, context_lens: tor
                              _dt(kv_cache), _stream(kv_cache))
     check(rc, "paged_kv_gather")
     return k, v
+
+
+def _pool_dims(t: torch.Tensor, name: str):
+    """[2, nb, b, hkv, d] pool on a GPU or in pinned host memory."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if not (t.is_cuda or t.is_pinned()):
+        raise ValueError(f"{name} must be on a GPU or in pinned host memory")
+    if not t.is_contiguous() or t.dim() != 5 or t.shape[0] != 2:
+        raise ValueError(f"{name} must be a contiguous [2, num_blocks, block_size, "
+                         "num_kv_heads, head_size] tensor")
+    return tuple(t.shape[1:])
+
+
+def copy_blocks(dst_cache: torch.Tensor, src_cache: torch.Tensor, src_blocks, dst_blocks) -> None:
+    """dst_cache[:, dst_blocks[i]] = src_cache[:, src_blocks[i]] (keys and values).
+
+    Copy-on-write copies (one pool) and swaps (a GPU pool and a pinned host
+    pool of the same block geometry).  Block id lists may be int32 tensors on
+    the GPU or Python sequences; the copy runs on the current stream of the
+    GPU pool's device."""
+    dnb, db, dh, dd = _pool_dims(dst_cache, "dst_cache")
+    snb, sb, sh, sd = _pool_dims(src_cache, "src_cache")
+    if (db, dh, dd) != (sb, sh, sd) or dst_cache.dtype != src_cache.dtype:
+        raise ValueError("pools differ in block geometry or element type")
+    gpu = dst_cache if dst_cache.is_cuda else src_cache
+    if not gpu.is_cuda:
+        raise ValueError("one pool must be on a GPU")
+    ids = []
+    for name, b in (("src_blocks", src_blocks), ("dst_blocks", dst_blocks)):
+        if not isinstance(b, torch.Tensor):
+            b = torch.tensor(list(b), dtype=torch.int32).to(gpu.device)
+        _need(b, name, torch.int32, 1, gpu.device)
+        ids.append(b)
+    if ids[0].shape[0] != ids[1].shape[0]:
+        raise ValueError("src_blocks and dst_blocks differ in length")
+    rc = lib.paged_kv_copy_blocks(dst_cache.data_ptr(), dnb, src_cache.data_ptr(), snb,
+                                  ids[0].data_ptr(), ids[1].data_ptr(), ids[0].shape[0],
+                                  db, dh, dd, _dt(gpu), _stream(gpu))
+    check(rc, "paged_kv_copy_blocks")
 
 
 def partition_size(num_seqs, num_q_heads, num_kv_heads, head_size, block_size, max_context_len,

@@ -16,10 +16,12 @@ PKV_BF16 = 1
 PKV_ATTN_CACHED_KV = 1
 
 STATUS = {0: "PKV_OK", -1: "PKV_ERR_INVALID", -2: "PKV_ERR_UNSUPPORTED",
-          -3: "PKV_ERR_WORKSPACE", -4: "PKV_ERR_HIP"}
+          -3: "PKV_ERR_WORKSPACE", -4: "PKV_ERR_HIP", -5: "PKV_ERR_NO_BLOCKS"}
+PKV_ERR_NO_BLOCKS = -5
 
 # every function include/paged_kv.h declares, with its C signature
 _i, _sz, _p, _f, _u = ctypes.c_int, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_float, ctypes.c_uint
+_i64 = ctypes.c_int64
 SIGNATURES = {
     "pkv_last_error": (ctypes.c_char_p, []),
     "paged_kv_slot_mapping": (_i, [_p, _p, _i, _p, _p, _i, _i, _i, _i, _p]),
@@ -33,6 +35,26 @@ SIGNATURES = {
                                         _i, _i, _p, _sz, _i, _u, _p]),
     "paged_attention_merge": (_i, [_p, _i, _p, _p, _p, _i, _p, _i, _i, _i, _i, _i, _i, _f,
                                    _i, _i, _p, _sz, _i, _u, _p]),
+    "paged_kv_copy_blocks": (_i, [_p, _i, _p, _i, _p, _p, _i, _i, _i, _i, _i, _p]),
+    "pkv_bm_create": (_p, [_i, _i, _i, _i]),
+    "pkv_bm_destroy": (None, [_p]),
+    "pkv_bm_set_free_order": (_i, [_p, _p, _i]),
+    "pkv_bm_allocate": (_i, [_p, _i64, _p, _i, _p]),
+    "pkv_bm_append": (_i, [_p, _i64, _p, _i, _p, _p, _p, _p]),
+    "pkv_bm_fork": (_i, [_p, _i64, _i64]),
+    "pkv_bm_free": (_i, [_p, _i64]),
+    "pkv_bm_swap_out": (_i, [_p, _p, _i, _p, _p, _i, _p]),
+    "pkv_bm_swap_in": (_i, [_p, _p, _i, _p, _p, _i, _p]),
+    "pkv_bm_num_tokens": (_i, [_p, _i64]),
+    "pkv_bm_is_swapped": (_i, [_p, _i64]),
+    "pkv_bm_block_table": (_i, [_p, _i64, _p, _i]),
+    "pkv_bm_slots": (_i, [_p, _i64, _i, _i, _p]),
+    "pkv_bm_batch_tables": (_i, [_p, _p, _i, _p, _i, _p]),
+    "pkv_bm_ref_count": (_i, [_p, _i]),
+    "pkv_bm_num_free": (_i, [_p]),
+    "pkv_bm_free_queue": (_i, [_p, _p, _i]),
+    "pkv_bm_block_hash": (_i, [_p, _i, _p]),
+    "pkv_bm_is_cached": (_i, [_p, _i]),
 }
 
 

@@ -40,6 +40,29 @@ int elem_bytes(pkv_dtype t) { return t == PKV_F32 ? 4 : (t == PKV_BF16 ? 2 : 0);
 
 int gcd(int a, int b) { return b ? gcd(b, a % b) : a; }
 
+// The address a kernel uses for p: p itself for device memory, the mapped
+// device address for pinned host memory.  Pageable host memory (or an
+// unknown pointer) is refused here rather than faulting in the kernel.
+bool device_address(const void* p, const char* what, void** out) {
+  hipPointerAttribute_t attr{};
+  if (hipPointerGetAttributes(&attr, p) != hipSuccess) {
+    (void)hipGetLastError();
+    set_error("%s: not device memory or pinned host memory", what);
+    return false;
+  }
+  if (attr.type == hipMemoryTypeDevice || attr.type == hipMemoryTypeManaged) {
+    *out = const_cast<void*>(p);
+    return true;
+  }
+  if (attr.type == hipMemoryTypeHost && attr.devicePointer) {
+    *out = attr.devicePointer;
+    return true;
+  }
+  set_error("%s: not device memory or pinned host memory (type %d)", what,
+            static_cast<int>(attr.type));
+  return false;
+}
+
 // Partitions are whole 32-token wave steps and whole blocks.
 int partition_unit(int B) { return 32 / gcd(32, B) * B; }
 
@@ -223,6 +246,44 @@ int paged_kv_gather(void* k_out, void* v_out, const void* kv_cache, const int32_
   }
   return launch_gather(k_out, v_out, kv_cache, block_tables, table_width, context_lens, num_seqs,
                        num_kv_heads, head_size, block_size, num_blocks, max_context_len, eb, stream);
+}
+
+int paged_kv_copy_blocks(void* dst_cache, int dst_num_blocks, const void* src_cache,
+                         int src_num_blocks, const int32_t* src_blocks, const int32_t* dst_blocks,
+                         int num_copies, int block_size, int num_kv_heads, int head_size,
+                         pkv_dtype dtype, hipStream_t stream) {
+  clear_error();
+  const int eb = elem_bytes(dtype);
+  if (eb == 0) { set_error("copy blocks: unknown dtype"); return PKV_ERR_INVALID; }
+  if (num_copies < 0 || num_copies > (1 << 30) || dst_num_blocks <= 0 || src_num_blocks <= 0 ||
+      block_size <= 0 || num_kv_heads <= 0 || head_size <= 0) {
+    set_error("copy blocks: bad sizes");
+    return PKV_ERR_INVALID;
+  }
+  if ((static_cast<int64_t>(head_size) * eb) % 16) {
+    set_error("copy blocks: head_size*%d bytes must be a multiple of 16", eb);
+    return PKV_ERR_UNSUPPORTED;
+  }
+  if (num_copies == 0) return PKV_OK;
+  if (!dst_cache || !src_cache || !src_blocks || !dst_blocks) {
+    set_error("copy blocks: null pointer");
+    return PKV_ERR_INVALID;
+  }
+  if (!aligned16(dst_cache) || !aligned16(src_cache)) {
+    set_error("copy blocks: pools must be 16-byte aligned");
+    return PKV_ERR_INVALID;
+  }
+  void *dst = nullptr, *src = nullptr, *src_ids = nullptr, *dst_ids = nullptr;
+  if (!device_address(dst_cache, "copy blocks: dst_cache", &dst) ||
+      !device_address(src_cache, "copy blocks: src_cache", &src) ||
+      !device_address(src_blocks, "copy blocks: src_blocks", &src_ids) ||
+      !device_address(dst_blocks, "copy blocks: dst_blocks", &dst_ids)) {
+    return PKV_ERR_INVALID;
+  }
+  const int64_t half = static_cast<int64_t>(block_size) * num_kv_heads * head_size * eb;
+  return launch_copy_blocks(dst, dst_num_blocks, src, src_num_blocks,
+                            static_cast<const int32_t*>(src_ids),
+                            static_cast<const int32_t*>(dst_ids), num_copies, half, stream);
 }
 
 int paged_attention_partition_size(int num_seqs, int num_q_heads, int num_kv_heads, int head_size,

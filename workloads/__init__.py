@@ -149,6 +149,11 @@ def _normal(rng: np.random.Generator, shape, dtype: str) -> np.ndarray:
     return out
 
 
+def normal(seed: int, shape, dtype: str = "bf16") -> np.ndarray:
+    """Seeded N(0,1) array of ``shape`` (bf16 bit patterns or float32)."""
+    return _normal(np.random.default_rng(seed), shape, dtype)
+
+
 def _blocks_to_hold(lens: np.ndarray, block_size: int) -> np.ndarray:
     """Blocks an allocator reserves so that ``len`` tokens fit (ceiling division)."""
     return np.ceil(np.asarray(lens, dtype=np.float64) / block_size).astype(np.int64)
