@@ -15,7 +15,8 @@ bytes the queries read through their block tables (sum over sequences of
 L * 2 * num_kv_heads * head_size * element bytes) divided by the step time.
 ``roofline`` relates the attention kernel alone (the average of per-launch HIP
 events on the launch stream) to the MI355X HBM peak; ``cpu_baseline`` times
-the CPU oracle on a bounded sample of the same workload.
+the CPU oracle on a bounded sample of the same workload; ``block_ops`` times
+the copy-on-write and swap block copies at the workload's block geometry.
 
 Usage: python bench.py [--steps K] [--warmup W] [--workload NAME] [--layers N]
 """
@@ -183,6 +184,71 @@ def cpu_baseline(w, seconds: float) -> dict:
             "us_per_step_extrapolated": round(dt / n * w.num_seqs * 1e6, 1)}
 
 
+def block_ops(w, dev, reps: int = 10) -> dict:
+    """Copy-on-write and swap copies at the workload's block geometry, each
+    one ``paged_kv_copy_blocks`` launch timed with HIP events on its stream:
+    one block copied per sequence within a device pool (the copy a forked
+    sample makes before its first write into a shared block), and a group of
+    blocks swapped to a pinned host pool and back (PCIe).  Caches are cold:
+    a 1 GiB fill runs before each launch.  Bytes count each
+    block's keys and values once read and once written; ``memcpy_GBps`` is a
+    plain contiguous device/host copy of the same bytes for comparison."""
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_81_amd as pkv
+
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    geo = (w.block_size, w.num_kv_heads, w.head_size)
+    blk = 2 * int(np.prod(geo)) * (2 if w.dtype == "bf16" else 4)
+    rng = np.random.default_rng(5)
+    cur = torch.cuda.current_stream(dev)
+
+    # a fill queued before each timed launch keeps the GPU busy while the
+    # host prepares the launch, so the events bracket the copy alone
+    filler = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(reps)]
+        for i, (a, b) in enumerate(ev):
+            filler.fill_(i)
+            a.record(cur)
+            fn()
+            b.record(cur)
+        torch.cuda.synchronize()
+        return float(np.mean([a.elapsed_time(b) for a, b in ev])) * 1e3  # us
+
+    out = {"block_bytes": blk}
+    n_dev = 2048
+    pool = torch.empty((2, n_dev) + geo, dtype=tdt, device=dev).normal_()
+    ids = rng.permutation(n_dev).astype(np.int32)
+    n = w.num_seqs
+    src = torch.from_numpy(ids[:n]).to(dev)
+    dst = torch.from_numpy(ids[n:2 * n]).to(dev)
+    us = timed(lambda: pkv.copy_blocks(pool, pool, src, dst))
+    out["cow_copy"] = {"copies": n, "us": round(us, 2), "GBps": round(2 * n * blk / us / 1e3, 1)}
+
+    n_swap = 512
+    host = torch.empty((2, n_swap) + geo, dtype=tdt, pin_memory=True)
+    src = torch.from_numpy(ids[:n_swap]).to(dev)
+    hid = torch.arange(n_swap, dtype=torch.int32, device=dev)
+    us_out = timed(lambda: pkv.copy_blocks(host, pool, src, hid))
+    us_in = timed(lambda: pkv.copy_blocks(pool, host, hid, src))
+    flat_dev = torch.empty(n_swap * blk, dtype=torch.uint8, device=dev)
+    flat_host = torch.empty(n_swap * blk, dtype=torch.uint8, pin_memory=True)
+    us_d2h = timed(lambda: flat_host.copy_(flat_dev, non_blocking=True))
+    us_h2d = timed(lambda: flat_dev.copy_(flat_host, non_blocking=True))
+    b = n_swap * blk
+    out["swap_out"] = {"blocks": n_swap, "us": round(us_out, 1), "GBps": round(b / us_out / 1e3, 1),
+                       "memcpy_GBps": round(b / us_d2h / 1e3, 1)}
+    out["swap_in"] = {"blocks": n_swap, "us": round(us_in, 1), "GBps": round(b / us_in / 1e3, 1),
+                      "memcpy_GBps": round(b / us_h2d / 1e3, 1)}
+    return out
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -196,6 +262,8 @@ def main() -> int:
                     help="also evict caches before every per-kernel timing launch")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-block-ops", action="store_true",
+                    help="skip the copy-on-write and swap copy timings")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (known bytes), for "
                          "scaling hardware byte counters")
@@ -415,6 +483,9 @@ def main() -> int:
         "kernel_us": {k: round(v, 2) for k, v in kernel_us.items()},
         "kernel_source_sha": kernel_source_sha(),
     }
+    if not args.no_block_ops:
+        result["block_ops"] = block_ops(w, dev)
+        log(f"[bench] block ops: {result['block_ops']}")
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle")
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)

@@ -1,4 +1,5 @@
-"""CPU oracle for paged decode attention and the paged KV write.
+"""CPU oracle for paged decode and prefill attention, the paged KV write and
+the block manager.
 
 TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
 benchmark's CPU-baseline leg may import or call anything in this package.  The
@@ -21,6 +22,7 @@ from .paged_attention import (  # noqa: F401
     attention_ref,
     blocks_needed,
     cache_shape_from_bytes,
+    chunk_positions,
     gather_ref,
     kv_bytes_per_token,
     last_block_fill,
@@ -29,6 +31,7 @@ from .paged_attention import (  # noqa: F401
     page_bytes,
     paged_attention_ref,
     partition_stats_ref,
+    prefill_attention_ref,
     slot_mapping_ref,
     slot_of,
     to_f64,

@@ -33,7 +33,9 @@ Readings where the pages are silent (each also listed in the design notes):
    (contiguous groups);
 6. a sequence with ``L_s == 0`` attends to nothing and its output is zero;
 7. a split into partitions of ``P`` tokens is merged by the log-sum-exp rule
-   (the pages do not describe a split; it is an exact identity).
+   (the pages do not describe a split; it is an exact identity);
+8. a chunk of query tokens (prefill) is the last tokens of its sequence, its
+   own K/V already in the cache, and each of its tokens attends causally.
 """
 from __future__ import annotations
 
@@ -198,6 +200,56 @@ def paged_attention_ref(query: np.ndarray, kv: np.ndarray, block_tables: np.ndar
     for s in (range(S) if seqs is None else seqs):
         k, v = gather_ref(kv, block_tables[s], int(context_lens[s]))
         out[s] = attention_ref(to_f64(query[s], dtype), to_f64(k, dtype), to_f64(v, dtype), scale)
+    return out
+
+
+# ---------------------------------------------------------------- prefill / chunked prefill
+
+def chunk_positions(context_len: int, chunk_len: int) -> np.ndarray:
+    """Positions of a chunk of ``chunk_len`` query tokens that ends a sequence
+    of ``context_len`` tokens: ``context_len - chunk_len .. context_len - 1``.
+
+    Reading 8: a chunk's own K/V is in the cache when it attends (as the decode
+    token's is, reading 3), so the chunk is the last ``chunk_len`` tokens of
+    the sequence.  Positions restart at 0 for every sequence of a batch
+    [walkthrough, "ブロックアロケーションの基本概念" (basics of block
+    allocation): concatenated prompts keep their own position ids].
+    """
+    if chunk_len > context_len or chunk_len < 0:
+        raise ValueError("a chunk cannot be longer than its sequence")
+    return np.arange(context_len - chunk_len, context_len, dtype=np.int64)
+
+
+def prefill_attention_ref(query: np.ndarray, kv: np.ndarray, block_tables: np.ndarray,
+                          context_lens: np.ndarray, query_start: np.ndarray, scale: float,
+                          dtype: str) -> np.ndarray:
+    """Causal attention of chunks of query tokens over their paged sequences
+    (float64): the prompt (prefill) step, and chunked prefill.
+
+    [review, "프리필(Prefill) 단계" (prefill stage)]: a prompt is processed with
+    ordinary self-attention, each token attending to itself and the tokens
+    before it; [review, "디코딩 과정" (the decoding process)]: the input
+    tokens of all requests of an iteration are joined into one sequence and
+    the kernel reads earlier K/V through the block tables;
+    [walkthrough, "ブロックアロケーションの基本概念"]: an attention mask keeps
+    each joined sequence to itself.
+
+    ``query`` is ``[T, Hq, D]``: rows ``query_start[s] .. query_start[s+1]-1``
+    are sequence ``s``'s chunk, whose tokens sit at :func:`chunk_positions`.
+    The token at position ``p`` attends to the sequence's keys ``0 .. p``.
+    Returns ``[T, Hq, D]``.
+    """
+    T = query.shape[0]
+    out = np.zeros(query.shape, dtype=np.float64)
+    for s in range(len(context_lens)):
+        r0, r1 = int(query_start[s]), int(query_start[s + 1])
+        L = int(context_lens[s])
+        pos = chunk_positions(L, r1 - r0)
+        k, v = gather_ref(kv, block_tables[s], L)
+        k, v = to_f64(k, dtype), to_f64(v, dtype)
+        for i, p in enumerate(pos):
+            out[r0 + i] = attention_ref(to_f64(query[r0 + i], dtype), k[:p + 1], v[:p + 1], scale)
+    assert r1 <= T
     return out
 
 

@@ -572,6 +572,89 @@ def pin_copy_blocks(o) -> None:
     assert np.array_equal(host[:, 1], before[:, 2]) and not host[:, [0, 2]].any()
 
 
+# ------------------------------------------------------------------ prefill
+
+def _concat_queries(rng, chunk_lens, Hq, D):
+    starts = np.concatenate([[0], np.cumsum(chunk_lens)]).astype(np.int64)
+    return _f32(rng.standard_normal((int(starts[-1]), Hq, D))), starts
+
+
+def _f32(x):
+    """float64 values that float32 holds exactly (so "f32" inputs widen back
+    to the same numbers)."""
+    return np.asarray(x).astype(np.float32).astype(np.float64)
+
+
+def _toy_paged_f32(rng, lens, B, Hkv, D, NB):
+    kv, tables, Ks, Vs = _toy_paged(rng, lens, B, Hkv, D, NB)
+    return _f32(kv), tables, [_f32(k) for k in Ks], [_f32(v) for v in Vs]
+
+
+def pin_prefill_sdpa(o) -> None:
+    """Whole prompts (each chunk is its entire sequence), several joined in one
+    batch, against torch's causal scaled_dot_product_attention on the CPU in
+    float64, one sequence at a time from its contiguous K/V."""
+    import torch
+    rng = np.random.default_rng(31)
+    for (Hq, Hkv, D, B, lens) in ((4, 4, 16, 4, [5, 17, 1]), (6, 2, 8, 16, [40, 16]),
+                                  (8, 1, 32, 8, [33])):
+        NB = sum((n + B - 1) // B for n in lens) + 3
+        kv, tables, Ks, Vs = _toy_paged_f32(rng, lens, B, Hkv, D, NB)
+        q, starts = _concat_queries(rng, lens, Hq, D)
+        scale = 1.0 / math.sqrt(D)
+        got = o.prefill_attention_ref(q, kv, tables, np.array(lens), starts, scale, "f32")
+        G = Hq // Hkv
+        for s, n in enumerate(lens):
+            tq = torch.from_numpy(q[starts[s]:starts[s + 1]]).permute(1, 0, 2)[None]
+            tk = torch.from_numpy(Ks[s]).permute(1, 0, 2).repeat_interleave(G, dim=0)[None]
+            tv = torch.from_numpy(Vs[s]).permute(1, 0, 2).repeat_interleave(G, dim=0)[None]
+            ref = torch.nn.functional.scaled_dot_product_attention(
+                tq, tk, tv, is_causal=True, scale=scale)[0].permute(1, 0, 2).numpy()
+            assert np.abs(got[starts[s]:starts[s + 1]] - ref).max() < 1e-12, (Hq, Hkv, D, n)
+
+
+def pin_prefill_chunks(o) -> None:
+    """A chunk that continues a sequence gives the rows a whole-prompt pass
+    gives for the same positions (chunked prefill), and a chunk of one token
+    is the decode step."""
+    rng = np.random.default_rng(37)
+    Hq, Hkv, D, B = 6, 3, 8, 4
+    lens = [9, 30, 1, 16]
+    kv, tables, _, _ = _toy_paged_f32(rng, lens, B, Hkv, D, 40)
+    L = np.array(lens)
+    q_all, starts_all = _concat_queries(rng, lens, Hq, D)
+    whole = o.prefill_attention_ref(q_all, kv, tables, L, starts_all, 0.4, "f32")
+    for chunk in ([4, 11, 1, 16], [1, 30, 1, 3], [9, 1, 1, 1]):
+        starts = np.concatenate([[0], np.cumsum(chunk)]).astype(np.int64)
+        rows = np.concatenate([np.arange(starts_all[s + 1] - c, starts_all[s + 1])
+                               for s, c in enumerate(chunk)])
+        got = o.prefill_attention_ref(q_all[rows], kv, tables, L, starts, 0.4, "f32")
+        assert np.abs(got - whole[rows]).max() < 1e-13, chunk
+    last = starts_all[1:] - 1
+    dec = o.paged_attention_ref(q_all[last], kv, tables, L, 0.4, "f32")
+    got = o.prefill_attention_ref(q_all[last], kv, tables, L, np.arange(len(lens) + 1), 0.4, "f32")
+    assert np.abs(got - dec).max() < 1e-13
+
+
+def pin_prefill_closed_forms(o) -> None:
+    """The first token of a prompt sees only itself (its value, exactly); with
+    every key equal, the token at position p gets the mean of values 0..p."""
+    rng = np.random.default_rng(41)
+    Hq, Hkv, D, B, n = 4, 2, 8, 4, 13
+    kv, tables, Ks, Vs = _toy_paged_f32(rng, [n], B, Hkv, D, 8)
+    q, starts = _concat_queries(rng, [n], Hq, D)
+    got = o.prefill_attention_ref(q, kv, tables, np.array([n]), starts, 0.5, "f32")
+    assert np.array_equal(got[0], np.repeat(Vs[0][0], Hq // Hkv, axis=0))
+    for t in range(n):  # all keys equal
+        b = tables[0, t // B]
+        kv[0, b, t % B] = Ks[0][0]
+    got = o.prefill_attention_ref(q, kv, tables, np.array([n]), starts, 0.5, "f32")
+    for p in range(n):
+        mean = np.repeat(Vs[0][:p + 1].mean(axis=0), Hq // Hkv, axis=0)
+        assert np.abs(got[p] - mean).max() < 1e-14, p
+    assert list(o.chunk_positions(10, 3)) == [7, 8, 9] and len(o.chunk_positions(4, 0)) == 0
+
+
 ALL_PINS = [
     pin_block_counts,
     pin_waste_bound,
@@ -591,4 +674,7 @@ ALL_PINS = [
     pin_block_hash_chain,
     pin_block_manager_invariants,
     pin_copy_blocks,
+    pin_prefill_sdpa,
+    pin_prefill_chunks,
+    pin_prefill_closed_forms,
 ]

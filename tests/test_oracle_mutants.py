@@ -211,7 +211,32 @@ def _copy_blocks_keys_only(kv, pairs, dst=None):
     return out
 
 
+def _prefill_with(positions, causal=True, shift=0):
+    """A prefill oracle whose chunk positions or mask bound are planted."""
+    def f(query, kv, tables, lens, starts, scale, dtype):
+        out = np.zeros(query.shape)
+        for s_, L in enumerate(lens):
+            r0, r1 = int(starts[s_]), int(starts[s_ + 1])
+            k, v = pa.gather_ref(kv, tables[s_], int(L))
+            k, v = pa.to_f64(k, dtype), pa.to_f64(v, dtype)
+            for i, p in enumerate(positions(int(L), r0, r1)):
+                stop = int(L) if not causal else max(0, p + 1 + shift)
+                out[r0 + i] = pa.attention_ref(pa.to_f64(query[r0 + i], dtype), k[:stop], v[:stop],
+                                               scale)
+        return out
+    return f
+
+
 MUTANTS = {
+    "prefill_top_left": dict(prefill_attention_ref=_prefill_with(lambda L, r0, r1: range(r1 - r0))),
+    "prefill_global_rows": dict(prefill_attention_ref=_prefill_with(
+        lambda L, r0, r1: [min(L - 1, r) for r in range(r0, r1)])),
+    "prefill_no_mask": dict(prefill_attention_ref=_prefill_with(
+        lambda L, r0, r1: range(L - (r1 - r0), L), causal=False)),
+    "prefill_mask_excludes_self": dict(prefill_attention_ref=_prefill_with(
+        lambda L, r0, r1: range(L - (r1 - r0), L), shift=-1)),
+    "prefill_mask_one_ahead": dict(prefill_attention_ref=_prefill_with(
+        lambda L, r0, r1: range(L - (r1 - r0), L), shift=1)),
     "bm_free_forward": dict(RefBlockManager=_FreeForward),
     "bm_no_eviction": dict(RefBlockManager=_NoEviction),
     "bm_cow_keeps_ref": dict(RefBlockManager=_CowKeepsRef),
