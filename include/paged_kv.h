@@ -233,6 +233,46 @@ int paged_attention_merge(void* out, pkv_dtype out_dtype, const void* query,
                           hipStream_t stream);
 
 /*
+ * paged_attention_prefill -- causal attention of chunks of query tokens over
+ * their paged sequences: the prompt step (prefill) and chunked prefill.
+ *
+ * A prompt is processed with ordinary self-attention, every token attending
+ * to itself and the tokens before it (studying-code.tistory.com vLLM review,
+ * "프리필(Prefill) 단계"); the input tokens of all requests of an iteration
+ * are joined into one sequence, and the kernel reads earlier K/V through the
+ * block tables (the same review, "디코딩 과정"); each joined request keeps
+ * its own positions from 0 and attends only to itself (itan.pw walk-through,
+ * "ブロックアロケーションの基本概念").  Sequence s's chunk is query rows
+ * [query_start[s], query_start[s+1]); its K/V must already be in the cache
+ * (written with paged_kv_write), so the chunk is the last chunk_len tokens of
+ * the sequence: row i sits at position context_lens[s] - chunk_len + i and
+ * attends keys 0 .. that position.  A whole prompt is the chunk with
+ * chunk_len == context_len; a chunk continuing cached tokens (an earlier
+ * chunk, or prefix-cache hits) has chunk_len < context_len; decode is
+ * chunk_len == 1.
+ *
+ *   out          out_dtype [num_tokens][num_q_heads][head_size]; rows outside
+ *                every chunk are not written
+ *   query        dtype [num_tokens][num_q_heads][head_size]
+ *   query_start  int32 [num_seqs + 1], device, non-decreasing, last <= num_tokens
+ *   max_query_len  host int >= every chunk length (sizes the grid); a longer
+ *                chunk, a chunk longer than its sequence, or a sequence longer
+ *                than table_width * block_size gives NaN rows; an
+ *                out-of-range table entry gives NaN for the rows reading it
+ *   kv_cache, block_tables, table_width, context_lens, num_blocks: as for
+ *                paged_attention_decode
+ * Supported: head_size 64 or 128; bf16: block_size 8, 16, 32 or 64 (matrix
+ * cores; scores and the weighted sum accumulate in fp32); fp32: any
+ * block_size (vector ALU).  Needs no workspace and no clearing.
+ */
+int paged_attention_prefill(void* out, pkv_dtype out_dtype, const void* query,
+                            const int32_t* query_start, int num_tokens, int max_query_len,
+                            const void* kv_cache, const int32_t* block_tables, int table_width,
+                            const int32_t* context_lens, int num_seqs, int num_q_heads,
+                            int num_kv_heads, int head_size, int block_size, int num_blocks,
+                            float scale, pkv_dtype dtype, hipStream_t stream);
+
+/*
  * paged_kv_copy_blocks -- copy whole blocks (keys and values) between two
  * pools of the same geometry: dst_cache[:, dst_blocks[i]] =
  * src_cache[:, src_blocks[i]] for every i.

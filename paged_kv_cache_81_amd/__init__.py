@@ -17,7 +17,8 @@ import torch
 from ._lib import PKV_ATTN_CACHED_KV, PKV_BF16, PKV_F32, PagedKVError, check, lib
 
 __all__ = ["slot_mapping", "write", "gather", "copy_blocks", "partition_size", "workspace_bytes",
-           "attention_decode", "attention_partitions", "attention_merge", "PagedKVError"]
+           "attention_decode", "attention_partitions", "attention_merge", "attention_prefill",
+           "PagedKVError"]
 
 _DTYPES = {torch.float32: PKV_F32, torch.bfloat16: PKV_BF16}
 
@@ -233,6 +234,42 @@ def attention_merge(*a, **k) -> torch.Tensor:
     """Second launch of attention_decode (log-sum-exp merge); same arguments."""
     out, args = _decode_args(*_norm(*a, **k))
     check(lib.paged_attention_merge(*args), "paged_attention_merge")
+    return out
+
+
+def attention_prefill(query: torch.Tensor, kv_cache: torch.Tensor, block_tables: torch.Tensor,
+                      context_lens: torch.Tensor, query_start: torch.Tensor, scale: float,
+                      max_query_len: Optional[int] = None, out_dtype=torch.float32,
+                      out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Causal attention of each sequence's chunk of query rows
+    (``query[query_start[s]:query_start[s+1]]``, the last tokens of sequence
+    ``s``, whose K/V is already cached) over its paged K/V.  ``[T, Hq, D]``.
+    Without ``max_query_len`` the chunk lengths are read back to the host."""
+    nb, b, hkv, d = _cache_dims(kv_cache)
+    dev = kv_cache.device
+    _need(query, "query", kv_cache.dtype, 3, dev)
+    T, hq, dq = query.shape
+    if dq != d:
+        raise ValueError(f"query head size {dq} differs from the cache's {d}")
+    _need(block_tables, "block_tables", torch.int32, 2, dev)
+    _need(context_lens, "context_lens", torch.int32, 1, dev)
+    _need(query_start, "query_start", torch.int32, 1, dev)
+    S = context_lens.shape[0]
+    if block_tables.shape[0] != S or query_start.shape[0] != S + 1:
+        raise ValueError("block_tables, context_lens and query_start disagree on the batch")
+    if max_query_len is None:
+        max_query_len = int((query_start[1:] - query_start[:-1]).max().item()) if S else 0
+    if out is None:
+        out = torch.empty((T, hq, d), dtype=out_dtype, device=dev)
+    _need(out, "out", None, 3, dev)
+    if tuple(out.shape) != (T, hq, d) or out.dtype not in _DTYPES:
+        raise ValueError("out must be a float32 or bfloat16 [T, Hq, D] tensor")
+    rc = lib.paged_attention_prefill(out.data_ptr(), _dt(out), query.data_ptr(),
+                                     query_start.data_ptr(), T, max_query_len, kv_cache.data_ptr(),
+                                     block_tables.data_ptr(), block_tables.shape[1],
+                                     context_lens.data_ptr(), S, hq, hkv, d, b, nb, float(scale),
+                                     _dt(kv_cache), _stream(kv_cache))
+    check(rc, "paged_attention_prefill")
     return out
 
 

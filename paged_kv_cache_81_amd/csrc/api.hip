@@ -525,6 +525,71 @@ int decode_impl(int phases, void* out, pkv_dtype out_dtype, const void* query,
 
 extern "C" {
 
+int paged_attention_prefill(void* out, pkv_dtype out_dtype, const void* query,
+                            const int32_t* query_start, int num_tokens, int max_query_len,
+                            const void* kv_cache, const int32_t* block_tables, int table_width,
+                            const int32_t* context_lens, int num_seqs, int num_q_heads,
+                            int num_kv_heads, int head_size, int block_size, int num_blocks,
+                            float scale, pkv_dtype dtype, hipStream_t stream) {
+  clear_error();
+  if (!shape_ok(num_seqs, num_q_heads, num_kv_heads, head_size, block_size, 0, dtype))
+    return PKV_ERR_INVALID;
+  if (out_dtype != PKV_F32 && out_dtype != PKV_BF16) { set_error("unknown out_dtype"); return PKV_ERR_INVALID; }
+  if (num_tokens < 0 || max_query_len < 0) {
+    set_error("num_tokens %d and max_query_len %d must be >= 0", num_tokens, max_query_len);
+    return PKV_ERR_INVALID;
+  }
+  if (head_size != 64 && head_size != 128) {
+    set_error("head_size %d is not built (64 or 128)", head_size);
+    return PKV_ERR_UNSUPPORTED;
+  }
+  if (dtype == PKV_BF16 && block_size != 8 && block_size != 16 && block_size != 32 &&
+      block_size != 64) {
+    set_error("bf16 prefill: block_size %d is not built (8, 16, 32 or 64)", block_size);
+    return PKV_ERR_UNSUPPORTED;
+  }
+  if (table_width <= 0 || num_blocks <= 0) { set_error("table_width and num_blocks must be positive"); return PKV_ERR_INVALID; }
+  if (!std::isfinite(scale)) { set_error("scale is not finite"); return PKV_ERR_INVALID; }
+  if (num_q_heads > kGridYZ) { set_error("num_q_heads %d above %d", num_q_heads, kGridYZ); return PKV_ERR_UNSUPPORTED; }
+  if (num_seqs == 0 || num_tokens == 0 || max_query_len == 0) return PKV_OK;
+  if (!out || !query || !query_start || !kv_cache || !block_tables || !context_lens) {
+    set_error("null pointer argument");
+    return PKV_ERR_INVALID;
+  }
+  if (!aligned16(out) || !aligned16(query) || !aligned16(kv_cache)) {
+    set_error("out, query and kv_cache must be 16-byte aligned");
+    return PKV_ERR_INVALID;
+  }
+  PrefillArgs a{};
+  a.out = out;
+  a.query = query;
+  a.kv = kv_cache;
+  a.tables = block_tables;
+  a.lens = context_lens;
+  a.qstart = query_start;
+  a.width = table_width;
+  a.S = num_seqs;
+  a.T = num_tokens;
+  a.Hq = num_q_heads;
+  a.Hkv = num_kv_heads;
+  a.D = head_size;
+  a.B = block_size;
+  a.NB = num_blocks;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.out_bf16 = out_dtype == PKV_BF16;
+  a.max_q = max_query_len;
+  if (dtype == PKV_F32) return launch_prefill_f32(a, stream);
+  a.qtiles = static_cast<int>(cdiv64(max_query_len, 128));
+  const int64_t total = static_cast<int64_t>(num_seqs) * num_q_heads * a.qtiles;
+  if (total > (int64_t{1} << 30)) {
+    set_error("prefill grid of %lld work items is too large", static_cast<long long>(total));
+    return PKV_ERR_UNSUPPORTED;
+  }
+  a.total = static_cast<int>(total);
+  a.items_per_xcd = static_cast<int>(cdiv64(total, 8));
+  return launch_prefill_bf16(a, stream);
+}
+
 int paged_attention_decode(PKV_DECODE_PARAMS) { return decode_impl(kAttend | kMerge, PKV_DECODE_ARGS); }
 
 int paged_attention_partitions(PKV_DECODE_PARAMS) { return decode_impl(kAttend, PKV_DECODE_ARGS); }

@@ -155,6 +155,27 @@ inline void stream_lds_plan(int G, int D, bool k_tile, int* slots, int* wave_flo
   *wave_floats = (tile + k * stream_slot_floats(G, D) + 3) / 4 * 4;
 }
 
+// Prefill (chunked) attention: sequence s's chunk is query rows
+// [qstart[s], qstart[s + 1]) at positions lens[s] - chunk_len .. lens[s] - 1.
+struct PrefillArgs {
+  void* out;             // [T][Hq][D] fp32 or bf16
+  const void* query;     // [T][Hq][D]
+  const void* kv;        // [2][NB][B][Hkv][D]
+  const int32_t* tables;
+  const int32_t* lens;
+  const int32_t* qstart;  // [S + 1]
+  int width, S, T, Hq, Hkv, D, B, NB;
+  float scale_log2;
+  int out_bf16;
+  int max_q;           // longest chunk the grid covers (longer ones give NaN)
+  int qtiles;          // query tiles per (sequence, head) in the grid
+  int items_per_xcd;   // work items each XCD takes
+  int total;           // work items: S * Hq * qtiles
+};
+
+int launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream);
+int launch_prefill_f32(const PrefillArgs& a, hipStream_t stream);
+
 int launch_attention_bf16(const AttnArgs& a, hipStream_t stream);
 int launch_attention_bf16_stream(const AttnArgs& a, hipStream_t stream);
 int launch_attention_f32(const AttnArgs& a, hipStream_t stream);

@@ -1,0 +1,445 @@
+// Paged prefill attention (gfx950): causal attention of chunks of query
+// tokens over their sequences' paged K/V -- a whole prompt, or one chunk of
+// it whose earlier tokens are already cached (chunked prefill, prefix-cache
+// hits).  Sequence s's chunk is query rows [qstart[s], qstart[s+1]); row i
+// of it sits at position lens[s] - chunk_len + i and attends keys 0 .. its
+// position of its own sequence, read through the block table.
+//
+// bf16 caches: a workgroup (4 waves) takes 128 query rows of one query head;
+// wave w takes rows 32w .. 32w + 31 as two 16-row column blocks.  Keys are
+// walked in steps of 64: the workgroup loads a step's K and V rows (through
+// the table) into one of two LDS buffers while the waves compute on the
+// other, so each K/V row is read from memory once per workgroup and 128
+// query rows use it.  Per 32 keys a wave runs, for each column block, the
+// scores S^T = K . Q^T on v_mfma_f32_16x16x32_bf16 (K rows from LDS as the
+// A operand, the query rows as B), the causal mask, an online softmax per
+// query row in the log2 domain, and O^T += V^T . P^T with P split into bf16
+// hi + lo parts and the values transposed in registers (dims permuted so
+// every LDS read is a contiguous piece of a V row).  Rows are finished
+// through LDS so every global store covers whole rows.
+//
+// fp32 caches: one wave per (query row, head), keys in batches of 64 with an
+// online softmax (vector ALU; a reference-precision path).
+#include "attention_bf16_wave.hpp"
+
+#include <cmath>
+
+namespace pkv {
+namespace {
+
+constexpr int kPThreads = 256;
+constexpr int kPRows = 128;  // query rows per workgroup (4 waves x 32)
+constexpr int kPKeys = 64;   // keys per LDS step
+constexpr int kXcds = 8;
+
+template <int D>
+struct PGeom {
+  static constexpr int QC = D / 32;   // score MFMAs per 16 x 16 tile
+  static constexpr int NV = D / 16;   // output blocks; dims per lane per V row
+  static constexpr int NW = NV / 2;   // 32-bit words per lane per V row
+  static constexpr int NCH = D / 8;   // 16-byte chunks per row
+  static constexpr int KROW = 2 * D;  // LDS bytes per K row (chunks skewed)
+  static constexpr int VROW = 2 * D + 16;  // LDS bytes per V row (padded)
+  static constexpr int KBYTES = kPKeys * KROW;
+  static constexpr int BUF = KBYTES + kPKeys * VROW;
+  static constexpr int CPT = kPKeys * NCH / kPThreads;  // chunks per thread per tensor
+  static constexpr int SROW = D + 4;  // floats per finished row in LDS
+  static constexpr int LDS = 2 * BUF > kPRows * SROW * 4 ? 2 * BUF : kPRows * SROW * 4;
+};
+
+// chunk ch of K row t sits at chunk position (ch + kskew(t)) mod NCH, so both
+// the row-wise stores and the MFMA-layout reads (16 rows, one chunk each)
+// spread over the banks
+template <int NCH>
+__device__ __forceinline__ int kskew(int t) { return (t * NCH / 16) % NCH; }
+
+template <int D, int B>
+__global__ void __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(2)))
+prefill_bf16_kernel(PrefillArgs a) {
+  using Gm = PGeom<D>;
+  constexpr int QC = Gm::QC, NV = Gm::NV, NW = Gm::NW, NCH = Gm::NCH, CPT = Gm::CPT;
+  extern __shared__ __align__(16) char lds[];
+  const int tid = threadIdx.x;
+  const int wv = tid >> 6, lane = tid & 63, j = lane & 15, g = lane >> 4;
+
+  // XCD-blocked numbering: XCD b % 8 runs items [b%8 * per, ...), so the
+  // items of one (sequence, kv head) share an L2; within a (sequence, head)
+  // the latest (longest) query tile comes first
+  const int bid = blockIdx.x;
+  const int item = (bid % kXcds) * a.items_per_xcd + bid / kXcds;
+  if (item >= a.total) return;
+  const int xr = item % a.qtiles;
+  const int sh = item / a.qtiles;
+  const int h = sh % a.Hq, s = sh / a.Hq;
+  const int x = a.qtiles - 1 - xr;
+  const int q0 = a.qstart[s];
+  const int qlen = a.qstart[s + 1] - q0;
+  if (q0 < 0 || qlen < 0 || q0 + qlen > a.T) return;  // rows outside the output
+  const int row0 = x * kPRows;
+  if (row0 >= qlen) return;
+  const int L = a.lens[s];
+  const int G = a.Hq / a.Hkv, kvh = h / G;
+  const bool bad_seq = L < 0 || (L + B - 1) / B > a.width || qlen > L || qlen > a.max_q;
+  const int tile_rows = min(kPRows, qlen - row0);
+  const int P0 = L - qlen + row0;  // position of the tile's first row
+  const int kend = bad_seq ? 0 : max(0, min(L, P0 + tile_rows));  // keys [0, kend)
+  const int nsteps = (kend + kPKeys - 1) / kPKeys;
+
+  // this wave's rows: column j of block cb is tile row 32 wv + 16 cb + j
+  const int wr0 = 32 * wv;
+  const int wave_rows = max(0, min(32, tile_rows - wr0));
+  const int wmin = P0 + wr0;                   // position of its first row
+  const int wmax = wave_rows > 0 ? P0 + wr0 + wave_rows - 1 : -1;  // ... and of its last
+  int pos[2];
+  bf16x8 qf[2][QC];
+  const uint16_t* qb = static_cast<const uint16_t*>(a.query);
+#pragma unroll
+  for (int cb = 0; cb < 2; ++cb) {
+    const int r = wr0 + 16 * cb + j;
+    const bool live = r < tile_rows;
+    pos[cb] = live ? P0 + r : kend - 1;
+    const uint16_t* qp = qb + (static_cast<int64_t>(q0 + row0 + r) * a.Hq + h) * D + 8 * g;
+#pragma unroll
+    for (int c = 0; c < QC; ++c) qf[cb][c] = live ? wave::load_bf16x8<false>(qp + 32 * c) : bf16x8{};
+  }
+
+  const int64_t rowst = static_cast<int64_t>(a.Hkv) * D;  // elements between slots
+  const uint16_t* kbase = static_cast<const uint16_t*>(a.kv) + static_cast<int64_t>(kvh) * D;
+  const uint16_t* vbase = kbase + static_cast<int64_t>(a.NB) * B * rowst;
+  const int32_t* trow = a.tables + static_cast<int64_t>(s) * a.width;
+  bool bad = false;
+
+  // global -> registers (step q) and registers -> LDS: thread chunk
+  // e = tid + 256 i is row e / NCH, chunk e % NCH of the step's K and V;
+  // rows at or past kend are zeros (the K/V there may be unwritten)
+  wave::u32x4 pk[CPT], pv[CPT];
+  auto issue = [&](int q) {
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int e = tid + kPThreads * i;
+      const int key = q * kPKeys + e / NCH;
+      wave::u32x4 kz{0u, 0u, 0u, 0u}, vz{0u, 0u, 0u, 0u};
+      if (key < kend) {
+        const int phys = trow[key / B];
+        if (phys >= 0 && phys < a.NB) {
+          const int64_t off = (static_cast<int64_t>(phys) * B + key % B) * rowst + 8 * (e % NCH);
+          kz = *reinterpret_cast<const wave::u32x4*>(kbase + off);
+          vz = *reinterpret_cast<const wave::u32x4*>(vbase + off);
+        } else {
+          bad = true;
+        }
+      }
+      pk[i] = kz;
+      pv[i] = vz;
+    }
+  };
+  auto stage = [&](char* buf) {
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int e = tid + kPThreads * i;
+      const int t = e / NCH, ch = e % NCH;
+      *reinterpret_cast<wave::u32x4*>(buf + t * Gm::KROW + 16 * ((ch + kskew<NCH>(t)) % NCH)) = pk[i];
+      *reinterpret_cast<wave::u32x4*>(buf + Gm::KBYTES + t * Gm::VROW + 16 * ch) = pv[i];
+    }
+  };
+
+  float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
+  f32x4 acc[2][NV];
+#pragma unroll
+  for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+    for (int n = 0; n < NV; ++n) acc[cb][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // fold 32 keys (rows 32 hs .. 32 hs + 31 of the LDS step at buf, first key
+  // kb) into both column blocks
+  auto substep = [&](const char* buf, int kb, int hs, bool mask) {
+    f32x4 sc[2][2];
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+      for (int u = 0; u < 2; ++u) sc[cb][u] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int t = 32 * hs + 16 * u + j;
+#pragma unroll
+      for (int c = 0; c < QC; ++c) {
+        const bf16x8 kf = __builtin_bit_cast(
+            bf16x8, *reinterpret_cast<const wave::u32x4*>(
+                        buf + t * Gm::KROW + 16 * ((4 * c + g + kskew<NCH>(t)) % NCH)));
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb)
+          sc[cb][u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[cb][c], sc[cb][u], 0, 0, 0);
+      }
+    }
+    float alpha[2];
+    bf16x8 phi[2], plo[2];
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) {
+      float xs[2][4];
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          xs[u][r] = sc[cb][u][r] * a.scale_log2;
+          if (mask && kb + 16 * u + 4 * g + r > pos[cb]) xs[u][r] = -INFINITY;
+        }
+      float mx = xs[0][0];
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) mx = fmaxf(mx, xs[u][r]);
+      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      const float m_new = fmaxf(m_run[cb], mx);
+      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+      alpha[cb] = wave::fast_exp2(m_run[cb] - m_use);
+      m_run[cb] = m_new;
+      float psum = 0.f;
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float pv_ = wave::fast_exp2(xs[u][r] - m_use);
+          psum += pv_;
+          const __bf16 hb = static_cast<__bf16>(pv_);
+          phi[cb][4 * u + r] = hb;
+          plo[cb][4 * u + r] = static_cast<__bf16>(pv_ - static_cast<float>(hb));
+        }
+      l_run[cb] = l_run[cb] * alpha[cb] + psum;
+    }
+    // V rows 4g + r of each 16-key tile: dims NV*j .. NV*j + NV - 1
+    wave::Words<NW> vw[2][4];
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const char* vp = buf + Gm::KBYTES + (32 * hs + 16 * u + 4 * g + r) * Gm::VROW + 2 * NV * j;
+        if constexpr (NW == 4) {
+          const wave::u32x4 v4 = *reinterpret_cast<const wave::u32x4*>(vp);
+          vw[u][r].w[0] = v4.x; vw[u][r].w[1] = v4.y; vw[u][r].w[2] = v4.z; vw[u][r].w[3] = v4.w;
+        } else {
+          const wave::u32x2 v2 = *reinterpret_cast<const wave::u32x2*>(vp);
+          vw[u][r].w[0] = v2.x; vw[u][r].w[1] = v2.y;
+        }
+      }
+#pragma unroll
+    for (int n = 0; n < NV; ++n) {
+      const uint32_t sel = (n & 1) ? 0x07060302u : 0x05040100u;
+      wave::u32x4 va;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int e0 = 2 * e, e1 = 2 * e + 1;  // key slots (u = e/4, r = e%4)
+        va[e] = __builtin_amdgcn_perm(vw[e1 >> 2][e1 & 3].w[n >> 1], vw[e0 >> 2][e0 & 3].w[n >> 1], sel);
+      }
+      const bf16x8 vb = __builtin_bit_cast(bf16x8, va);
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb) {
+        f32x4 o = acc[cb][n] * alpha[cb];
+        o = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vb, phi[cb], o, 0, 0, 0);
+        o = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vb, plo[cb], o, 0, 0, 0);
+        acc[cb][n] = o;
+      }
+    }
+  };
+
+  if (nsteps > 0) {
+    issue(0);
+    stage(lds);
+  }
+  __syncthreads();
+  for (int q = 0; q < nsteps; ++q) {
+    const char* cur = lds + (q & 1) * Gm::BUF;
+    if (q + 1 < nsteps) issue(q + 1);
+    const int k0 = q * kPKeys;
+    // keys past every row of the wave need no work; a step reaching past
+    // the wave's first row needs the causal mask
+    const bool mask = k0 + kPKeys - 1 > wmin;
+    if (k0 <= wmax) substep(cur, k0, 0, mask);
+    if (k0 + 32 <= wmax) substep(cur, k0 + 32, 1, mask);
+    if (q + 1 < nsteps) stage(lds + ((q + 1) & 1) * Gm::BUF);
+    __syncthreads();
+  }
+  bad = __syncthreads_or(bad) || bad_seq;
+
+  // finish: normalise, stage rows [128][SROW] in LDS (no wave reads K/V any
+  // more), then store whole rows
+  float* rows = reinterpret_cast<float*>(lds);
+#pragma unroll
+  for (int cb = 0; cb < 2; ++cb) {
+    float lsum = l_run[cb] + __shfl_xor(l_run[cb], 16, 64);
+    lsum += __shfl_xor(lsum, 32, 64);
+    const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+    float* dst = rows + (wr0 + 16 * cb + j) * Gm::SROW;
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int n0 = 0; n0 < NV; n0 += 4) {
+        float4 o = make_float4(acc[cb][n0][r] * inv, acc[cb][n0 + 1][r] * inv,
+                               acc[cb][n0 + 2][r] * inv, acc[cb][n0 + 3][r] * inv);
+        if (bad) o = make_float4(NAN, NAN, NAN, NAN);
+        *reinterpret_cast<float4*>(dst + NV * (4 * g + r) + n0) = o;
+      }
+  }
+  __syncthreads();
+  constexpr int D4 = D / 4;
+  for (int e = lane; e < 32 * D4; e += 64) {
+    const int rr = wr0 + e / D4;
+    if (rr >= tile_rows) break;
+    const int d = (e % D4) * 4;
+    const float4 o = *reinterpret_cast<const float4*>(rows + rr * Gm::SROW + d);
+    const int64_t off = (static_cast<int64_t>(q0 + row0 + rr) * a.Hq + h) * D + d;
+    if (a.out_bf16) {
+      const uint32_t lo = f32_to_bf16(o.x) | (static_cast<uint32_t>(f32_to_bf16(o.y)) << 16);
+      const uint32_t hi = f32_to_bf16(o.z) | (static_cast<uint32_t>(f32_to_bf16(o.w)) << 16);
+      *reinterpret_cast<wave::u32x2*>(static_cast<uint16_t*>(a.out) + off) = wave::u32x2{lo, hi};
+    } else {
+      *reinterpret_cast<float4*>(static_cast<float*>(a.out) + off) = o;
+    }
+  }
+}
+
+// fp32: one wave per (query row, query head)
+template <int D>
+__global__ void __launch_bounds__(64) prefill_f32_kernel(PrefillArgs a) {
+  constexpr int PER = D / 64;
+  __shared__ float s_q[D];
+  __shared__ float s_p[64];
+  __shared__ int s_phys[64];
+  const int lane = threadIdx.x;
+  const int row = blockIdx.x, h = blockIdx.y;
+  // the sequence whose chunk holds this row: largest s with qstart[s] <= row
+  int lo = 0, hi = a.S;  // qstart[lo] <= row < qstart[hi] if the row is covered
+  if (a.S == 0 || row < a.qstart[0] || row >= a.qstart[a.S]) return;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) / 2;
+    if (a.qstart[mid] <= row) lo = mid; else hi = mid;
+  }
+  const int s = lo;
+  const int q0 = a.qstart[s], qlen = a.qstart[s + 1] - q0;
+  const int L = a.lens[s];
+  const int B = a.B;
+  const bool bad_seq = L < 0 || (L + B - 1) / B > a.width || qlen > L || qlen > a.max_q;
+  const int n = bad_seq ? 0 : max(0, min(L, L - qlen + (row - q0) + 1));  // keys 0 .. position
+  const int kvh = h / (a.Hq / a.Hkv);
+  const float* q = static_cast<const float*>(a.query) + (static_cast<int64_t>(row) * a.Hq + h) * D;
+  for (int d = lane; d < D; d += 64) s_q[d] = q[d];
+  __syncthreads();
+
+  const int64_t rowst = static_cast<int64_t>(a.Hkv) * D;
+  const float* kbase = static_cast<const float*>(a.kv) + static_cast<int64_t>(kvh) * D;
+  const float* vbase = kbase + static_cast<int64_t>(a.NB) * B * rowst;
+  const int32_t* trow = a.tables + static_cast<int64_t>(s) * a.width;
+  bool bad = bad_seq;
+  float m = -INFINITY, l = 0.f, acc[PER];
+#pragma unroll
+  for (int e = 0; e < PER; ++e) acc[e] = 0.f;
+  for (int t0 = 0; t0 < n; t0 += 64) {
+    const int t = t0 + lane;
+    float sc = -INFINITY;
+    int phys = -1;
+    if (t < n) {
+      phys = trow[t / B];
+      if (phys < 0 || phys >= a.NB) {
+        bad = true;
+        phys = -1;
+      } else {
+        const float4* kr = reinterpret_cast<const float4*>(kbase + (static_cast<int64_t>(phys) * B + t % B) * rowst);
+        float dot = 0.f;
+        for (int c = 0; c < D / 4; ++c) {
+          const float4 kk = kr[c];
+          dot = fmaf(kk.x, s_q[4 * c], dot);
+          dot = fmaf(kk.y, s_q[4 * c + 1], dot);
+          dot = fmaf(kk.z, s_q[4 * c + 2], dot);
+          dot = fmaf(kk.w, s_q[4 * c + 3], dot);
+        }
+        sc = dot * a.scale_log2;
+      }
+    }
+    const float m_new = fmaxf(m, wave_max(sc));
+    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+    const float alpha = __builtin_amdgcn_exp2f(m - m_use);
+    const float p = __builtin_amdgcn_exp2f(sc - m_use);
+    l = l * alpha + wave_sum(p);
+    m = m_new;
+    s_p[lane] = p;
+    s_phys[lane] = phys;
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < PER; ++e) acc[e] *= alpha;
+    const int cnt = min(64, n - t0);
+    for (int k = 0; k < cnt; ++k) {
+      const int ph = s_phys[k];
+      if (ph < 0) continue;
+      const float pk = s_p[k];
+      const float* vr = vbase + (static_cast<int64_t>(ph) * B + (t0 + k) % B) * rowst + lane * PER;
+#pragma unroll
+      for (int e = 0; e < PER; ++e) acc[e] = fmaf(pk, vr[e], acc[e]);
+    }
+    __syncthreads();
+  }
+  bad = __any(bad);
+  const float inv = l > 0.f ? 1.f / l : 0.f;
+#pragma unroll
+  for (int e = 0; e < PER; ++e) {
+    const float o = bad ? NAN : acc[e] * inv;
+    const int64_t off = (static_cast<int64_t>(row) * a.Hq + h) * D + lane * PER + e;
+    if (a.out_bf16) static_cast<uint16_t*>(a.out)[off] = f32_to_bf16(o);
+    else static_cast<float*>(a.out)[off] = o;
+  }
+}
+
+template <int D, int B>
+int launch_bf16_db(const PrefillArgs& a, hipStream_t stream) {
+  auto kern = prefill_bf16_kernel<D, B>;
+  const int lds = PGeom<D>::LDS;
+  static bool raised = false;
+  if (!raised) {
+    if (hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, lds) != hipSuccess) {
+      (void)hipGetLastError();
+      set_error("paged prefill: cannot reserve %d bytes of LDS", lds);
+      return PKV_ERR_HIP;
+    }
+    raised = true;
+  }
+  kern<<<dim3(static_cast<unsigned>(a.items_per_xcd) * kXcds), dim3(kPThreads), lds, stream>>>(a);
+  return check_launch("paged prefill (bf16)");
+}
+
+template <int D>
+int launch_bf16_d(const PrefillArgs& a, hipStream_t stream) {
+  switch (a.B) {
+    case 8: return launch_bf16_db<D, 8>(a, stream);
+    case 16: return launch_bf16_db<D, 16>(a, stream);
+    case 32: return launch_bf16_db<D, 32>(a, stream);
+    case 64: return launch_bf16_db<D, 64>(a, stream);
+  }
+  set_error("paged prefill (bf16): block_size %d is not built (8, 16, 32, 64)", a.B);
+  return PKV_ERR_UNSUPPORTED;
+}
+
+}  // namespace
+
+int launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream) {
+  if (a.total == 0) return PKV_OK;
+  if (a.D == 64) return launch_bf16_d<64>(a, stream);
+  if (a.D == 128) return launch_bf16_d<128>(a, stream);
+  set_error("paged prefill (bf16): head_size %d is not built (64, 128)", a.D);
+  return PKV_ERR_UNSUPPORTED;
+}
+
+int launch_prefill_f32(const PrefillArgs& a, hipStream_t stream) {
+  if (a.T == 0 || a.S == 0) return PKV_OK;
+  const dim3 grid(static_cast<unsigned>(a.T), static_cast<unsigned>(a.Hq));
+  if (a.D == 64) {
+    prefill_f32_kernel<64><<<grid, dim3(64), 0, stream>>>(a);
+  } else if (a.D == 128) {
+    prefill_f32_kernel<128><<<grid, dim3(64), 0, stream>>>(a);
+  } else {
+    set_error("paged prefill (fp32): head_size %d is not built (64, 128)", a.D);
+    return PKV_ERR_UNSUPPORTED;
+  }
+  return check_launch("paged prefill (fp32)");
+}
+
+}  // namespace pkv

@@ -36,10 +36,13 @@ def test_binding_refuses_to_work_without_the_library(tmp_path, monkeypatch):
     import importlib
     import paged_kv_cache_81_amd._lib as L
     monkeypatch.setenv("PKV_LIBRARY", str(tmp_path / "missing.so"))
-    with pytest.raises(ImportError):
+    try:
+        importlib.reload(L)  # importing works (the build script needs that) ...
+        with pytest.raises(ImportError):
+            L.lib.pkv_last_error()  # ... but the first call refuses
+    finally:
+        monkeypatch.delenv("PKV_LIBRARY")
         importlib.reload(L)
-    monkeypatch.delenv("PKV_LIBRARY")
-    importlib.reload(L)
 
 
 @pytest.fixture

@@ -355,6 +355,82 @@ def custom(seed: int, lens: Sequence[int], *, dtype: str = "bf16", num_q_heads: 
                         partition_size=partition_size, scale=scale)
 
 
+# --------------------------------------------------------------------------
+# prefill (chunked) workloads
+
+@dataclass
+class PrefillWorkload:
+    """Inputs of one prefill step: each sequence's chunk of ``chunk_lens[s]``
+    query tokens ends its ``cache.context_lens[s]`` tokens, all of whose K/V
+    (the cached prefix and the chunk's own) is written before attention.
+    ``cache`` describes the pool, the tables and those K/V rows (its decode
+    query is unused); ``query`` holds the chunks' rows, sequence ``s`` at
+    ``query_start[s] .. query_start[s+1]-1``."""
+
+    name: str
+    cache: Workload
+    chunk_lens: np.ndarray    # int32 [S]
+    query_start: np.ndarray   # int32 [S + 1]
+    query: np.ndarray         # [T, Hq, D]
+
+    @property
+    def num_tokens(self) -> int:
+        return int(self.query_start[-1])
+
+    @property
+    def max_query_len(self) -> int:
+        return int(self.chunk_lens.max()) if self.chunk_lens.size else 0
+
+    def flops(self) -> int:
+        """4 D flops per (query row, head, key it attends): q.k and p.v."""
+        L = self.cache.context_lens.astype(np.int64)
+        c = self.chunk_lens.astype(np.int64)
+        keys = (c * L - c * (c - 1) // 2).sum()  # row i of a chunk attends L - c + i + 1 keys
+        return int(4 * self.cache.head_size * self.cache.num_q_heads * keys)
+
+
+def prefill(seed: int, cached_lens: Sequence[int], chunk_lens: Sequence[int], *,
+            dtype: str = "bf16", num_q_heads: int = 8, num_kv_heads: int = 2,
+            head_size: int = 128, block_size: int = 16, name: str = "prefill",
+            **kw) -> PrefillWorkload:
+    """Chunks of ``chunk_lens`` tokens after ``cached_lens`` cached tokens
+    (0: a whole prompt).  Draw order: the cache workload's, then the query."""
+    cached = np.asarray(cached_lens, dtype=np.int64)
+    chunks = np.asarray(chunk_lens, dtype=np.int64)
+    rng = np.random.Generator(np.random.PCG64(seed))
+    cache = _independent(name, rng, cached + chunks, dtype=dtype, num_q_heads=num_q_heads,
+                         num_kv_heads=num_kv_heads, head_size=head_size,
+                         block_size=block_size, **kw)
+    starts = np.concatenate([[0], np.cumsum(chunks)]).astype(np.int32)
+    query = _normal(rng, (int(starts[-1]), num_q_heads, head_size), dtype)
+    return PrefillWorkload(name=name, cache=cache, chunk_lens=chunks.astype(np.int32),
+                           query_start=starts, query=query)
+
+
+def prefill_opt13b(seed: int = 81011, num_seqs: int = 16, chunk: int = 512,
+                   max_cached: int = 1536) -> PrefillWorkload:
+    """OPT-13B-shaped layer (40/40 heads, D 128, B 16, bf16): chunks of 512
+    prompt tokens after 0 .. 1536 cached tokens (earlier chunks or prefix hits)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    cached = rng.integers(0, max_cached + 1, size=num_seqs)
+    return prefill(seed + 1, cached, np.full(num_seqs, chunk), num_q_heads=40, num_kv_heads=40,
+                   head_size=128, block_size=16, name="prefill_opt13b")
+
+
+def prefill_qwen2(seed: int = 81012, num_seqs: int = 32, max_chunk: int = 1024,
+                  max_cached: int = 1024, block_size: int = 16) -> PrefillWorkload:
+    """Qwen2-0.5B-shaped layer (14/2 heads, D 64, bf16): whole prompts and
+    continuing chunks of 64 .. 1024 tokens after 0 .. 1024 cached tokens."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    chunks = rng.integers(64, max_chunk + 1, size=num_seqs)
+    cached = np.where(rng.random(num_seqs) < 0.5, 0, rng.integers(0, max_cached + 1, size=num_seqs))
+    return prefill(seed + 1, cached, chunks, num_q_heads=14, num_kv_heads=2, head_size=64,
+                   block_size=block_size, name="prefill_qwen2")
+
+
+PREFILL = {"prefill_opt13b": prefill_opt13b, "prefill_qwen2": prefill_qwen2}
+
+
 NAMED = {
     "tiny": tiny,
     "opt13b_mha": opt13b_mha,
