@@ -40,7 +40,7 @@ DEFAULT_WORKLOAD = "opt13b_mha"
 # is a model's layer shape (OPT-13B 40, Qwen2-0.5B 24), else enough pools to
 # hold several times the 256 MB memory-side cache
 DEFAULT_LAYERS = {"opt13b_mha": 40, "qwen2_gqa": 24, "shared_prefix": 8, "long_context": 4,
-                  "tiny": 1}
+                  "tiny": 1, "prefill_opt13b": 40, "prefill_qwen2": 24}
 # the sources that decide what the attention launch does (the counter
 # summary in profiles/ holds for this set only)
 KERNEL_SOURCES = ["paged_kv_cache_81_amd/csrc/api.hip",
@@ -49,15 +49,20 @@ KERNEL_SOURCES = ["paged_kv_cache_81_amd/csrc/api.hip",
                   "paged_kv_cache_81_amd/csrc/attention_bf16_wave.hpp",
                   "paged_kv_cache_81_amd/csrc/attention_f32.hip",
                   "paged_kv_cache_81_amd/csrc/common.hpp"]
+# ... and the prefill launch
+PREFILL_SOURCES = ["paged_kv_cache_81_amd/csrc/api.hip",
+                   "paged_kv_cache_81_amd/csrc/prefill.hip",
+                   "paged_kv_cache_81_amd/csrc/attention_bf16_wave.hpp",
+                   "paged_kv_cache_81_amd/csrc/common.hpp"]
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def kernel_source_sha() -> str:
+def kernel_source_sha(sources=None) -> str:
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
+    for p in sources or KERNEL_SOURCES:
         with open(os.path.join(ROOT, p), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -249,6 +254,193 @@ def block_ops(w, dev, reps: int = 10) -> dict:
     return out
 
 
+PREFILL_METRIC = "paged prefill attn TFLOP/s (% of MI355X bf16 MFMA dense peak)"
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak, AMD's published figure
+
+
+def prefill_cpu_baseline(pw, seconds: float) -> dict:
+    """The CPU oracle, one thread, on a bounded sample of the prefill rows:
+    each row is float64 attention over its sequence's keys up to its position."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    import oracle
+    from tests import gpu_harness as H
+
+    w = pw.cache
+    with threadpool_limits(limits=1):
+        pool = H.nan_pool_numpy(w)
+        oracle.write_ref(pool, w.cached_k, w.cached_v,
+                         oracle.slot_mapping_ref(w.block_tables, w.cached_seq, w.cached_pos,
+                                                 w.block_size))
+        oracle.write_ref(pool, w.new_k, w.new_v,
+                         oracle.slot_mapping_ref(w.block_tables, np.arange(w.num_seqs), w.new_pos,
+                                                 w.block_size))
+        rng = np.random.default_rng(0)
+        flops, n = 0, 0
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < seconds:
+            r = int(rng.integers(0, pw.num_tokens))
+            s = int(np.searchsorted(pw.query_start, r, side="right") - 1)
+            L = int(w.context_lens[s])
+            p = int(oracle.chunk_positions(L, int(pw.chunk_lens[s]))[r - pw.query_start[s]])
+            k, v = oracle.gather_ref(pool, w.block_tables[s], p + 1)
+            oracle.attention_ref(oracle.to_f64(pw.query[r], w.dtype), oracle.to_f64(k, w.dtype),
+                                 oracle.to_f64(v, w.dtype), w.scale)
+            flops += 4 * w.head_size * w.num_q_heads * (p + 1)
+            n += 1
+        dt = time.perf_counter() - t0
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
+            "sample": f"{n} random query rows of {pw.name} (all heads), float64 numpy, one "
+                      f"thread, {dt:.1f} s"}
+
+
+def prefill_bench(args, dev) -> dict:
+    """One step = slot mapping and write of the chunks' K/V, then prefill
+    attention, cycling through layer pools; K steps in one graph."""
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_81_amd._lib as lib_mod
+    import workloads
+    from paged_kv_cache_81_amd._lib import check, lib
+    from tests import gpu_harness as H
+
+    pw = workloads.PREFILL[args.workload]()
+    w = pw.cache
+    S, B, NB = w.num_seqs, w.block_size, w.num_blocks
+    Hq, Hkv, D = w.num_q_heads, w.num_kv_heads, w.head_size
+    T = pw.num_tokens
+    log(f"[bench] workload {pw.name}: S={S} T={T} Hq={Hq} Hkv={Hkv} D={D} B={B} NB={NB} "
+        f"sumL={int(w.context_lens.sum())} flops={pw.flops() / 1e9:.1f} G")
+    st = H.upload(w, device=dev)
+    # the chunks' K/V rows and positions (the last chunk_len tokens of each sequence)
+    ks, vs, seqs, poss = [], [], [], []
+    for si in range(S):
+        k, v = w.logical_kv(si)
+        c = int(pw.chunk_lens[si])
+        L = int(w.context_lens[si])
+        ks.append(k[L - c:])
+        vs.append(v[L - c:])
+        seqs.append(np.full(c, si, dtype=np.int32))
+        poss.append(np.arange(L - c, L, dtype=np.int32))
+    ck = H.to_torch(np.concatenate(ks), w.dtype, dev)
+    cv = H.to_torch(np.concatenate(vs), w.dtype, dev)
+    cseq = torch.from_numpy(np.concatenate(seqs)).to(dev)
+    cpos = torch.from_numpy(np.concatenate(poss)).to(dev)
+    cslots = torch.empty(T, dtype=torch.int64, device=dev)
+    q = H.to_torch(pw.query, w.dtype, dev)
+    qs = torch.from_numpy(pw.query_start).to(dev)
+    out = torch.empty((T, Hq, D), dtype=torch.float32, device=dev)
+    dt = lib_mod.PKV_BF16 if w.dtype == "bf16" else lib_mod.PKV_F32
+    nl = args.layers if args.layers is not None else DEFAULT_LAYERS.get(pw.name, 4)
+    free, _ = torch.cuda.mem_get_info(dev)
+    nl = max(1, min(nl, int(0.5 * free // st.kv.numel() // st.kv.element_size())))
+    pools = [st.kv] + [st.kv.clone() for _ in range(nl - 1)]
+    torch.cuda.synchronize()
+
+    def calls(sh, layer):
+        kv = pools[layer]
+        return {
+            "slot_mapping": lambda: check(lib.paged_kv_slot_mapping(
+                cslots.data_ptr(), st.tables.data_ptr(), w.table_width, cseq.data_ptr(),
+                cpos.data_ptr(), T, S, B, NB, sh), "slot mapping"),
+            "kv_write": lambda: check(lib.paged_kv_write(
+                ck.data_ptr(), cv.data_ptr(), kv.data_ptr(), cslots.data_ptr(), T, NB, B, Hkv, D,
+                dt, sh), "kv write"),
+            "prefill": lambda: check(lib.paged_attention_prefill(
+                out.data_ptr(), 0, q.data_ptr(), qs.data_ptr(), T, pw.max_query_len,
+                kv.data_ptr(), st.tables.data_ptr(), w.table_width, st.lens.data_ptr(), S, Hq,
+                Hkv, D, B, NB, w.scale, dt, sh), "prefill"),
+        }
+
+    cur = torch.cuda.current_stream(dev)
+    eager = [calls(cur.cuda_stream, layer) for layer in range(nl)]
+    for f in eager[0].values():
+        f()
+    torch.cuda.synchronize()
+    ref_out = out.clone()
+    for i in range(args.warmup):
+        for f in eager[i % nl].values():
+            f()
+    graph = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream(device=dev)
+    cap.wait_stream(cur)
+    with torch.cuda.stream(cap):
+        captured = [calls(cap.cuda_stream, layer) for layer in range(nl)]
+        for f in captured[0].values():
+            f()
+        cap.synchronize()
+        with torch.cuda.graph(graph, stream=cap):
+            for i in range(args.steps):
+                for f in captured[i % nl].values():
+                    f()
+    cur.wait_stream(cap)
+    torch.cuda.synchronize()
+    graph.replay()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(cur)
+    graph.replay()
+    t1.record(cur)
+    torch.cuda.synchronize()
+    ms_per_step = t0.elapsed_time(t1) / args.steps
+    log(f"[bench] {args.steps} steps: {ms_per_step * 1e3:.1f} us/step")
+    for f in eager[(args.steps - 1) % nl].values():
+        f()
+    torch.cuda.synchronize()
+    if not torch.equal(out, ref_out):
+        raise SystemExit("[bench] the timed steps' output differs from the first eager step's")
+    reps = max(10, min(args.steps, 50))
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(reps)]
+    for r, (a, b) in enumerate(ev):
+        a.record(cur)
+        eager[r % nl]["prefill"]()
+        b.record(cur)
+    torch.cuda.synchronize()
+    kernel_us = float(np.mean([a.elapsed_time(b) for a, b in ev])) * 1e3
+    flops = pw.flops()
+    tflops = flops / (kernel_us * 1e-6) / 1e12
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    log(f"[bench] prefill kernel {kernel_us:.1f} us = {tflops:.1f} TFLOP/s")
+    return {
+        "metric": PREFILL_METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "us_per_step": round(ms_per_step * 1e3, 2),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "accumulate": "f32",
+        "data": "synthetic (seeded N(0,1) K/V/q, shuffled block pool)",
+        "config": {
+            "workload": pw.name, "num_seqs": S, "num_tokens": T, "num_q_heads": Hq,
+            "num_kv_heads": Hkv, "head_size": D, "block_size": B, "num_blocks": NB,
+            "sum_context_len": int(w.context_lens.sum()), "max_query_len": pw.max_query_len,
+            "flops": flops, "graph": True, "layers_cycled": nl,
+        },
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(tflops, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+            "traffic": None,
+            "kernel": f"prefill_bf16_kernel<{D},{B}>" if w.dtype == "bf16" else f"prefill_f32_kernel<{D}>",
+            "kernel_us": round(kernel_us, 2),
+            "algorithmic_flops": flops,
+        },
+        "kernel_source_sha": kernel_source_sha(PREFILL_SOURCES),
+    }
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -304,6 +496,15 @@ def main() -> int:
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes_read": 1 << 30, "copy_bytes_written": 1 << 30, "launches": 5}))
+        return 0
+
+    if args.workload in workloads.PREFILL:
+        result = prefill_bench(args, dev)
+        if not args.no_cpu_baseline:
+            log("[bench] timing the CPU oracle")
+            result["cpu_baseline"] = prefill_cpu_baseline(workloads.PREFILL[args.workload](),
+                                                          args.cpu_seconds)
+        print(json.dumps(result), flush=True)
         return 0
 
     t = time.time()

@@ -47,6 +47,21 @@ struct PGeom {
   static constexpr int LDS = 2 * BUF > kPRows * SROW * 4 ? 2 * BUF : kPRows * SROW * 4;
 };
 
+// max(v[l], v[l ^ 16]) and max(v[l], v[l ^ 32]) without LDS: the permlane
+// swaps exchange the two halves of each 32-lane (resp. the 64-lane) group
+// between their two operands, so swapping v with itself leaves one half's
+// values in the first result and the other half's in the second.
+__device__ __forceinline__ float max_xor16(float v) {
+  const uint32_t b = __float_as_uint(v);
+  const auto r = __builtin_amdgcn_permlane16_swap(b, b, false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_xor32(float v) {
+  const uint32_t b = __float_as_uint(v);
+  const auto r = __builtin_amdgcn_permlane32_swap(b, b, false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 // chunk ch of K row t sits at chunk position (ch + kskew(t)) mod NCH, so both
 // the row-wise stores and the MFMA-layout reads (16 rows, one chunk each)
 // spread over the banks
@@ -88,7 +103,7 @@ prefill_bf16_kernel(PrefillArgs a) {
   // this wave's rows: column j of block cb is tile row 32 wv + 16 cb + j
   const int wr0 = 32 * wv;
   const int wave_rows = max(0, min(32, tile_rows - wr0));
-  const int wmin = P0 + wr0;                   // position of its first row
+  const int wmin = P0 + wr0;  // position of the wave's first row
   const int wmax = wave_rows > 0 ? P0 + wr0 + wave_rows - 1 : -1;  // ... and of its last
   int pos[2];
   bf16x8 qf[2][QC];
@@ -109,35 +124,51 @@ prefill_bf16_kernel(PrefillArgs a) {
   const int32_t* trow = a.tables + static_cast<int64_t>(s) * a.width;
   bool bad = false;
 
-  // global -> registers (step q) and registers -> LDS: thread chunk
-  // e = tid + 256 i is row e / NCH, chunk e % NCH of the step's K and V;
-  // rows at or past kend are zeros (the K/V there may be unwritten)
+  // global -> registers (step q) and registers -> LDS.  Thread chunk
+  // e = tid + 256 i is row t0 + i * RSTEP of the step, 16-byte chunk ch; B
+  // divides the 64-key step, so the row's offset inside its block is fixed
+  // per thread.  The table entries a step's loads need are read one step
+  // earlier, so the K/V loads never wait for them.  Rows at or past kend
+  // read block 0 (always in the pool) and are zeroed in LDS instead (their
+  // K/V may be unwritten); an out-of-range table entry is clamped into the
+  // pool and poisons the result.
+  constexpr int RSTEP = kPThreads / NCH;
+  const int t0 = tid / NCH, ch = tid % NCH;
+  const char* kbytes = reinterpret_cast<const char*>(kbase);
+  const int64_t vdelta = reinterpret_cast<const char*>(vbase) - kbytes;
+  const int64_t blockbytes = static_cast<int64_t>(B) * rowst * 2;
   wave::u32x4 pk[CPT], pv[CPT];
-  auto issue = [&](int q) {
+  int tab[CPT];
+  auto load_table = [&](int q) {
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
-      const int e = tid + kPThreads * i;
-      const int key = q * kPKeys + e / NCH;
-      wave::u32x4 kz{0u, 0u, 0u, 0u}, vz{0u, 0u, 0u, 0u};
-      if (key < kend) {
-        const int phys = trow[key / B];
-        if (phys >= 0 && phys < a.NB) {
-          const int64_t off = (static_cast<int64_t>(phys) * B + key % B) * rowst + 8 * (e % NCH);
-          kz = *reinterpret_cast<const wave::u32x4*>(kbase + off);
-          vz = *reinterpret_cast<const wave::u32x4*>(vbase + off);
-        } else {
-          bad = true;
-        }
-      }
-      pk[i] = kz;
-      pv[i] = vz;
+      const int key = q * kPKeys + t0 + RSTEP * i;
+      tab[i] = key < kend ? trow[key / B] : 0;
     }
   };
-  auto stage = [&](char* buf) {
+  auto issue = [&]() {
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
-      const int e = tid + kPThreads * i;
-      const int t = e / NCH, ch = e % NCH;
+      const uint32_t phys = min(static_cast<uint32_t>(tab[i]), static_cast<uint32_t>(a.NB - 1));
+      bad = bad || phys != static_cast<uint32_t>(tab[i]);
+      const uint32_t inoff = (((t0 + RSTEP * i) % B) * static_cast<uint32_t>(rowst) + 8 * ch) * 2;
+      const char* kp = kbytes + (static_cast<int64_t>(phys) * blockbytes + inoff);
+      pk[i] = *reinterpret_cast<const wave::u32x4*>(kp);
+      pv[i] = *reinterpret_cast<const wave::u32x4*>(kp + vdelta);
+    }
+  };
+  auto stage = [&](char* buf, int valid_rows) {
+    if (valid_rows < kPKeys) {  // the sequence's keys end inside this step
+#pragma unroll
+      for (int i = 0; i < CPT; ++i)
+        if (t0 + RSTEP * i >= valid_rows) {
+          pk[i] = wave::u32x4{0u, 0u, 0u, 0u};
+          pv[i] = wave::u32x4{0u, 0u, 0u, 0u};
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int t = t0 + RSTEP * i;
       *reinterpret_cast<wave::u32x4*>(buf + t * Gm::KROW + 16 * ((ch + kskew<NCH>(t)) % NCH)) = pk[i];
       *reinterpret_cast<wave::u32x4*>(buf + Gm::KBYTES + t * Gm::VROW + 16 * ch) = pv[i];
     }
@@ -151,8 +182,10 @@ prefill_bf16_kernel(PrefillArgs a) {
     for (int n = 0; n < NV; ++n) acc[cb][n] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // fold 32 keys (rows 32 hs .. 32 hs + 31 of the LDS step at buf, first key
-  // kb) into both column blocks
-  auto substep = [&](const char* buf, int kb, int hs, bool mask) {
+  // kb) into both column blocks.  The causal mask is applied on every step:
+  // a second, unmasked copy of this code costs more in registers (spills)
+  // than the compare and select it saves.
+  auto substep = [&](const char* buf, int kb, int hs) {
     f32x4 sc[2][2];
 #pragma unroll
     for (int cb = 0; cb < 2; ++cb)
@@ -171,6 +204,10 @@ prefill_bf16_kernel(PrefillArgs a) {
           sc[cb][u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[cb][c], sc[cb][u], 0, 0, 0);
       }
     }
+    // online softmax per row in the log2 domain: the running max m_run is
+    // in scaled units, the raw scores are scaled inside the exponent
+    // (scale > 0 keeps their order)
+    const float sl2 = a.scale_log2;
     float alpha[2];
     bf16x8 phi[2], plo[2];
 #pragma unroll
@@ -179,18 +216,23 @@ prefill_bf16_kernel(PrefillArgs a) {
 #pragma unroll
       for (int u = 0; u < 2; ++u)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          xs[u][r] = sc[cb][u][r] * a.scale_log2;
-          if (mask && kb + 16 * u + 4 * g + r > pos[cb]) xs[u][r] = -INFINITY;
-        }
+        for (int r = 0; r < 4; ++r) xs[u][r] = sc[cb][u][r];
+      if (kb + 31 > wmin) {  // some key may be past some row of the wave
+        int k = kb + 4 * g;
+        asm volatile("" : "+v"(k));  // keep the compares inside the branch
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (k + 16 * u + r > pos[cb]) xs[u][r] = -INFINITY;
+      }
       float mx = xs[0][0];
 #pragma unroll
       for (int u = 0; u < 2; ++u)
 #pragma unroll
         for (int r = 0; r < 4; ++r) mx = fmaxf(mx, xs[u][r]);
-      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const float m_new = fmaxf(m_run[cb], mx);
+      mx = max_xor32(max_xor16(mx));
+      const float m_new = fmaxf(m_run[cb], mx * sl2);
       const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
       alpha[cb] = wave::fast_exp2(m_run[cb] - m_use);
       m_run[cb] = m_new;
@@ -198,14 +240,30 @@ prefill_bf16_kernel(PrefillArgs a) {
 #pragma unroll
       for (int u = 0; u < 2; ++u)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float pv_ = wave::fast_exp2(xs[u][r] - m_use);
-          psum += pv_;
-          const __bf16 hb = static_cast<__bf16>(pv_);
-          phi[cb][4 * u + r] = hb;
-          plo[cb][4 * u + r] = static_cast<__bf16>(pv_ - static_cast<float>(hb));
+        for (int r = 0; r < 4; r += 2) {
+          const float p0 = wave::fast_exp2(fmaf(xs[u][r], sl2, -m_use));
+          const float p1 = wave::fast_exp2(fmaf(xs[u][r + 1], sl2, -m_use));
+          psum += p0 + p1;
+          // P = hi + lo, both bf16 (pairs converted together)
+          const bf16x2 h = __builtin_convertvector(f32x2{p0, p1}, bf16x2);
+          const uint32_t hw = __builtin_bit_cast(uint32_t, h);
+          const bf16x2 l = __builtin_convertvector(
+              f32x2{p0 - __uint_as_float(hw << 16), p1 - __uint_as_float(hw & 0xFFFF0000u)}, bf16x2);
+          phi[cb][4 * u + r] = h.x;
+          phi[cb][4 * u + r + 1] = h.y;
+          plo[cb][4 * u + r] = l.x;
+          plo[cb][4 * u + r + 1] = l.y;
         }
       l_run[cb] = l_run[cb] * alpha[cb] + psum;
+    }
+    // the accumulators need rescaling only when some row's max moved
+    if (__any(alpha[0] != 1.f || alpha[1] != 1.f)) {
+      float al[2] = {alpha[0], alpha[1]};
+      asm volatile("" : "+v"(al[0]), "+v"(al[1]));  // keep the multiplies inside the branch
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+        for (int n = 0; n < NV; ++n) acc[cb][n] *= al[cb];
     }
     // V rows 4g + r of each 16-key tile: dims NV*j .. NV*j + NV - 1
     wave::Words<NW> vw[2][4];
@@ -234,8 +292,7 @@ prefill_bf16_kernel(PrefillArgs a) {
       const bf16x8 vb = __builtin_bit_cast(bf16x8, va);
 #pragma unroll
       for (int cb = 0; cb < 2; ++cb) {
-        f32x4 o = acc[cb][n] * alpha[cb];
-        o = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vb, phi[cb], o, 0, 0, 0);
+        f32x4 o = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vb, phi[cb], acc[cb][n], 0, 0, 0);
         o = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vb, plo[cb], o, 0, 0, 0);
         acc[cb][n] = o;
       }
@@ -243,20 +300,22 @@ prefill_bf16_kernel(PrefillArgs a) {
   };
 
   if (nsteps > 0) {
-    issue(0);
-    stage(lds);
+    load_table(0);
+    issue();
+    if (nsteps > 1) load_table(1);
+    stage(lds, kend);
   }
   __syncthreads();
   for (int q = 0; q < nsteps; ++q) {
     const char* cur = lds + (q & 1) * Gm::BUF;
-    if (q + 1 < nsteps) issue(q + 1);
+    if (q + 1 < nsteps) issue();
+    if (q + 2 < nsteps) load_table(q + 2);
     const int k0 = q * kPKeys;
     // keys past every row of the wave need no work; a step reaching past
     // the wave's first row needs the causal mask
-    const bool mask = k0 + kPKeys - 1 > wmin;
-    if (k0 <= wmax) substep(cur, k0, 0, mask);
-    if (k0 + 32 <= wmax) substep(cur, k0 + 32, 1, mask);
-    if (q + 1 < nsteps) stage(lds + ((q + 1) & 1) * Gm::BUF);
+    if (k0 <= wmax) substep(cur, k0, 0);
+    if (k0 + 32 <= wmax) substep(cur, k0 + 32, 1);
+    if (q + 1 < nsteps) stage(lds + ((q + 1) & 1) * Gm::BUF, kend - (q + 1) * kPKeys);
     __syncthreads();
   }
   bad = __syncthreads_or(bad) || bad_seq;
