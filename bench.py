@@ -306,7 +306,7 @@ def prefill_bench(args, dev) -> dict:
     from paged_kv_cache_81_amd._lib import check, lib
     from tests import gpu_harness as H
 
-    pw = workloads.PREFILL[args.workload]()
+    pw = workloads.PREFILL[args.workload](**_block_kw(args))
     w = pw.cache
     S, B, NB = w.num_seqs, w.block_size, w.num_blocks
     Hq, Hkv, D = w.num_q_heads, w.num_kv_heads, w.head_size
@@ -441,6 +441,10 @@ def prefill_bench(args, dev) -> dict:
     }
 
 
+def _block_kw(args) -> dict:
+    return {"block_size": args.block_size} if args.block_size else {}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -448,6 +452,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--partition-size", type=int, default=None)
+    ap.add_argument("--block-size", type=int, default=None,
+                    help="tokens per block (default: the workload's own, 16 or 32)")
     ap.add_argument("--layers", type=int, default=None, help="layer cache pools to cycle through")
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying a graph")
     ap.add_argument("--flush", action="store_true",
@@ -502,13 +508,13 @@ def main() -> int:
         result = prefill_bench(args, dev)
         if not args.no_cpu_baseline:
             log("[bench] timing the CPU oracle")
-            result["cpu_baseline"] = prefill_cpu_baseline(workloads.PREFILL[args.workload](),
-                                                          args.cpu_seconds)
+            result["cpu_baseline"] = prefill_cpu_baseline(
+                workloads.PREFILL[args.workload](**_block_kw(args)), args.cpu_seconds)
         print(json.dumps(result), flush=True)
         return 0
 
     t = time.time()
-    w = workloads.make(args.workload)
+    w = workloads.make(args.workload, **_block_kw(args))
     log(f"[bench] workload {w.name}: S={w.num_seqs} Hq={w.num_q_heads} Hkv={w.num_kv_heads} "
         f"D={w.head_size} B={w.block_size} NB={w.num_blocks} sumL={int(w.context_lens.sum())} "
         f"(generated in {time.time() - t:.1f} s)")
@@ -663,6 +669,10 @@ def main() -> int:
             "head_size": D, "block_size": B, "num_blocks": NB,
             "sum_context_len": int(w.context_lens.sum()), "max_context_len": w.max_context_len,
             "kv_read_bytes": kvb, "kv_unique_bytes": ukvb, "partition_size": P,
+            "reserved_slot_waste": round(float(
+                (np.ceil(w.context_lens / B) * B - w.context_lens).sum() /
+                max(1, int(w.context_lens.sum()))), 5),
+            "table_bytes": int(np.ceil(w.context_lens / B).sum()) * 4,
             "graph": not args.no_graph,
             "layers_cycled": nl, "kv_flags": "cached (shared blocks)" if shared else "streamed",
         },

@@ -194,7 +194,7 @@ size_t paged_attention_workspace_bytes(int num_seqs, int num_q_heads, int num_kv
  *   flags         0 or PKV_ATTN_CACHED_KV
  *   workspace     device scratch of at least paged_attention_workspace_bytes()
  *                 bytes (may be NULL when that is 0), 256-byte aligned
- * Supported: head_size 64 or 128; block_size 16, 32 or 64 (PKV_BF16) and any
+ * Supported: head_size 64 or 128; block_size 8, 16, 32 or 64 (PKV_BF16) and any
  * block_size from 1 to 256 (PKV_F32); num_q_heads a multiple of num_kv_heads.
  */
 int paged_attention_decode(void* out, pkv_dtype out_dtype, const void* query,

@@ -396,8 +396,9 @@ int decode_impl(int phases, void* out, pkv_dtype out_dtype, const void* query,
     set_error("head_size %d is not built (64 or 128)", head_size);
     return PKV_ERR_UNSUPPORTED;
   }
-  if (dtype == PKV_BF16 && block_size != 16 && block_size != 32 && block_size != 64) {
-    set_error("bf16 path: block_size %d is not built (16, 32 or 64)", block_size);
+  if (dtype == PKV_BF16 && block_size != 8 && block_size != 16 && block_size != 32 &&
+      block_size != 64) {
+    set_error("bf16 path: block_size %d is not built (8, 16, 32 or 64)", block_size);
     return PKV_ERR_UNSUPPORTED;
   }
   if (dtype == PKV_F32 && block_size > 256) {

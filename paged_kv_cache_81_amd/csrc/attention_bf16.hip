@@ -300,9 +300,11 @@ int launch_attention_bf16(const AttnArgs& a, hipStream_t stream) {
   if (a.S == 0) return PKV_OK;
   if (a.stream) return launch_attention_bf16_stream(a, stream);
   switch (a.D * 1000 + a.B) {
+    case 64008: return launch<64, 8>(a, stream);
     case 64016: return launch<64, 16>(a, stream);
     case 64032: return launch<64, 32>(a, stream);
     case 64064: return launch<64, 64>(a, stream);
+    case 128008: return launch<128, 8>(a, stream);
     case 128016: return launch<128, 16>(a, stream);
     case 128032: return launch<128, 32>(a, stream);
     case 128064: return launch<128, 64>(a, stream);

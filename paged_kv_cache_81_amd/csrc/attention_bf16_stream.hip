@@ -224,9 +224,11 @@ int launch_attention_bf16_stream(const AttnArgs& a, hipStream_t stream) {
     return PKV_ERR_UNSUPPORTED;
   }
   switch (a.D * 1000 + a.B) {
+    case 64008: return launch_stream<64, 8>(a, stream);
     case 64016: return launch_stream<64, 16>(a, stream);
     case 64032: return launch_stream<64, 32>(a, stream);
     case 64064: return launch_stream<64, 64>(a, stream);
+    case 128008: return launch_stream<128, 8>(a, stream);
     case 128016: return launch_stream<128, 16>(a, stream);
     case 128032: return launch_stream<128, 32>(a, stream);
     case 128064: return launch_stream<128, 64>(a, stream);

@@ -84,6 +84,11 @@ struct Wave {
   static constexpr int NW = NV / 2;  // 32-bit words per lane per V token
   static constexpr int NCH = D / 8;  // 16-byte chunks per K row
   static constexpr int SROW = D + 4;  // LDS floats per finished head row (padded)
+  // block-table entries per 32-token step: one per 16-token tile, or one
+  // per block when blocks are smaller than a tile (B = 8: a tile spans two)
+  static constexpr int EPS = B < 16 ? 32 / B : 2;
+  static constexpr int WIN = 64 / EPS;  // steps one table window covers
+  static_assert(B >= 8 && 64 % EPS == 0, "unsupported block size");
 
   // K arrives either row-wise like V and is rearranged through LDS (KL), or
   // straight in MFMA layout (token j, dims 32c + 8g: 16 rows of 64 bytes per
@@ -110,7 +115,7 @@ struct Wave {
   const char* vbase;
   const int32_t* trow;
   int t_begin, t_end;
-  int win, win_q0;  // block-table window of steps [win_q0, win_q0 + 32) (see load_window)
+  int win, win_q0;  // block-table window of steps [win_q0, win_q0 + WIN) (see load_window)
   int win_next;     // ... and of the 32 steps after it
   bf16x8 qf[QC];
 
@@ -131,8 +136,8 @@ struct Wave {
     // instruction covers 4 rows of D*2 contiguous bytes (lane (j, g): row
     // 4g + r, bytes 2*NV*j ..).
 #pragma unroll
-    for (int r = 0; r < 4; ++r) voff[r] = ((4 * g + r) * static_cast<uint32_t>(row) + NV * j) * 2u;
-    koff = (j * static_cast<uint32_t>(row) + 8 * g) * 2u;
+    for (int r = 0; r < 4; ++r) voff[r] = ((4 * g + r) % B * static_cast<uint32_t>(row) + NV * j) * 2u;
+    koff = (j % B * static_cast<uint32_t>(row) + 8 * g) * 2u;
     reset();
   }
 
@@ -144,11 +149,11 @@ struct Wave {
     bad_blk = false;
   }
 
-  // Block-table window: lane l holds the physical block of tile (l & 1) of
-  // step q0 + (l >> 1), so 32 steps need one load; per step the entries are
-  // read back as scalars.
+  // Block-table window: lane l holds the physical block of piece l % EPS
+  // (a 16-token tile, or a block of 8 tokens) of step q0 + l / EPS, so WIN
+  // steps need one load; per step the entries are read back as scalars.
   __device__ __forceinline__ int load_window(int q0) const {
-    const int tt = t_begin + (q0 + (lane >> 1)) * kStep + 16 * (lane & 1);
+    const int tt = t_begin + (q0 + lane / EPS) * kStep + (kStep / EPS) * (lane % EPS);
     return tt < t_end ? trow[tt / B] : -1;
   }
 
@@ -170,7 +175,7 @@ struct Wave {
     win_q0 = 0;
     win = load_window(0);
     asm volatile("" ::"v"(win));
-    win_next = load_window(32);
+    win_next = load_window(WIN);
   }
 
   // Issue the loads of step q (tokens t_begin + 32q ..), steps in order.
@@ -183,32 +188,61 @@ struct Wave {
   // is requested (ahead of this step's K/V, so waiting for it later costs
   // nothing extra).
   __device__ __forceinline__ void issue(Step& d, int q) {
-    if (q - win_q0 >= 32) {
+    if (q - win_q0 >= WIN) {
       win = win_next;
-      win_q0 += 32;
-      win_next = load_window(win_q0 + 32);
+      win_q0 += WIN;
+      win_next = load_window(win_q0 + WIN);
     }
     const int ts = t_begin + q * kStep;
     d.bad = false;
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const int tt = ts + 16 * u;
-      const int phys = __builtin_amdgcn_readlane(win, 2 * (q - win_q0) + u);
-      const bool in_range = phys >= 0 && phys < NB;
-      d.bad = d.bad || (tt < t_end && !in_range);
-      const int blk = (tt < t_end && in_range) ? phys : 0;
-      const int64_t base = ((static_cast<int64_t>(blk) * B + (tt % B)) * row) * 2;
-      const char* kp = kbase + base;
-      const char* vp = vbase + base;
-      if constexpr (KL) {
+      if constexpr (B >= 16) {
+        const int phys = __builtin_amdgcn_readlane(win, 2 * (q - win_q0) + u);
+        const bool in_range = phys >= 0 && phys < NB;
+        d.bad = d.bad || (tt < t_end && !in_range);
+        const int blk = (tt < t_end && in_range) ? phys : 0;
+        const int64_t base = ((static_cast<int64_t>(blk) * B + (tt % B)) * row) * 2;
+        const char* kp = kbase + base;
+        const char* vp = vbase + base;
+        if constexpr (KL) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) d.k[u][r] = load_words<NW, NT>(kp + voff[r]);
+          for (int r = 0; r < 4; ++r) d.k[u][r] = load_words<NW, NT>(kp + voff[r]);
+        } else {
+#pragma unroll
+          for (int c = 0; c < QC; ++c) d.kd[u][c] = load_bf16x8<NT>(kp + koff + 64 * c);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) d.v[u][r] = load_words<NW, NT>(vp + voff[r]);
       } else {
+        // blocks of 8: the tile spans two, tokens 0-7 in the first and 8-15
+        // in the second; each lane's rows (4g + r for V and row-wise K, j
+        // for K in MFMA layout) sit in one of them
+        static_assert(B == 8, "blocks below 16 tokens: only 8 is built");
+        int64_t base[2];
 #pragma unroll
-        for (int c = 0; c < QC; ++c) d.kd[u][c] = load_bf16x8<NT>(kp + koff + 64 * c);
+        for (int p = 0; p < 2; ++p) {
+          const int phys = __builtin_amdgcn_readlane(win, EPS * (q - win_q0) + 2 * u + p);
+          const bool live = tt + B * p < t_end;
+          const bool in_range = phys >= 0 && phys < NB;
+          d.bad = d.bad || (live && !in_range);
+          base[p] = static_cast<int64_t>((live && in_range) ? phys : 0) * B * row * 2;
+        }
+        const int64_t vrow = g >= 2 ? base[1] : base[0];
+        const char* kp = kbase + vrow;
+        const char* vp = vbase + vrow;
+        if constexpr (KL) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) d.k[u][r] = load_words<NW, NT>(kp + voff[r]);
+        } else {
+          const char* kj = kbase + (j >= 8 ? base[1] : base[0]);
+#pragma unroll
+          for (int c = 0; c < QC; ++c) d.kd[u][c] = load_bf16x8<NT>(kj + koff + 64 * c);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) d.v[u][r] = load_words<NW, NT>(vp + voff[r]);
       }
-#pragma unroll
-      for (int r = 0; r < 4; ++r) d.v[u][r] = load_words<NW, NT>(vp + voff[r]);
     }
   }
 

@@ -101,7 +101,7 @@ def test_host_checks_reject_bad_arguments(lib):
                                           a["B"], a["NB"], a["scale"], a["max_len"], a["P"], a["ws"],
                                           a["ws_bytes"], a["dtype"], a["flags"], a["stream"])
     assert call(D=96) == -2
-    assert call(B=8) == -2                      # bf16 blocks of 8 are not built
+    assert call(B=12) == -2                     # bf16 blocks of 12 are not built
     assert call(Hq=7) == -1
     assert call(query=None) == -1
     assert call(out=ctypes.c_void_p(0x1004)) == -1   # misaligned

@@ -145,7 +145,8 @@ def test_attention_full_size_sampled(name):
 EDGE_LENS = [0, 1, 2, 15, 16, 17, 31, 32, 33, 63, 64, 65, 511, 512, 513, 1024, 1025, 1500]
 
 
-@pytest.mark.parametrize("D,B", [(128, 16), (128, 32), (128, 64), (64, 16), (64, 32), (64, 64)])
+@pytest.mark.parametrize("D,B", [(128, 8), (128, 16), (128, 32), (128, 64), (64, 8), (64, 16),
+                                 (64, 32), (64, 64)])
 def test_attention_edge_lengths_bf16(D, B):
     w = workloads.custom(900 + D + B, EDGE_LENS, dtype="bf16", num_q_heads=8, num_kv_heads=2,
                          head_size=D, block_size=B)
@@ -156,6 +157,18 @@ def test_attention_edge_lengths_bf16(D, B):
         got = H.attend(st, partition_size=P).cpu().numpy()
         assert not got[0].any(), "a sequence of length 0 must give zeros"
         _check_rows(got[1:], ref[1:], 2e-3, f"D={D} B={B} P={P}")
+
+
+@pytest.mark.parametrize("P", [0, 64, 512])
+def test_block_size_8_row_wise_keys(P):
+    """Blocks of 8 tokens (a 16-token tile spans two blocks) with keys loaded
+    row-wise through LDS (16 kv heads of 128 dims)."""
+    w = workloads.custom(971, [1, 7, 8, 9, 33, 700, 1029], dtype="bf16", num_q_heads=16,
+                         num_kv_heads=16, head_size=128, block_size=8)
+    ref_kv, _, _ = oracle_pool(w)
+    ref = oracle.paged_attention_ref(w.query, ref_kv, w.block_tables, w.context_lens, w.scale, w.dtype)
+    got = H.attend(H.upload(w), partition_size=P).cpu().numpy()
+    _check_rows(got, ref, 2e-3, f"B=8 row-wise keys P={P}")
 
 
 @pytest.mark.parametrize("D,B", [(64, 16), (128, 8), (64, 48), (128, 1)])

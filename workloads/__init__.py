@@ -303,22 +303,23 @@ def tiny(seed: int = 81000) -> Workload:
 
 
 def opt13b_mha(seed: int = 81001, num_seqs: int = 64, lo: int = 256, hi: int = 2048,
-               num_heads: int = 40) -> Workload:
+               num_heads: int = 40, block_size: int = 16) -> Workload:
     """OPT-13B-shaped MHA layer: 40/40 heads, D 128, B 16, bf16, L ~ U[lo, hi]."""
     rng = np.random.Generator(np.random.PCG64(seed))
     lens = rng.integers(lo, hi + 1, size=num_seqs)
     return _independent("opt13b_mha", rng, lens, dtype="bf16", num_q_heads=num_heads,
-                        num_kv_heads=num_heads, head_size=128, block_size=16)
+                        num_kv_heads=num_heads, head_size=128, block_size=block_size)
 
 
 def qwen2_gqa(seed: int = 81002, num_seqs: int = 256, median: float = 512.0,
-              sigma: float = 1.0, lo: int = 16, hi: int = 8192) -> Workload:
+              sigma: float = 1.0, lo: int = 16, hi: int = 8192,
+              block_size: int = 16) -> Workload:
     """Qwen2-0.5B-shaped GQA layer: 14/2 heads, D 64, B 16, bf16, log-normal lengths."""
     rng = np.random.Generator(np.random.PCG64(seed))
     lens = np.clip(np.rint(np.exp(np.log(median) + sigma * rng.standard_normal(num_seqs))),
                    lo, hi).astype(np.int64)
     return _independent("qwen2_gqa", rng, lens, dtype="bf16", num_q_heads=14,
-                        num_kv_heads=2, head_size=64, block_size=16)
+                        num_kv_heads=2, head_size=64, block_size=block_size)
 
 
 def shared_prefix(seed: int = 81003, num_prompts: int = 32, prompt_len: int = 1024,
@@ -408,13 +409,13 @@ def prefill(seed: int, cached_lens: Sequence[int], chunk_lens: Sequence[int], *,
 
 
 def prefill_opt13b(seed: int = 81011, num_seqs: int = 16, chunk: int = 512,
-                   max_cached: int = 1536) -> PrefillWorkload:
+                   max_cached: int = 1536, block_size: int = 16) -> PrefillWorkload:
     """OPT-13B-shaped layer (40/40 heads, D 128, B 16, bf16): chunks of 512
     prompt tokens after 0 .. 1536 cached tokens (earlier chunks or prefix hits)."""
     rng = np.random.Generator(np.random.PCG64(seed))
     cached = rng.integers(0, max_cached + 1, size=num_seqs)
     return prefill(seed + 1, cached, np.full(num_seqs, chunk), num_q_heads=40, num_kv_heads=40,
-                   head_size=128, block_size=16, name="prefill_opt13b")
+                   head_size=128, block_size=block_size, name="prefill_opt13b")
 
 
 def prefill_qwen2(seed: int = 81012, num_seqs: int = 32, max_chunk: int = 1024,
