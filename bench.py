@@ -82,15 +82,23 @@ def unique_kv_bytes(w) -> int:
     return rows * 2 * w.num_kv_heads * w.head_size * w.elem_bytes
 
 
-def measured_traffic(workload: str):
+def _is_prefill(workload: str) -> bool:
+    return workload.startswith("prefill_")
+
+
+def measured_traffic(workload: str, block_size=None):
     """HBM bytes per attention launch from the committed rocprofv3 counter
-    summary, if it was taken on the current kernel source; else None."""
+    summary, if it was taken on the current kernel source and block size;
+    else None."""
     path = os.path.join(ROOT, "profiles", "attention_traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f).get(workload)
-    if not rec or rec.get("kernel_source_sha") != kernel_source_sha():
+    sources = PREFILL_SOURCES if _is_prefill(workload) else KERNEL_SOURCES
+    if not rec or rec.get("kernel_source_sha") != kernel_source_sha(sources):
+        return None
+    if block_size is not None and rec.get("block_size", block_size) != block_size:
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -116,16 +124,23 @@ def summarize_counters(d: str, workload: str) -> int:
     import workloads
 
     csv_of = lambda c: os.path.join(d, c, "run_counter_collection.csv")
-    fetch, n, kname = _counter_means(csv_of("FETCH_SIZE"), "attention_bf16")
-    write, _, _ = _counter_means(csv_of("WRITE_SIZE"), "attention_bf16")
+    part = "prefill_bf16" if _is_prefill(workload) else "attention_bf16"
+    fetch, n, kname = _counter_means(csv_of("FETCH_SIZE"), part)
+    write, _, _ = _counter_means(csv_of("WRITE_SIZE"), part)
     # the 1 GiB copies (smaller copies of the same kernel in the run are ignored)
     cfetch, _, _ = _counter_means(csv_of("cal_FETCH_SIZE"), "copyBuffer", 1e5)
     cwrite, _, _ = _counter_means(csv_of("cal_WRITE_SIZE"), "copyBuffer", 1e5)
     fscale, wscale = (1 << 30) / (cfetch * 1024), (1 << 30) / (cwrite * 1024)
-    w = workloads.make(workload)
+    if _is_prefill(workload):
+        w = workloads.PREFILL[workload]().cache
+        sources = PREFILL_SOURCES
+    else:
+        w = workloads.make(workload)
+        sources = KERNEL_SOURCES
     rec = {
         "kernel": kname,
-        "kernel_source_sha": kernel_source_sha(),
+        "kernel_source_sha": kernel_source_sha(sources),
+        "block_size": w.block_size,
         "fetch_size_kib_per_launch": round(fetch, 2),
         "write_size_kib_per_launch": round(write, 2),
         "copy_fetch_size_kib": round(cfetch, 3),
@@ -194,8 +209,9 @@ def block_ops(w, dev, reps: int = 10) -> dict:
     one ``paged_kv_copy_blocks`` launch timed with HIP events on its stream:
     one block copied per sequence within a device pool (the copy a forked
     sample makes before its first write into a shared block), and a group of
-    blocks swapped to a pinned host pool and back (PCIe).  Caches are cold:
-    a 1 GiB fill runs before each launch.  Bytes count each
+    blocks swapped to a pinned host pool and back (PCIe).  Caches are cold
+    (a 1 GiB read runs before each launch); the copy-on-write copy is also
+    timed with warm caches.  Bytes count each
     block's keys and values once read and once written; ``memcpy_GBps`` is a
     plain contiguous device/host copy of the same bytes for comparison."""
     import numpy as np
@@ -209,17 +225,21 @@ def block_ops(w, dev, reps: int = 10) -> dict:
     rng = np.random.default_rng(5)
     cur = torch.cuda.current_stream(dev)
 
-    # a fill queued before each timed launch keeps the GPU busy while the
-    # host prepares the launch, so the events bracket the copy alone
-    filler = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    # work queued before each timed launch keeps the GPU busy while the host
+    # prepares the launch, so the events bracket the copy alone: a 1 GiB read
+    # (evicts the caches without leaving dirty lines) or a spin (caches warm)
+    sweep = torch.ones(1 << 28, dtype=torch.float32, device=dev)
 
-    def timed(fn):
+    def timed(fn, cold=True):
         fn()
         torch.cuda.synchronize()
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
               for _ in range(reps)]
         for i, (a, b) in enumerate(ev):
-            filler.fill_(i)
+            if cold:
+                sweep.sum()
+            else:
+                torch.cuda._sleep(400_000)
             a.record(cur)
             fn()
             b.record(cur)
@@ -234,7 +254,9 @@ def block_ops(w, dev, reps: int = 10) -> dict:
     src = torch.from_numpy(ids[:n]).to(dev)
     dst = torch.from_numpy(ids[n:2 * n]).to(dev)
     us = timed(lambda: pkv.copy_blocks(pool, pool, src, dst))
-    out["cow_copy"] = {"copies": n, "us": round(us, 2), "GBps": round(2 * n * blk / us / 1e3, 1)}
+    us_hot = timed(lambda: pkv.copy_blocks(pool, pool, src, dst), cold=False)
+    out["cow_copy"] = {"copies": n, "us": round(us, 2), "GBps": round(2 * n * blk / us / 1e3, 1),
+                       "us_warm_caches": round(us_hot, 2)}
 
     n_swap = 512
     host = torch.empty((2, n_swap) + geo, dtype=tdt, pin_memory=True)
@@ -432,7 +454,7 @@ def prefill_bench(args, dev) -> dict:
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
-            "traffic": None,
+            "traffic": measured_traffic(pw.name, B),
             "kernel": f"prefill_bf16_kernel<{D},{B}>" if w.dtype == "bf16" else f"prefill_f32_kernel<{D}>",
             "kernel_us": round(kernel_us, 2),
             "algorithmic_flops": flops,
@@ -646,7 +668,7 @@ def main() -> int:
     attn_gbps = ukvb / (kernel_us["attention"] * 1e-6) / 1e9
     kname = (f"attention_f32_kernel<{D}>" if not dt else
              f"attention_bf16_stream_kernel<{D},{B}>" if P == 0 else f"attention_bf16_kernel<{D},{B}>")
-    traffic = measured_traffic(w.name)
+    traffic = measured_traffic(w.name, B)
 
     result = {
         "metric": METRIC,

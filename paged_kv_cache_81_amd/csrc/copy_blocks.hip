@@ -28,16 +28,21 @@ copy_blocks_kernel(uint4* dst, int dst_nb, const uint4* src, int src_nb, const i
   const uint4* from = src + (static_cast<int64_t>(kv) * src_nb + s) * half_vecs;
   uint4* to = dst + (static_cast<int64_t>(kv) * dst_nb + d) * half_vecs;
   const int64_t begin = chunk * kChunkVecs + threadIdx.x;
-  uint4 v[kUnroll];
-#pragma unroll
-  for (int u = 0; u < kUnroll; ++u) {
-    const int64_t e = begin + u * kThreads;
-    if (e < half_vecs) v[u] = from[e];
-  }
-#pragma unroll
-  for (int u = 0; u < kUnroll; ++u) {
-    const int64_t e = begin + u * kThreads;
-    if (e < half_vecs) to[e] = v[u];
+  static_assert(kUnroll == 4, "the whole-chunk path names its four registers");
+  if ((chunk + 1) * kChunkVecs <= half_vecs) {
+    // a whole chunk: all loads in flight before the first store
+    const uint4 v0 = from[begin], v1 = from[begin + kThreads];
+    const uint4 v2 = from[begin + 2 * kThreads], v3 = from[begin + 3 * kThreads];
+    to[begin] = v0;
+    to[begin + kThreads] = v1;
+    to[begin + 2 * kThreads] = v2;
+    to[begin + 3 * kThreads] = v3;
+  } else {
+    // the ragged end of a half
+    for (int u = 0; u < kUnroll; ++u) {
+      const int64_t e = begin + u * kThreads;
+      if (e < half_vecs) to[e] = from[e];
+    }
   }
 }
 
