@@ -327,7 +327,9 @@ int paged_kv_copy_blocks(void* dst_cache, int dst_num_blocks, const void* src_ca
  *    loses its entry (the walk-through, "プレイフィックスキャッシュの詳細");
  *  - a group of sequences (every sequence sharing a block with another must
  *    be in it) is swapped out to, and back in from, a pool of num_cpu_blocks
- *    host blocks, all or nothing; the caller makes the reported copies.
+ *    host blocks, all or nothing; the caller makes the reported copies
+ *    (studying-code.tistory.com vLLM review, "All-or-Nothing Eviction" and
+ *    "스와핑(Swapping)").
  *
  * A request the pool cannot satisfy returns PKV_ERR_NO_BLOCKS and changes
  * nothing.  Sequences are named by caller-chosen int64 ids.  A manager is not

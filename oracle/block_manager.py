@@ -41,8 +41,9 @@ What is modelled, and from where:
   and time 6].
 * Running out of blocks refuses the request and changes nothing; a group of
   sequences sharing blocks is swapped out to a CPU pool, and back in, all or
-  nothing [review, the FCFS / all-or-nothing eviction passages; walkthrough,
-  preemption].
+  nothing; the CPU pool has its own allocator and a bounded number of blocks
+  [review, "All-or-Nothing Eviction" and "스와핑(Swapping)"; walkthrough,
+  "ブロックアロケーションの基本概念", the preemption paragraph].
 """
 from __future__ import annotations
 
