@@ -13,8 +13,9 @@ the K timed steps are captured in one HIP graph and replayed once.
 Prints one JSON line.  ``value`` is the KV-read throughput of the step: the
 bytes the queries read through their block tables (sum over sequences of
 L * 2 * num_kv_heads * head_size * element bytes) divided by the step time.
-``roofline`` relates the attention kernel alone (the average of per-launch HIP
-events on the launch stream) to the MI355X HBM peak; ``cpu_baseline`` times
+``roofline`` relates the attention kernel alone (its average launch duration:
+HIP events on the launch stream around a graph of consecutive launches) to
+the MI355X HBM peak; ``cpu_baseline`` times
 the CPU oracle on a bounded sample of the same workload; ``block_ops`` times
 the copy-on-write and swap block copies at the workload's block geometry.
 
@@ -35,6 +36,9 @@ if ROOT not in sys.path:
 
 METRIC = "paged decode attn µs/step + KV-read GB/s (% of MI355X HBM peak)"
 PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E, AMD's published figure
+# GPU clock cycles of the spin queued before each separately timed launch
+# (tens of microseconds: longer than the host takes to queue the launch)
+SPIN_CYCLES = 100_000
 DEFAULT_WORKLOAD = "opt13b_mha"
 # layer caches the steps cycle through: the model's depth where the workload
 # is a model's layer shape (OPT-13B 40, Qwen2-0.5B 24), else enough pools to
@@ -414,15 +418,28 @@ def prefill_bench(args, dev) -> dict:
     torch.cuda.synchronize()
     if not torch.equal(out, ref_out):
         raise SystemExit("[bench] the timed steps' output differs from the first eager step's")
+    # the prefill kernel alone: events around a graph of `reps` consecutive
+    # launches (cycling the layer pools), divided by `reps`
     reps = max(10, min(args.steps, 50))
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(reps)]
-    for r, (a, b) in enumerate(ev):
-        a.record(cur)
-        eager[r % nl]["prefill"]()
-        b.record(cur)
+    g = torch.cuda.CUDAGraph()
+    cap2 = torch.cuda.Stream(device=dev)
+    cap2.wait_stream(cur)
+    with torch.cuda.stream(cap2):
+        fs = [calls(cap2.cuda_stream, layer)["prefill"] for layer in range(nl)]
+        fs[0]()
+        cap2.synchronize()
+        with torch.cuda.graph(g, stream=cap2):
+            for r in range(reps):
+                fs[r % nl]()
+    cur.wait_stream(cap2)
     torch.cuda.synchronize()
-    kernel_us = float(np.mean([a.elapsed_time(b) for a, b in ev])) * 1e3
+    g.replay()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(cur)
+    g.replay()
+    b.record(cur)
+    torch.cuda.synchronize()
+    kernel_us = a.elapsed_time(b) * 1e3 / reps
     flops = pw.flops()
     tflops = flops / (kernel_us * 1e-6) / 1e12
     value = flops / (ms_per_step * 1e-3) / 1e12
@@ -635,28 +652,56 @@ def main() -> int:
         log("[bench] the timed steps' output differs from the first eager step's")
         return 1
 
-    # each kernel on its own: HIP events around every launch on the launch
-    # stream, cycling through the layer pools (and, with --flush, evicting
-    # the caches in between, outside the event pair)
-    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev) if args.flush else None
+    # each kernel on its own, `reps` launches in a row cycling through the
+    # layer pools: HIP events on the launch stream around one replay of a
+    # graph holding those launches, divided by `reps` -- the kernel's average
+    # launch duration, as a kernel trace reports it.  (Event pairs around
+    # single launches add the events' own few microseconds to each.)  With
+    # --flush: eager launches, each after a cache-evicting fill and a spin
+    # that keeps the GPU busy while the host queues the event pair.
     reps = max(10, min(args.steps, 100))
     names = list(eager[0])
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(reps * len(names))]
-    per = {k: [] for k in names}
-    i = 0
-    for r in range(reps):
-        for name, f in eager[r % nl].items():
-            if flush is not None:
+    kernel_us = {}
+    if args.flush:
+        flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(reps * len(names))]
+        per = {k: [] for k in names}
+        i = 0
+        for r in range(reps):
+            for name, f in eager[r % nl].items():
                 flush.fill_(r & 0xFF)
-            ev[i][0].record(cur)
-            f()
-            ev[i][1].record(cur)
-            per[name].append(i)
-            i += 1
-    torch.cuda.synchronize()
-    kernel_us = {k: float(np.mean([ev[j][0].elapsed_time(ev[j][1]) for j in idx])) * 1e3
-                 for k, idx in per.items()}
+                torch.cuda._sleep(SPIN_CYCLES)
+                ev[i][0].record(cur)
+                f()
+                ev[i][1].record(cur)
+                per[name].append(i)
+                i += 1
+        torch.cuda.synchronize()
+        kernel_us = {k: float(np.mean([ev[j][0].elapsed_time(ev[j][1]) for j in idx])) * 1e3
+                     for k, idx in per.items()}
+    else:
+        for name in names:
+            g = torch.cuda.CUDAGraph()
+            cap = torch.cuda.Stream(device=dev)
+            cap.wait_stream(cur)
+            with torch.cuda.stream(cap):
+                fs = [calls(cap.cuda_stream, layer)[name] for layer in range(nl)]
+                fs[0]()
+                cap.synchronize()
+                with torch.cuda.graph(g, stream=cap):
+                    for r in range(reps):
+                        fs[r % nl]()
+            cur.wait_stream(cap)
+            torch.cuda.synchronize()
+            g.replay()  # untimed
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(cur)
+            g.replay()
+            b.record(cur)
+            torch.cuda.synchronize()
+            kernel_us[name] = a.elapsed_time(b) * 1e3 / reps
+            del g
     log("[bench] per-kernel us: " + ", ".join(f"{k} {v:.1f}" for k, v in kernel_us.items()))
 
     kvb = kv_bytes(w)
@@ -707,10 +752,12 @@ def main() -> int:
             "traffic": traffic,
             "kernel": kname,
             "kernel_us": round(kernel_us["attention"], 2),
+            "timing": (f"HIP events around single launches" if args.flush else
+                       f"HIP events around a graph of {reps} consecutive launches"),
             "algorithmic_bytes": ukvb,
             "logical_bytes": kvb,
             "logical_GBps": round(kvb / (kernel_us["attention"] * 1e-6) / 1e9, 2),
-            "caches": ("evicted before each launch" if flush is not None else
+            "caches": ("evicted before each launch" if args.flush else
                        f"cold: launches cycle through {nl} layer pools" if nl > 1 else "warm"),
         },
         "kernel_us": {k: round(v, 2) for k, v in kernel_us.items()},
