@@ -497,6 +497,13 @@ def main() -> int:
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying a graph")
     ap.add_argument("--flush", action="store_true",
                     help="also evict caches before every per-kernel timing launch")
+    ap.add_argument("--no-shared-prefix", action="store_true",
+                    help="forked workloads: read the shared prompt per sequence (the ordinary "
+                         "decode) instead of once per group")
+    ap.add_argument("--kv-flags", choices=["auto", "streamed", "cached"], default="auto",
+                    help="K/V loads: nontemporal streaming or through the caches (auto: cached "
+                         "for forked workloads, whose shared blocks are read by several "
+                         "workgroups, else streamed)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-block-ops", action="store_true",
@@ -571,7 +578,25 @@ def main() -> int:
     ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
     out = torch.empty((S, Hq, D), dtype=torch.float32, device=dev)
     shared = bool(w.meta.get("forks"))  # forks alias their prompt's blocks
-    flags = lib_mod.PKV_ATTN_CACHED_KV if shared else 0
+    # forks read their shared prompt once per group (the shared-prefix
+    # decode) unless told to read it per sequence through the caches
+    grouped = shared and not args.no_shared_prefix
+    if args.kv_flags == "auto":
+        flags = lib_mod.PKV_ATTN_CACHED_KV if shared else 0
+    else:
+        flags = lib_mod.PKV_ATTN_CACHED_KV if args.kv_flags == "cached" else 0
+    if grouped:
+        g_starts, g_plens, g_maxp = pkv.prefix_groups(w.block_tables, w.context_lens, B)
+        n_groups = len(g_plens)
+        d_starts = torch.from_numpy(g_starts).to(dev)
+        d_plens = torch.from_numpy(g_plens).to(dev)
+        P = lib.paged_attention_shared_partition_size(S, Hq, Hkv, D, B, n_groups, g_maxp,
+                                                      args.partition_size or 0)
+        ws_bytes = pkv.shared_workspace_bytes(S, Hq, Hkv, D, B, n_groups, w.max_context_len,
+                                              g_maxp, P)
+        ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+        log(f"[bench] shared-prefix decode: {n_groups} groups, longest prefix {g_maxp}, "
+            f"partition {P}")
 
     # one cache pool per layer, all indexed by the same block tables
     nl = args.layers if args.layers is not None else DEFAULT_LAYERS.get(w.name, 4)
@@ -588,6 +613,18 @@ def main() -> int:
                   st.new_pos.data_ptr(), S, S, B, NB, stream_handle)
         write_a = (st.new_k.data_ptr(), st.new_v.data_ptr(), kv.data_ptr(),
                    st.new_slots.data_ptr(), S, NB, B, Hkv, D, dt, stream_handle)
+        if grouped:
+            sh_a = (out.data_ptr(), 0, st.query.data_ptr(), kv.data_ptr(), st.tables.data_ptr(),
+                    w.table_width, st.lens.data_ptr(), d_starts.data_ptr(), d_plens.data_ptr(),
+                    n_groups, S, Hq, Hkv, D, B, NB, w.scale, w.max_context_len, g_maxp, P,
+                    ws.data_ptr(), ws.numel(), dt, flags, stream_handle)
+            return {
+                "slot_mapping": lambda: check(lib.paged_kv_slot_mapping(*slot_a), "slot mapping"),
+                "kv_write": lambda: check(lib.paged_kv_write(*write_a), "kv write"),
+                "attention": lambda: check(lib.paged_attention_shared_partitions(*sh_a),
+                                           "attention"),
+                "merge": lambda: check(lib.paged_attention_shared_merge(*sh_a), "merge"),
+            }
         attn_a = (out.data_ptr(), 0, st.query.data_ptr(), kv.data_ptr(), st.tables.data_ptr(),
                   w.table_width, st.lens.data_ptr(), S, Hq, Hkv, D, B, NB, w.scale,
                   w.max_context_len, P, ws.data_ptr(), ws.numel(), dt, flags, stream_handle)
@@ -712,6 +749,7 @@ def main() -> int:
     # HBM peak would not be a fraction of it
     attn_gbps = ukvb / (kernel_us["attention"] * 1e-6) / 1e9
     kname = (f"attention_f32_kernel<{D}>" if not dt else
+             f"attention_bf16_shared_kernel<{D},{B}>" if grouped else
              f"attention_bf16_stream_kernel<{D},{B}>" if P == 0 else f"attention_bf16_kernel<{D},{B}>")
     traffic = measured_traffic(w.name, B)
 
@@ -741,7 +779,11 @@ def main() -> int:
                 max(1, int(w.context_lens.sum()))), 5),
             "table_bytes": int(np.ceil(w.context_lens / B).sum()) * 4,
             "graph": not args.no_graph,
-            "layers_cycled": nl, "kv_flags": "cached (shared blocks)" if shared else "streamed",
+            "layers_cycled": nl,
+            "kv_flags": "cached" if flags & lib_mod.PKV_ATTN_CACHED_KV else "streamed",
+            "attention_path": ("shared prefix (groups read their prompt once)" if grouped else
+                               "per sequence"),
+            **({"groups": n_groups, "max_prefix_len": g_maxp} if grouped else {}),
         },
         "roofline": {
             "bound": "hbm",

@@ -233,6 +233,120 @@ int paged_attention_merge(void* out, pkv_dtype out_dtype, const void* query,
                           hipStream_t stream);
 
 /*
+ * paged_attention_prefix_groups -- find groups of consecutive sequences that
+ * share their first blocks.  HOST pointers; host only.
+ *
+ * The samples of one prompt (parallel sampling, beam candidates) store the
+ * prompt's K/V once: their tables name the same physical blocks, each with a
+ * reference count above one, until a write into a shared block copies it
+ * (studying-code.tistory.com vLLM review: the two-sample example with both
+ * sequences' logical blocks 0 and 1 on physical blocks 7 and 1, section
+ * "생성 단계에서의 Copy-on-Write", and "vLLM과 Beam Search의 KV 블록 관리";
+ * tech.blogsailing.com explainer, section 3).  Sequences are scanned in batch
+ * order; a sequence joins the current group when its table starts with the
+ * same entries as the group's first sequence for at least as many tokens as
+ * the group shares so far (and at least min_prefix_len), else it starts a new
+ * group.  A group's prefix is its shared tokens, cut to a multiple of
+ * lcm(32, block_size) and to its shortest member's length; a group of one
+ * sequence has prefix 0.
+ *
+ *   block_tables   int32 [num_seqs][table_width], host
+ *   context_lens   int32 [num_seqs], host
+ *   group_starts   int32 [num_seqs + 1] (output, host): group g is sequences
+ *                  [group_starts[g], group_starts[g + 1])
+ *   prefix_lens    int32 [num_seqs] (output, host): prefix tokens of group g
+ *   num_groups, max_prefix_len  (outputs, host)
+ */
+int paged_attention_prefix_groups(const int32_t* block_tables, int table_width,
+                                  const int32_t* context_lens, int num_seqs, int block_size,
+                                  int min_prefix_len, int32_t* group_starts, int32_t* prefix_lens,
+                                  int* num_groups, int* max_prefix_len);
+
+/*
+ * Partition size (tokens) paged_attention_decode_shared uses for these
+ * arguments: partition_size itself if it is valid (a multiple of 32 and of
+ * block_size), or, for 0, a size giving prefix work items for about half
+ * the workgroups resident on the current device; -1 if invalid.  Host only.
+ */
+int paged_attention_shared_partition_size(int num_seqs, int num_q_heads, int num_kv_heads,
+                                          int head_size, int block_size, int num_groups,
+                                          int max_prefix_len, int partition_size);
+
+/*
+ * Workspace bytes paged_attention_decode_shared needs for these arguments
+ * (partition_size as given to it, 0 = automatic).  Host only.
+ */
+size_t paged_attention_shared_workspace_bytes(int num_seqs, int num_q_heads, int num_kv_heads,
+                                              int head_size, int block_size, int num_groups,
+                                              int max_context_len, int max_prefix_len,
+                                              int partition_size);
+
+/*
+ * paged_attention_decode_shared -- paged_attention_decode for a batch whose
+ * sequences come in groups sharing their first blocks (the case of
+ * paged_attention_prefix_groups).  Same result as paged_attention_decode
+ * (the same attention per sequence, up to rounding), but each group's shared
+ * prefix is read once for all its members' query heads instead of once per
+ * member; each sequence's remaining tokens are read on their own, and the
+ * parts are merged by the log-sum-exp rule.  Two launches (attention pass,
+ * merge) on `stream`.  bf16 only.
+ *
+ *   group_starts  int32 [num_groups + 1], device: group g is sequences
+ *                 [group_starts[g], group_starts[g + 1]); 0 = first <= ... <=
+ *                 last = num_seqs, else every output row is NaN
+ *   prefix_lens   int32 [num_groups], device: tokens 0 .. prefix_lens[g] - 1
+ *                 of every member of group g are read through the table of
+ *                 the group's first member.  A multiple of lcm(32, block_size),
+ *                 <= max_prefix_len, <= every member's context length; else
+ *                 the group's rows are NaN.  A member whose own table entries
+ *                 for those tokens differ from the first member's gets NaN.
+ *   num_groups    1 .. num_seqs (num_seqs <= 512)
+ *   max_prefix_len   host int >= every prefix_lens[g] (sizes the workspace)
+ *   partition_size   0 = automatic, else a multiple of 32 and of block_size
+ *   workspace     device scratch of paged_attention_shared_workspace_bytes()
+ *                 bytes, 256-byte aligned; every byte read is written first
+ *                 in the same call
+ * Other arguments, layouts and limits as paged_attention_decode.
+ */
+int paged_attention_decode_shared(void* out, pkv_dtype out_dtype, const void* query,
+                                  const void* kv_cache, const int32_t* block_tables,
+                                  int table_width, const int32_t* context_lens,
+                                  const int32_t* group_starts, const int32_t* prefix_lens,
+                                  int num_groups, int num_seqs, int num_q_heads, int num_kv_heads,
+                                  int head_size, int block_size, int num_blocks, float scale,
+                                  int max_context_len, int max_prefix_len, int partition_size,
+                                  void* workspace, size_t workspace_bytes, pkv_dtype dtype,
+                                  unsigned flags, hipStream_t stream);
+
+/*
+ * The two launches paged_attention_decode_shared makes, for timing or
+ * scheduling them separately: the attention pass (partial results of every
+ * prefix and suffix partition into the workspace) and the log-sum-exp merge
+ * into out[].  Both take exactly paged_attention_decode_shared's arguments
+ * and must be given the same ones, in this order, on the same stream.
+ */
+int paged_attention_shared_partitions(void* out, pkv_dtype out_dtype, const void* query,
+                                      const void* kv_cache, const int32_t* block_tables,
+                                      int table_width, const int32_t* context_lens,
+                                      const int32_t* group_starts, const int32_t* prefix_lens,
+                                      int num_groups, int num_seqs, int num_q_heads,
+                                      int num_kv_heads, int head_size, int block_size,
+                                      int num_blocks, float scale, int max_context_len,
+                                      int max_prefix_len, int partition_size, void* workspace,
+                                      size_t workspace_bytes, pkv_dtype dtype, unsigned flags,
+                                      hipStream_t stream);
+
+int paged_attention_shared_merge(void* out, pkv_dtype out_dtype, const void* query,
+                                 const void* kv_cache, const int32_t* block_tables,
+                                 int table_width, const int32_t* context_lens,
+                                 const int32_t* group_starts, const int32_t* prefix_lens,
+                                 int num_groups, int num_seqs, int num_q_heads, int num_kv_heads,
+                                 int head_size, int block_size, int num_blocks, float scale,
+                                 int max_context_len, int max_prefix_len, int partition_size,
+                                 void* workspace, size_t workspace_bytes, pkv_dtype dtype,
+                                 unsigned flags, hipStream_t stream);
+
+/*
  * paged_attention_prefill -- causal attention of chunks of query tokens over
  * their paged sequences: the prompt step (prefill) and chunked prefill.
  *

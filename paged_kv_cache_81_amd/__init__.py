@@ -10,6 +10,8 @@ num_kv_heads, head_size]``, index 0 keys and index 1 values.
 """
 from __future__ import annotations
 
+import ctypes
+
 from typing import Optional, Tuple
 
 import torch
@@ -270,6 +272,82 @@ def attention_prefill(query: torch.Tensor, kv_cache: torch.Tensor, block_tables:
                                      context_lens.data_ptr(), S, hq, hkv, d, b, nb, float(scale),
                                      _dt(kv_cache), _stream(kv_cache))
     check(rc, "paged_attention_prefill")
+    return out
+
+
+def prefix_groups(block_tables, context_lens, block_size: int, min_prefix_len: int = 0):
+    """Groups of consecutive sequences sharing their first blocks (host
+    arrays; ``paged_attention_prefix_groups``).  Returns ``(group_starts
+    [G + 1], prefix_lens [G], max_prefix_len)`` as int32 numpy arrays and an
+    int."""
+    import numpy as np
+    tables = np.ascontiguousarray(np.asarray(block_tables, dtype=np.int32))
+    lens = np.ascontiguousarray(np.asarray(context_lens, dtype=np.int32))
+    S = lens.shape[0]
+    if tables.ndim != 2 or tables.shape[0] != S:
+        raise ValueError("block_tables must be [S, width] for S context lengths")
+    starts = np.zeros(S + 1, dtype=np.int32)
+    plens = np.zeros(max(S, 1), dtype=np.int32)
+    ng, mp = ctypes.c_int(0), ctypes.c_int(0)
+    rc = lib.paged_attention_prefix_groups(tables.ctypes.data, tables.shape[1], lens.ctypes.data,
+                                           S, int(block_size), int(min_prefix_len),
+                                           starts.ctypes.data, plens.ctypes.data,
+                                           ctypes.byref(ng), ctypes.byref(mp))
+    check(rc, "paged_attention_prefix_groups")
+    return starts[:ng.value + 1].copy(), plens[:ng.value].copy(), mp.value
+
+
+def shared_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_size, block_size, num_groups,
+                           max_context_len, max_prefix_len, requested: int = 0) -> int:
+    return int(lib.paged_attention_shared_workspace_bytes(
+        num_seqs, num_q_heads, num_kv_heads, head_size, block_size, num_groups, max_context_len,
+        max_prefix_len, requested))
+
+
+def attention_decode_shared(query: torch.Tensor, kv_cache: torch.Tensor, block_tables: torch.Tensor,
+                            context_lens: torch.Tensor, group_starts: torch.Tensor,
+                            prefix_lens: torch.Tensor, scale: float, max_context_len: int,
+                            max_prefix_len: int, partition_size: int = 0,
+                            out: Optional[torch.Tensor] = None,
+                            out_dtype: torch.dtype = torch.float32,
+                            workspace: Optional[torch.Tensor] = None,
+                            cached_kv: bool = False) -> torch.Tensor:
+    """Paged decode attention for groups of sequences sharing their first
+    blocks (``paged_attention_decode_shared``): each group's prefix is read
+    once for all its members.  ``group_starts`` [G + 1] and ``prefix_lens``
+    [G] are int32 device tensors (see :func:`prefix_groups`).  Returns ``out``."""
+    nb, b, hkv, d = _cache_dims(kv_cache)
+    dev = kv_cache.device
+    _need(query, "query", kv_cache.dtype, 3, dev)
+    S, hq, dq = query.shape
+    if dq != d:
+        raise ValueError("query head_size differs from the cache's")
+    _need(block_tables, "block_tables", torch.int32, 2, dev)
+    _need(context_lens, "context_lens", torch.int32, 1, dev)
+    _need(group_starts, "group_starts", torch.int32, 1, dev)
+    _need(prefix_lens, "prefix_lens", torch.int32, 1, dev)
+    ng = prefix_lens.shape[0]
+    if group_starts.shape[0] != ng + 1:
+        raise ValueError("group_starts must have one more entry than prefix_lens")
+    if block_tables.shape[0] != S or context_lens.shape[0] != S:
+        raise ValueError("query, block_tables and context_lens differ in batch size")
+    if out is None:
+        out = torch.empty((S, hq, d), dtype=out_dtype, device=dev)
+    _need(out, "out", None, 3, dev)
+    if tuple(out.shape) != (S, hq, d):
+        raise ValueError("out must be [S, Hq, D]")
+    need = shared_workspace_bytes(S, hq, hkv, d, b, ng, max_context_len, max_prefix_len,
+                                  partition_size)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _need(workspace, "workspace", torch.uint8, 1, dev)
+    rc = lib.paged_attention_decode_shared(
+        out.data_ptr(), _dt(out), query.data_ptr(), kv_cache.data_ptr(), block_tables.data_ptr(),
+        block_tables.shape[1], context_lens.data_ptr(), group_starts.data_ptr(),
+        prefix_lens.data_ptr(), ng, S, hq, hkv, d, b, nb, float(scale), int(max_context_len),
+        int(max_prefix_len), int(partition_size), workspace.data_ptr(), workspace.numel(),
+        _dt(kv_cache), PKV_ATTN_CACHED_KV if cached_kv else 0, _stream(kv_cache))
+    check(rc, "paged_attention_decode_shared")
     return out
 
 

@@ -24,6 +24,8 @@ PKV_ERR_NO_BLOCKS = -5
 # every function include/paged_kv.h declares, with its C signature
 _i, _sz, _p, _f, _u = ctypes.c_int, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_float, ctypes.c_uint
 _i64 = ctypes.c_int64
+_SHARED = (_i, [_p, _i, _p, _p, _p, _i, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _f, _i, _i, _i, _p,
+                _sz, _i, _u, _p])
 SIGNATURES = {
     "pkv_last_error": (ctypes.c_char_p, []),
     "paged_kv_slot_mapping": (_i, [_p, _p, _i, _p, _p, _i, _i, _i, _i, _p]),
@@ -37,6 +39,12 @@ SIGNATURES = {
                                         _i, _i, _p, _sz, _i, _u, _p]),
     "paged_attention_merge": (_i, [_p, _i, _p, _p, _p, _i, _p, _i, _i, _i, _i, _i, _i, _f,
                                    _i, _i, _p, _sz, _i, _u, _p]),
+    "paged_attention_prefix_groups": (_i, [_p, _i, _p, _i, _i, _i, _p, _p, _p, _p]),
+    "paged_attention_shared_partition_size": (_i, [_i, _i, _i, _i, _i, _i, _i, _i]),
+    "paged_attention_shared_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i, _i, _i, _i]),
+    "paged_attention_decode_shared": _SHARED,
+    "paged_attention_shared_partitions": _SHARED,
+    "paged_attention_shared_merge": _SHARED,
     "paged_attention_prefill": (_i, [_p, _i, _p, _p, _i, _i, _p, _p, _i, _p, _i, _i, _i, _i, _i,
                                      _i, _f, _i, _p]),
     "paged_kv_copy_blocks": (_i, [_p, _i, _p, _i, _p, _p, _i, _i, _i, _i, _i, _p]),

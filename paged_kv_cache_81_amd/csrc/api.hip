@@ -598,3 +598,318 @@ int paged_attention_partitions(PKV_DECODE_PARAMS) { return decode_impl(kAttend, 
 int paged_attention_merge(PKV_DECODE_PARAMS) { return decode_impl(kMerge, PKV_DECODE_ARGS); }
 
 }  // extern "C"
+
+// ---------------------------------------------------------------- shared prefixes
+
+namespace pkv {
+namespace {
+
+// Workgroups of the shared-prefix kernel resident at once on the current
+// device (0 if it cannot be queried).
+int shared_resident_wgs() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus <= 0)
+    return 0;
+  return cus * kSharedWgsPerCu;
+}
+
+// Items of a group's prefix partition: (kv-head groups) x (16-column blocks
+// of its members' query heads); estimated for groups of equal size.
+int64_t shared_items_per_partition(int S, int Hq, int Hkv, int num_groups) {
+  const int G = Hq / Hkv;
+  const int64_t per_group = cdiv64(cdiv64(S, num_groups) * G, 16);
+  return static_cast<int64_t>(Hkv / bf16_heads_per_group(Hkv)) * per_group * num_groups;
+}
+
+// A requested partition size is checked; 0 picks the largest one that still
+// gives prefix items for about half the resident item slots (the suffix
+// items fill the rest; longer prefix partitions leave fewer parts to merge,
+// and measured no slower), or 256 tokens when there is no prefix.
+int resolve_shared_partition(int S, int Hq, int Hkv, int B, int num_groups, int max_prefix,
+                             int req) {
+  const int unit = partition_unit(B);
+  if (req < 0) return -1;
+  if (req > 0) return req % unit == 0 ? req : -1;
+  if (max_prefix <= 0 || S <= 0 || num_groups <= 0) return std::max(unit, 256 / unit * unit);
+  const int64_t slots = static_cast<int64_t>(shared_resident_wgs()) * (4 / bf16_heads_per_group(Hkv));
+  const int64_t per_part = std::max<int64_t>(1, shared_items_per_partition(S, Hq, Hkv, num_groups));
+  const int64_t parts = std::max<int64_t>(1, cdiv64(slots, 2 * per_part));
+  const int64_t P = max_prefix / parts / unit * unit;
+  return static_cast<int>(std::max<int64_t>(unit, std::min<int64_t>(P, cdiv64(max_prefix, unit) * unit)));
+}
+
+struct SharedLayout {
+  int64_t parts, ml_off, seq_off, bytes;
+};
+// Partial results [parts][S][Hq][D] floats, their (m, l) [parts][S][Hq][2],
+// then per sequence: parts, group leader, prefix length, table mismatch
+// (int32 [4][S]).
+SharedLayout shared_layout(int S, int Hq, int D, int max_len, int max_prefix, int P) {
+  auto up256 = [](int64_t b) { return (b + 255) / 256 * 256; };
+  SharedLayout l;
+  l.parts = cdiv64(std::max(max_prefix, 0), P) + cdiv64(std::max(max_len, 1), P);
+  const int64_t rows = l.parts * S * Hq;
+  l.ml_off = up256(rows * D * 4);
+  l.seq_off = l.ml_off + up256(rows * 2 * 4);
+  l.bytes = l.seq_off + up256(static_cast<int64_t>(4) * S * 4);
+  return l;
+}
+
+}  // namespace
+}  // namespace pkv
+
+extern "C" {
+
+int paged_attention_prefix_groups(const int32_t* block_tables, int table_width,
+                                  const int32_t* context_lens, int num_seqs, int block_size,
+                                  int min_prefix_len, int32_t* group_starts, int32_t* prefix_lens,
+                                  int* num_groups, int* max_prefix_len) {
+  clear_error();
+  if (num_seqs < 0 || block_size <= 0 || table_width < 0) {
+    set_error("num_seqs %d, block_size %d, table_width %d: invalid", num_seqs, block_size,
+              table_width);
+    return PKV_ERR_INVALID;
+  }
+  if (!group_starts || !num_groups || !max_prefix_len ||
+      (num_seqs > 0 && (!block_tables || !context_lens || !prefix_lens || table_width == 0))) {
+    set_error("null pointer argument");
+    return PKV_ERR_INVALID;
+  }
+  const int unit = partition_unit(block_size);
+  // whole partition units of the first `blocks` blocks, within length L
+  auto usable = [&](int64_t blocks, int L) {
+    const int64_t t = std::min<int64_t>(blocks * block_size, L);
+    return static_cast<int>(t / unit * unit);
+  };
+  auto nblocks = [&](int L) {
+    return static_cast<int>(std::min<int64_t>(cdiv64(L, block_size), table_width));
+  };
+  int ng = 0, maxp = 0;
+  group_starts[0] = 0;
+  if (num_seqs > 0) {
+    int lead = 0;
+    int64_t common = -1;  // blocks every member shares with the leader (-1: one member)
+    int min_len = std::max(context_lens[0], 0);
+    auto close = [&](int end) {
+      const int p = (end - group_starts[ng] >= 2 && common > 0) ? usable(common, min_len) : 0;
+      prefix_lens[ng] = p;
+      maxp = std::max(maxp, p);
+      group_starts[++ng] = end;
+    };
+    for (int s = 1; s < num_seqs; ++s) {
+      const int L = std::max(context_lens[s], 0);
+      const int n = std::min(nblocks(L), nblocks(std::max(context_lens[lead], 0)));
+      const int32_t* a = block_tables + static_cast<int64_t>(s) * table_width;
+      const int32_t* b = block_tables + static_cast<int64_t>(lead) * table_width;
+      int64_t k = 0;
+      while (k < n && a[k] == b[k]) ++k;
+      const int64_t cand = common < 0 ? k : std::min(common, k);
+      const int tok = usable(cand, std::min(min_len, L));
+      const int cur = common < 0 ? 0 : usable(common, min_len);
+      if (tok > 0 && tok >= min_prefix_len && tok >= cur) {
+        common = cand;
+        min_len = std::min(min_len, L);
+      } else {
+        close(s);
+        lead = s;
+        common = -1;
+        min_len = L;
+      }
+    }
+    close(num_seqs);
+  }
+  *num_groups = ng;
+  *max_prefix_len = maxp;
+  return PKV_OK;
+}
+
+int paged_attention_shared_partition_size(int num_seqs, int num_q_heads, int num_kv_heads,
+                                          int head_size, int block_size, int num_groups,
+                                          int max_prefix_len, int partition_size) {
+  clear_error();
+  if (!shape_ok(num_seqs, num_q_heads, num_kv_heads, head_size, block_size, 0, PKV_BF16)) return -1;
+  const int P = resolve_shared_partition(num_seqs, num_q_heads, num_kv_heads, block_size,
+                                         num_groups, max_prefix_len, partition_size);
+  if (P < 0) set_error("partition_size %d is not a positive multiple of %d", partition_size,
+                       partition_unit(block_size));
+  return P;
+}
+
+size_t paged_attention_shared_workspace_bytes(int num_seqs, int num_q_heads, int num_kv_heads,
+                                              int head_size, int block_size, int num_groups,
+                                              int max_context_len, int max_prefix_len,
+                                              int partition_size) {
+  const int P = paged_attention_shared_partition_size(num_seqs, num_q_heads, num_kv_heads,
+                                                      head_size, block_size, num_groups,
+                                                      max_prefix_len, partition_size);
+  if (P <= 0 || num_seqs <= 0) return 0;
+  return static_cast<size_t>(
+      shared_layout(num_seqs, num_q_heads, head_size, max_context_len, max_prefix_len, P).bytes);
+}
+
+}  // extern "C"
+
+namespace {
+
+int decode_shared_impl(int phases, void* out, pkv_dtype out_dtype, const void* query,
+                       const void* kv_cache, const int32_t* block_tables, int table_width,
+                       const int32_t* context_lens, const int32_t* group_starts,
+                       const int32_t* prefix_lens, int num_groups, int num_seqs, int num_q_heads,
+                       int num_kv_heads, int head_size, int block_size, int num_blocks,
+                       float scale, int max_context_len, int max_prefix_len, int partition_size,
+                       void* workspace, size_t workspace_bytes, pkv_dtype dtype, unsigned flags,
+                       hipStream_t stream) {
+  clear_error();
+  if (!shape_ok(num_seqs, num_q_heads, num_kv_heads, head_size, block_size, max_context_len, dtype))
+    return PKV_ERR_INVALID;
+  if (out_dtype != PKV_F32 && out_dtype != PKV_BF16) { set_error("unknown out_dtype"); return PKV_ERR_INVALID; }
+  if (dtype != PKV_BF16) {
+    set_error("shared-prefix decode: bf16 caches only");
+    return PKV_ERR_UNSUPPORTED;
+  }
+  if (head_size != 64 && head_size != 128) {
+    set_error("head_size %d is not built (64 or 128)", head_size);
+    return PKV_ERR_UNSUPPORTED;
+  }
+  if (block_size != 8 && block_size != 16 && block_size != 32 && block_size != 64) {
+    set_error("block_size %d is not built (8, 16, 32 or 64)", block_size);
+    return PKV_ERR_UNSUPPORTED;
+  }
+  if (num_seqs > kMaxCompactSeqs) {
+    set_error("shared-prefix decode: num_seqs %d above %d", num_seqs, kMaxCompactSeqs);
+    return PKV_ERR_UNSUPPORTED;
+  }
+  if (table_width <= 0 || num_blocks <= 0) { set_error("table_width and num_blocks must be positive"); return PKV_ERR_INVALID; }
+  if (!std::isfinite(scale)) { set_error("scale is not finite"); return PKV_ERR_INVALID; }
+  if (flags & ~static_cast<unsigned>(PKV_ATTN_CACHED_KV)) {
+    set_error("unknown flags 0x%x", flags);
+    return PKV_ERR_INVALID;
+  }
+  if (max_prefix_len < 0) { set_error("max_prefix_len %d < 0", max_prefix_len); return PKV_ERR_INVALID; }
+  if (num_seqs == 0) return PKV_OK;
+  if (num_groups < 1 || num_groups > num_seqs) {
+    set_error("num_groups %d outside [1, num_seqs = %d]", num_groups, num_seqs);
+    return PKV_ERR_INVALID;
+  }
+  if (!out || !query || !kv_cache || !block_tables || !context_lens || !group_starts ||
+      !prefix_lens) {
+    set_error("null pointer argument");
+    return PKV_ERR_INVALID;
+  }
+  if (!aligned16(out) || !aligned16(query) || !aligned16(kv_cache)) {
+    set_error("out, query and kv_cache must be 16-byte aligned");
+    return PKV_ERR_INVALID;
+  }
+  const int P = resolve_shared_partition(num_seqs, num_q_heads, num_kv_heads, block_size,
+                                         num_groups, max_prefix_len, partition_size);
+  if (P <= 0) {
+    set_error("partition_size %d is not a positive multiple of %d", partition_size,
+              partition_unit(block_size));
+    return PKV_ERR_INVALID;
+  }
+  const SharedLayout lay =
+      shared_layout(num_seqs, num_q_heads, head_size, max_context_len, max_prefix_len, P);
+  if (!workspace || workspace_bytes < static_cast<size_t>(lay.bytes)) {
+    set_error("workspace of %zu bytes is smaller than the %lld needed", workspace_bytes,
+              static_cast<long long>(lay.bytes));
+    return PKV_ERR_WORKSPACE;
+  }
+  if (reinterpret_cast<uintptr_t>(workspace) & 255u) {
+    set_error("workspace must be 256-byte aligned");
+    return PKV_ERR_INVALID;
+  }
+  // work items (counted in 32-bit integers): prefix items are at most
+  // (kv-head groups) x (column blocks, at most S*G/16 + groups) x parts,
+  // suffix items (kv-head groups) x (head chunks) x parts per sequence
+  const int G = num_q_heads / num_kv_heads;
+  const int HG = bf16_heads_per_group(num_kv_heads);
+  const int64_t hgn = num_kv_heads / HG;
+  const int64_t upper =
+      hgn * (cdiv64(static_cast<int64_t>(num_seqs) * G, 16) + num_groups) *
+          cdiv64(max_prefix_len, P) +
+      static_cast<int64_t>(num_seqs) * hgn * cdiv64(G, 16) * cdiv64(std::max(max_context_len, 1), P);
+  if (upper >= (int64_t{1} << 31) || lay.parts * num_seqs * num_q_heads >= (int64_t{1} << 31)) {
+    set_error("shared-prefix decode: too many work items or workspace rows");
+    return PKV_ERR_UNSUPPORTED;
+  }
+  const int resident = shared_resident_wgs();
+  if (resident <= 0) {
+    set_error("cannot query the current device");
+    return PKV_ERR_HIP;
+  }
+  const int nslot = 4 / HG;
+  int64_t wgs = std::min<int64_t>(resident, cdiv64(upper, nslot));
+  if (wgs >= 16) wgs = cdiv64(wgs, 16) * 16;  // whole blocks of 16 for the XCD pairing
+  wgs = std::max<int64_t>(1, wgs);
+
+  AttnArgs a{};
+  a.out = out;
+  a.query = query;
+  a.kv = kv_cache;
+  a.tables = block_tables;
+  a.lens = context_lens;
+  a.width = table_width;
+  a.S = num_seqs;
+  a.Hq = num_q_heads;
+  a.Hkv = num_kv_heads;
+  a.D = head_size;
+  a.B = block_size;
+  a.NB = num_blocks;
+  a.partition = P;
+  a.max_parts = static_cast<int>(lay.parts);
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.out_bf16 = out_dtype == PKV_BF16 ? 1 : 0;
+  a.nontemporal = (flags & PKV_ATTN_CACHED_KV) ? 0 : 1;
+  a.k_via_lds = static_cast<int64_t>(num_kv_heads) * head_size * 2 >= 4096;
+  a.max_len = max_context_len;
+  a.group_starts = group_starts;
+  a.prefix_lens = prefix_lens;
+  a.num_groups = num_groups;
+  a.max_prefix = max_prefix_len;
+  a.stream_waves = static_cast<int>(wgs) * 4;
+  shared_lds_plan(head_size, a.k_via_lds != 0, &a.stream_slots, &a.stream_wave_floats);
+  char* ws = static_cast<char*>(workspace);
+  a.ws_o = reinterpret_cast<float*>(ws);
+  a.ws_ml = reinterpret_cast<float*>(ws + lay.ml_off);
+  a.ws_seq = reinterpret_cast<int*>(ws + lay.seq_off);
+  if (phases & kAttend) {
+    const int rc = launch_attention_bf16_shared(a, stream);
+    if (rc != PKV_OK) return rc;
+  }
+  if (phases & kMerge) return launch_reduce_shared(a, stream);
+  return PKV_OK;
+}
+
+}  // namespace
+
+#define PKV_SHARED_ARGS                                                                          \
+  out, out_dtype, query, kv_cache, block_tables, table_width, context_lens, group_starts,        \
+      prefix_lens, num_groups, num_seqs, num_q_heads, num_kv_heads, head_size, block_size,       \
+      num_blocks, scale, max_context_len, max_prefix_len, partition_size, workspace,             \
+      workspace_bytes, dtype, flags, stream
+
+#define PKV_SHARED_PARAMS                                                                        \
+  void *out, pkv_dtype out_dtype, const void *query, const void *kv_cache,                       \
+      const int32_t *block_tables, int table_width, const int32_t *context_lens,                 \
+      const int32_t *group_starts, const int32_t *prefix_lens, int num_groups, int num_seqs,     \
+      int num_q_heads, int num_kv_heads, int head_size, int block_size, int num_blocks,          \
+      float scale, int max_context_len, int max_prefix_len, int partition_size, void *workspace, \
+      size_t workspace_bytes, pkv_dtype dtype, unsigned flags, hipStream_t stream
+
+extern "C" {
+
+int paged_attention_decode_shared(PKV_SHARED_PARAMS) {
+  return decode_shared_impl(kAttend | kMerge, PKV_SHARED_ARGS);
+}
+
+int paged_attention_shared_partitions(PKV_SHARED_PARAMS) {
+  return decode_shared_impl(kAttend, PKV_SHARED_ARGS);
+}
+
+int paged_attention_shared_merge(PKV_SHARED_PARAMS) {
+  return decode_shared_impl(kMerge, PKV_SHARED_ARGS);
+}
+
+}  // extern "C"

@@ -162,10 +162,17 @@ struct Wave {
   // and the first table window.
   __device__ __forceinline__ void begin(const AttnArgs& a, int s, int kvh, int h0, int nh, int t0,
                                         int t1) {
-    const uint16_t* qp = static_cast<const uint16_t*>(a.query) +
-                         (static_cast<int64_t>(s) * a.Hq + h0 + j) * D + 8 * g;
+    begin_rows(a, j < nh ? static_cast<int64_t>(s) * a.Hq + h0 + j : -1, s, kvh, t0, t1);
+  }
+
+  // The same with any query rows: column j of the score tile is query row
+  // qrow (of the [S * Hq] rows; qrow < 0: no query, a zero column) of the
+  // lane's j, and the tokens are read through table row s.
+  __device__ __forceinline__ void begin_rows(const AttnArgs& a, int64_t qrow, int s, int kvh, int t0,
+                                             int t1) {
+    const uint16_t* qp = static_cast<const uint16_t*>(a.query) + (qrow < 0 ? 0 : qrow) * D + 8 * g;
 #pragma unroll
-    for (int c = 0; c < QC; ++c) qf[c] = (j < nh) ? load_bf16x8<false>(qp + 32 * c) : bf16x8{};
+    for (int c = 0; c < QC; ++c) qf[c] = (qrow >= 0) ? load_bf16x8<false>(qp + 32 * c) : bf16x8{};
     const uint16_t* kb = static_cast<const uint16_t*>(a.kv) + static_cast<int64_t>(kvh) * D;
     kbase = reinterpret_cast<const char*>(kb);
     vbase = reinterpret_cast<const char*>(kb + static_cast<int64_t>(NB) * B * row);

@@ -90,6 +90,14 @@ struct AttnArgs {
   int stream_wave_floats;  // LDS floats of one wave
   int* ws_pref;            // [S + 1] first stream step of each sequence
   int max_len;             // longest valid context (longer ones give NaN)
+  // shared-prefix schedule (sequences in groups that read their first
+  // prefix_lens[g] tokens through identical table entries)
+  const int32_t* group_starts;  // [num_groups + 1]
+  const int32_t* prefix_lens;   // [num_groups]
+  int num_groups;
+  int max_prefix;               // longest valid prefix (longer ones give NaN)
+  int* ws_seq;                  // [4][S]: parts of each sequence (or -1), its group's
+                                // first sequence, its prefix length, table mismatch
 };
 
 // Stream schedule: wave w of W reads stream steps [start(w), start(w + 1))
@@ -108,6 +116,8 @@ __host__ __device__ inline int64_t stream_wave_of(int64_t x, int64_t T, int64_t 
 constexpr int kMaxRankedSeqs = 128;
 // largest batch whose bf16 workgroups can number the work items themselves
 constexpr int kMaxCompactSeqs = 512;
+// most groups (and sequences, kMaxCompactSeqs) the shared-prefix schedule takes
+constexpr int kMaxSharedGroups = 512;
 // largest batch the stream schedule takes (its workgroups scan the lengths);
 // it serves batches of fewer than 512 (sequence, kv-head group) units
 constexpr int kMaxStreamSeqs = 512;
@@ -157,6 +167,27 @@ inline void stream_lds_plan(int G, int D, bool k_tile, int* slots, int* wave_flo
   *wave_floats = (tile + k * stream_slot_floats(G, D) + 3) / 4 * 4;
 }
 
+// Shared-prefix schedule: static LDS of a workgroup's plan (group starts,
+// item scans, prefix lengths, sequence lengths), ints describing where a
+// finished result goes, and the LDS floats of one result (16 rows of D + 4,
+// their (m, l), its description).  Two workgroups per CU (registers).
+constexpr int kSharedPlanInts = 2 * (kMaxSharedGroups + 1) + 3 * kMaxCompactSeqs + 5 +
+                                (kMaxSharedGroups + 1 + kMaxCompactSeqs + 1) / 2;
+constexpr int kSharedMeta = 8;
+constexpr int kSharedWgsPerCu = 2;
+inline int shared_slot_floats(int D) { return 16 * (D + 4) + 2 * 16 + kSharedMeta; }
+// Finished results each wave keeps in LDS (1 .. 4) and LDS floats per wave.
+inline void shared_lds_plan(int D, bool k_tile, int* slots, int* wave_floats) {
+  size_t per_wg = 160 * 1024 / kSharedWgsPerCu - kSharedPlanInts * sizeof(int) - 256;
+  if (per_wg > bf16_lds_limit()) per_wg = bf16_lds_limit();
+  const int per_wave = static_cast<int>(per_wg / 4 / sizeof(float));
+  const int tile = k_tile ? 16 * D : 0;
+  int k = (per_wave - tile) / shared_slot_floats(D);
+  k = k < 1 ? 1 : (k > 4 ? 4 : k);
+  *slots = k;
+  *wave_floats = (tile + k * shared_slot_floats(D) + 3) / 4 * 4;
+}
+
 // Prefill (chunked) attention: sequence s's chunk is query rows
 // [qstart[s], qstart[s + 1]) at positions lens[s] - chunk_len .. lens[s] - 1.
 struct PrefillArgs {
@@ -179,6 +210,8 @@ int launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream);
 int launch_prefill_f32(const PrefillArgs& a, hipStream_t stream);
 
 int launch_attention_bf16(const AttnArgs& a, hipStream_t stream);
+int launch_attention_bf16_shared(const AttnArgs& a, hipStream_t stream);
+int launch_reduce_shared(const AttnArgs& a, hipStream_t stream);
 int launch_attention_bf16_stream(const AttnArgs& a, hipStream_t stream);
 int launch_attention_f32(const AttnArgs& a, hipStream_t stream);
 int launch_reduce(const AttnArgs& a, hipStream_t stream);

@@ -185,7 +185,72 @@ __global__ void __launch_bounds__(64 * kWaves) reduce_stream_kernel(AttnArgs a) 
                  static_cast<int>(w1 - w0 + 1), sh * D);
 }
 
+// Shared-prefix schedule: sequence s has ws_seq[s] parts (-1: NaN output,
+// 0: an empty context, zero output); part p of (s, h) is workspace row
+// p*S*Hq + s*Hq + h, so each part of a sequence is Hq*D contiguous floats.
+// ws_seq[3S + s] is set when s's own table entries for its group's prefix
+// differ from those the prefix was read through: NaN.  One workgroup per
+// sequence; thread t combines the parts of dims 4e .. 4e + 3 of its rows (e =
+// t, t + 256, ...), parts in order, so every load instruction reads 4 KB of
+// one part.  A part with NaN statistics poisons its row.
+__global__ void __launch_bounds__(256) reduce_shared_kernel(AttnArgs a) {
+  const int s = blockIdx.x;
+  const int64_t SH = static_cast<int64_t>(a.S) * a.Hq;
+  const int np = a.ws_seq[s];
+  const bool bad = np < 0 || a.ws_seq[3 * a.S + s] != 0;
+  const int nvec = a.Hq * a.D / 4;
+  const int64_t row0 = static_cast<int64_t>(s) * a.Hq;
+  for (int e = threadIdx.x; e < nvec; e += blockDim.x) {
+    const int h = 4 * e / a.D;
+    const int64_t row = row0 + h;
+    float4 r;
+    if (bad || np <= 0) {
+      const float v = bad ? NAN : 0.f;
+      r = make_float4(v, v, v, v);
+    } else {
+      float M = -INFINITY;
+      bool poison = false;
+      for (int p = 0; p < np; ++p) {
+        const float m = a.ws_ml[2 * (p * SH + row)];
+        const float l = a.ws_ml[2 * (p * SH + row) + 1];
+        poison = poison || m != m || l != l;
+        M = fmaxf(M, m);
+      }
+      const float Mu = M == -INFINITY ? 0.f : M;
+      float den = 0.f;
+      float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+      for (int p = 0; p < np; ++p) {
+        const float w = a.ws_ml[2 * (p * SH + row) + 1] *
+                        __builtin_amdgcn_exp2f(a.ws_ml[2 * (p * SH + row)] - Mu);
+        const float4 o = *reinterpret_cast<const float4*>(a.ws_o + (p * SH + row0) * a.D + 4 * e);
+        den += w;
+        acc.x = fmaf(w, o.x, acc.x);
+        acc.y = fmaf(w, o.y, acc.y);
+        acc.z = fmaf(w, o.z, acc.z);
+        acc.w = fmaf(w, o.w, acc.w);
+      }
+      const float inv = den > 0.f ? 1.f / den : 0.f;
+      r = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+      if (poison) r = make_float4(NAN, NAN, NAN, NAN);
+    }
+    const int64_t off = row0 * a.D + 4 * static_cast<int64_t>(e);
+    if (a.out_bf16) {
+      const uint32_t lo = f32_to_bf16(r.x) | (static_cast<uint32_t>(f32_to_bf16(r.y)) << 16);
+      const uint32_t hi = f32_to_bf16(r.z) | (static_cast<uint32_t>(f32_to_bf16(r.w)) << 16);
+      *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + off) = make_uint2(lo, hi);
+    } else {
+      *reinterpret_cast<float4*>(static_cast<float*>(a.out) + off) = r;
+    }
+  }
+}
+
 }  // namespace
+
+int launch_reduce_shared(const AttnArgs& a, hipStream_t stream) {
+  if (a.S == 0) return PKV_OK;
+  reduce_shared_kernel<<<dim3(a.S), dim3(256), 0, stream>>>(a);
+  return check_launch("partition merge (shared prefix)");
+}
 
 int launch_reduce(const AttnArgs& a, hipStream_t stream) {
   if (a.S == 0 || (!a.stream && a.max_parts <= 1)) return PKV_OK;

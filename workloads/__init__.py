@@ -323,13 +323,16 @@ def qwen2_gqa(seed: int = 81002, num_seqs: int = 256, median: float = 512.0,
 
 
 def shared_prefix(seed: int = 81003, num_prompts: int = 32, prompt_len: int = 1024,
-                  forks: int = 8, max_private: int = 256) -> Workload:
-    """32 prompts of 1024 tokens, 8 forks each aliasing them, 0-256 private tokens."""
+                  forks: int = 8, max_private: int = 256, *, num_q_heads: int = 32,
+                  num_kv_heads: int = 8, head_size: int = 128, block_size: int = 16) -> Workload:
+    """32 prompts of 1024 tokens, 8 forks each aliasing them, 0-256 private
+    tokens (GQA 32/8, D 128, B 16, bf16; other head and block shapes for
+    parity cases)."""
     rng = np.random.Generator(np.random.PCG64(seed))
     return _shared_prefix("shared_prefix", rng, num_prompts=num_prompts,
                           prompt_len=prompt_len, forks=forks, max_private=max_private,
-                          dtype="bf16", num_q_heads=32, num_kv_heads=8, head_size=128,
-                          block_size=16)
+                          dtype="bf16", num_q_heads=num_q_heads, num_kv_heads=num_kv_heads,
+                          head_size=head_size, block_size=block_size)
 
 
 def long_context(seed: int = 81004, num_seqs: int = 16, context_len: int = 32768,
