@@ -2,9 +2,9 @@
 """One-GPU benchmark of the paged decode step.
 
 A step is one pass of the whole hot path over one batch for one attention
-layer: the slot of each sequence's new token (slot mapping), the KV write, the
-attention pass over the paged cache and the log-sum-exp merge of context
-partitions.  A model has many layers, each with its own cache pool indexed by
+layer: the slot of each sequence's new token (slot mapping) and the KV write
+(one launch, paged_kv_write_positions), the attention pass over the paged
+cache and the log-sum-exp merge of context partitions.  A model has many layers, each with its own cache pool indexed by
 the same block tables; consecutive steps here cycle through ``--layers`` such
 pools, as the layers of a decode step do, so no step finds its K/V still in a
 cache from the previous one.  Inputs are resident in HBM before timing starts;
@@ -368,12 +368,10 @@ def prefill_bench(args, dev) -> dict:
     def calls(sh, layer):
         kv = pools[layer]
         return {
-            "slot_mapping": lambda: check(lib.paged_kv_slot_mapping(
-                cslots.data_ptr(), st.tables.data_ptr(), w.table_width, cseq.data_ptr(),
-                cpos.data_ptr(), T, S, B, NB, sh), "slot mapping"),
-            "kv_write": lambda: check(lib.paged_kv_write(
-                ck.data_ptr(), cv.data_ptr(), kv.data_ptr(), cslots.data_ptr(), T, NB, B, Hkv, D,
-                dt, sh), "kv write"),
+            "kv_write": lambda: check(lib.paged_kv_write_positions(
+                ck.data_ptr(), cv.data_ptr(), kv.data_ptr(), st.tables.data_ptr(), w.table_width,
+                cseq.data_ptr(), cpos.data_ptr(), cslots.data_ptr(), T, S, NB, B, Hkv, D, dt, sh),
+                "kv write"),
             "prefill": lambda: check(lib.paged_attention_prefill(
                 out.data_ptr(), 0, q.data_ptr(), qs.data_ptr(), T, pw.max_query_len,
                 kv.data_ptr(), st.tables.data_ptr(), w.table_width, st.lens.data_ptr(), S, Hq,
@@ -497,6 +495,10 @@ def main() -> int:
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying a graph")
     ap.add_argument("--flush", action="store_true",
                     help="also evict caches before every per-kernel timing launch")
+    ap.add_argument("--separate-slot-mapping", action="store_true",
+                    help="derive the new tokens' slots and write their K/V in two launches "
+                         "(paged_kv_slot_mapping, paged_kv_write) instead of one "
+                         "(paged_kv_write_positions)")
     ap.add_argument("--no-shared-prefix", action="store_true",
                     help="forked workloads: read the shared prompt per sequence (the ordinary "
                          "decode) instead of once per group")
@@ -613,14 +615,27 @@ def main() -> int:
                   st.new_pos.data_ptr(), S, S, B, NB, stream_handle)
         write_a = (st.new_k.data_ptr(), st.new_v.data_ptr(), kv.data_ptr(),
                    st.new_slots.data_ptr(), S, NB, B, Hkv, D, dt, stream_handle)
+        # slot of each new token and its write in one launch (the slots are
+        # recorded too), or the two separate launches
+        wpos_a = (st.new_k.data_ptr(), st.new_v.data_ptr(), kv.data_ptr(), st.tables.data_ptr(),
+                  w.table_width, None, st.new_pos.data_ptr(), st.new_slots.data_ptr(), S, S, NB, B,
+                  Hkv, D, dt, stream_handle)
+        if args.separate_slot_mapping:
+            write_step = {
+                "slot_mapping": lambda: check(lib.paged_kv_slot_mapping(*slot_a), "slot mapping"),
+                "kv_write": lambda: check(lib.paged_kv_write(*write_a), "kv write"),
+            }
+        else:
+            write_step = {
+                "kv_write": lambda: check(lib.paged_kv_write_positions(*wpos_a), "kv write"),
+            }
         if grouped:
             sh_a = (out.data_ptr(), 0, st.query.data_ptr(), kv.data_ptr(), st.tables.data_ptr(),
                     w.table_width, st.lens.data_ptr(), d_starts.data_ptr(), d_plens.data_ptr(),
                     n_groups, S, Hq, Hkv, D, B, NB, w.scale, w.max_context_len, g_maxp, P,
                     ws.data_ptr(), ws.numel(), dt, flags, stream_handle)
             return {
-                "slot_mapping": lambda: check(lib.paged_kv_slot_mapping(*slot_a), "slot mapping"),
-                "kv_write": lambda: check(lib.paged_kv_write(*write_a), "kv write"),
+                **write_step,
                 "attention": lambda: check(lib.paged_attention_shared_partitions(*sh_a),
                                            "attention"),
                 "merge": lambda: check(lib.paged_attention_shared_merge(*sh_a), "merge"),
@@ -629,8 +644,7 @@ def main() -> int:
                   w.table_width, st.lens.data_ptr(), S, Hq, Hkv, D, B, NB, w.scale,
                   w.max_context_len, P, ws.data_ptr(), ws.numel(), dt, flags, stream_handle)
         return {
-            "slot_mapping": lambda: check(lib.paged_kv_slot_mapping(*slot_a), "slot mapping"),
-            "kv_write": lambda: check(lib.paged_kv_write(*write_a), "kv write"),
+            **write_step,
             "attention": lambda: check(lib.paged_attention_partitions(*attn_a), "attention"),
             "merge": lambda: check(lib.paged_attention_merge(*attn_a), "merge"),
         }

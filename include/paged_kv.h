@@ -118,6 +118,29 @@ int paged_kv_write(const void* key, const void* value, void* kv_cache, const int
                    int head_size, pkv_dtype dtype, hipStream_t stream);
 
 /*
+ * paged_kv_write_positions -- paged_kv_slot_mapping and paged_kv_write in one
+ * launch: each token's slot is derived from its sequence's table and its
+ * position (the same rule and the same -1 cases as paged_kv_slot_mapping:
+ * itan.pw walk-through, "ブロックアロケーションの基本概念", slot_mapping) and
+ * its key and value are stored there (studying-code.tistory.com vLLM review,
+ * "디코딩 과정").  A token whose slot is -1 writes nothing.  slot_mapping, if
+ * not NULL, receives the slots.  Bit-exact; distinct tokens must have
+ * distinct slots.
+ *
+ *   key, value    dtype [num_tokens][num_kv_heads][head_size]
+ *   kv_cache      dtype [2][num_blocks][block_size][num_kv_heads][head_size]   (in/out)
+ *   block_tables  int32 [num_seqs][table_width]
+ *   seq_ids       int32 [num_tokens] or NULL (token i belongs to sequence i)
+ *   positions     int32 [num_tokens]
+ *   slot_mapping  int64 [num_tokens] (output) or NULL
+ */
+int paged_kv_write_positions(const void* key, const void* value, void* kv_cache,
+                             const int32_t* block_tables, int table_width, const int32_t* seq_ids,
+                             const int32_t* positions, int64_t* slot_mapping, int num_tokens,
+                             int num_seqs, int num_blocks, int block_size, int num_kv_heads,
+                             int head_size, pkv_dtype dtype, hipStream_t stream);
+
+/*
  * paged_kv_gather -- read every sequence's keys and values, in logical order,
  * through its block table into contiguous arrays (a checking path).
  *

@@ -103,6 +103,43 @@ def write(key: torch.Tensor, value: torch.Tensor, kv_cache: torch.Tensor,
     check(rc, "paged_kv_write")
 
 
+def write_positions(key: torch.Tensor, value: torch.Tensor, kv_cache: torch.Tensor,
+                    block_tables: torch.Tensor, positions: torch.Tensor,
+                    seq_ids: Optional[torch.Tensor] = None,
+                    slot_mapping: Optional[torch.Tensor] = None) -> Optional[torch.Tensor]:
+    """Store key[t] / value[t] at the slot of (seq_ids[t] or t, positions[t])
+    found through the block tables, in one launch; fills ``slot_mapping``
+    (int64 [T]) with the slots if given and returns it."""
+    nb, b, hkv, d = _cache_dims(kv_cache)
+    dev = kv_cache.device
+    for name, t in (("key", key), ("value", value)):
+        _need(t, name, kv_cache.dtype, 3, dev)
+        if tuple(t.shape[1:]) != (hkv, d):
+            raise ValueError(f"{name} must be [T, {hkv}, {d}]")
+    _need(block_tables, "block_tables", torch.int32, 2, dev)
+    _need(positions, "positions", torch.int32, 1, dev)
+    T = key.shape[0]
+    if value.shape[0] != T or positions.shape[0] != T:
+        raise ValueError("key, value and positions differ in length")
+    if seq_ids is not None:
+        _need(seq_ids, "seq_ids", torch.int32, 1, dev)
+        if seq_ids.shape[0] != T:
+            raise ValueError("seq_ids and positions differ in length")
+    elif T > block_tables.shape[0]:
+        raise ValueError("without seq_ids, token i belongs to sequence i")
+    if slot_mapping is not None:
+        _need(slot_mapping, "slot_mapping", torch.int64, 1, dev)
+        if slot_mapping.shape[0] != T:
+            raise ValueError("slot_mapping must have one entry per token")
+    rc = lib.paged_kv_write_positions(
+        key.data_ptr(), value.data_ptr(), kv_cache.data_ptr(), block_tables.data_ptr(),
+        block_tables.shape[1], seq_ids.data_ptr() if seq_ids is not None else None,
+        positions.data_ptr(), slot_mapping.data_ptr() if slot_mapping is not None else None, T,
+        block_tables.shape[0], nb, b, hkv, d, _dt(kv_cache), _stream(kv_cache))
+    check(rc, "paged_kv_write_positions")
+    return slot_mapping
+
+
 def gather(kv_cache: torch.Tensor, block_tables: torch.Tensor, context_lens: torch.Tensor,
            max_context_len: int) -> Tuple[torch.Tensor, torch.Tensor]:
     """K and V of every sequence in logical order: two [S, max_len, Hkv, D] tensors."""

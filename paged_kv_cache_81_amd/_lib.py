@@ -30,6 +30,8 @@ SIGNATURES = {
     "pkv_last_error": (ctypes.c_char_p, []),
     "paged_kv_slot_mapping": (_i, [_p, _p, _i, _p, _p, _i, _i, _i, _i, _p]),
     "paged_kv_write": (_i, [_p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _p]),
+    "paged_kv_write_positions": (_i, [_p, _p, _p, _p, _i, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i,
+                                      _p]),
     "paged_kv_gather": (_i, [_p, _p, _p, _p, _i, _p, _i, _i, _i, _i, _i, _i, _i, _p]),
     "paged_attention_partition_size": (_i, [_i, _i, _i, _i, _i, _i, _i, _i]),
     "paged_attention_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i, _i, _i]),

@@ -222,6 +222,37 @@ int paged_kv_write(const void* key, const void* value, void* kv_cache, const int
                       num_kv_heads, head_size, eb, stream);
 }
 
+int paged_kv_write_positions(const void* key, const void* value, void* kv_cache,
+                             const int32_t* block_tables, int table_width, const int32_t* seq_ids,
+                             const int32_t* positions, int64_t* slot_mapping, int num_tokens,
+                             int num_seqs, int num_blocks, int block_size, int num_kv_heads,
+                             int head_size, pkv_dtype dtype, hipStream_t stream) {
+  clear_error();
+  const int eb = elem_bytes(dtype);
+  if (eb == 0) { set_error("kv write: unknown dtype"); return PKV_ERR_INVALID; }
+  if (num_tokens < 0 || num_seqs < 0 || table_width <= 0 || num_blocks <= 0 || block_size <= 0 ||
+      num_kv_heads <= 0 || head_size <= 0) {
+    set_error("kv write: bad sizes");
+    return PKV_ERR_INVALID;
+  }
+  if ((head_size * eb) % 16) {
+    set_error("kv write: head_size*%d bytes must be a multiple of 16", eb);
+    return PKV_ERR_UNSUPPORTED;
+  }
+  if (num_tokens == 0) return PKV_OK;
+  if (!key || !value || !kv_cache || !block_tables || !positions) {
+    set_error("kv write: null pointer");
+    return PKV_ERR_INVALID;
+  }
+  if (!aligned16(key) || !aligned16(value) || !aligned16(kv_cache)) {
+    set_error("kv write: key, value and cache must be 16-byte aligned");
+    return PKV_ERR_INVALID;
+  }
+  return launch_write_positions(key, value, kv_cache, block_tables, table_width, seq_ids, positions,
+                                slot_mapping, num_tokens, num_seqs, num_blocks, block_size,
+                                num_kv_heads, head_size, eb, stream);
+}
+
 int paged_kv_gather(void* k_out, void* v_out, const void* kv_cache, const int32_t* block_tables,
                     int table_width, const int32_t* context_lens, int num_seqs, int num_kv_heads,
                     int head_size, int block_size, int num_blocks, int max_context_len,

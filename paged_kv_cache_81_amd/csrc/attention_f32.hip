@@ -16,11 +16,14 @@ namespace {
 constexpr int kMaxPart = 512;
 constexpr int kMaxHeads = 16;
 
-template <int D>
+// NH: query heads one wave serves (the group's heads, rounded up to a power
+// of two; the padding rows of q are zero), fixed at compile time so that no
+// per-head branch separates the loads from the arithmetic.
+template <int D, int NH>
 __global__ void __launch_bounds__(64) attention_f32_kernel(AttnArgs a) {
   constexpr int PER = D / 64;  // output dims per lane
-  __shared__ float s_q[kMaxHeads][D];
-  __shared__ float s_p[kMaxHeads][kMaxPart];
+  __shared__ float s_q[NH][D];
+  __shared__ float s_p[NH][kMaxPart];
   __shared__ int s_phys[kMaxPart];  // physical block of each token of the partition
 
   const int lane = threadIdx.x;
@@ -38,11 +41,11 @@ __global__ void __launch_bounds__(64) attention_f32_kernel(AttnArgs a) {
   const bool bad_seq = L < 0 || (L + B - 1) / B > a.width || nparts > a.max_parts;
   if (part > 0 && (bad_seq || part >= nparts)) return;
 
-  const int nh = min(kMaxHeads, G - chunk * kMaxHeads);
+  const int nh = min(NH, G - chunk * kMaxHeads);
   const int h0 = kvh * G + chunk * kMaxHeads;
   const float* q = static_cast<const float*>(a.query);
-  for (int i = lane; i < nh * D; i += 64)
-    s_q[i / D][i % D] = q[(static_cast<int64_t>(s) * a.Hq + h0) * D + i];
+  for (int i = lane; i < NH * D; i += 64)
+    s_q[i / D][i % D] = i < nh * D ? q[(static_cast<int64_t>(s) * a.Hq + h0) * D + i] : 0.f;
   __syncthreads();
 
   const int t_begin = part * P;
@@ -59,9 +62,9 @@ __global__ void __launch_bounds__(64) attention_f32_kernel(AttnArgs a) {
     const int t = t_begin + i;
     const int phys = trow[t / B];
     s_phys[i] = phys;
-    float dot[kMaxHeads];
+    float dot[NH];
 #pragma unroll
-    for (int h = 0; h < kMaxHeads; ++h) dot[h] = 0.f;
+    for (int h = 0; h < NH; ++h) dot[h] = 0.f;
     if (phys < 0 || phys >= a.NB) {
       bad = true;
     } else {
@@ -69,77 +72,73 @@ __global__ void __launch_bounds__(64) attention_f32_kernel(AttnArgs a) {
       for (int c = 0; c < D / 4; ++c) {
         const float4 kk = kr[c];
 #pragma unroll
-        for (int h = 0; h < kMaxHeads; ++h) {
-          if (h < nh) {
-            dot[h] = fmaf(kk.x, s_q[h][4 * c + 0], dot[h]);
-            dot[h] = fmaf(kk.y, s_q[h][4 * c + 1], dot[h]);
-            dot[h] = fmaf(kk.z, s_q[h][4 * c + 2], dot[h]);
-            dot[h] = fmaf(kk.w, s_q[h][4 * c + 3], dot[h]);
-          }
+        for (int h = 0; h < NH; ++h) {
+          dot[h] = fmaf(kk.x, s_q[h][4 * c + 0], dot[h]);
+          dot[h] = fmaf(kk.y, s_q[h][4 * c + 1], dot[h]);
+          dot[h] = fmaf(kk.z, s_q[h][4 * c + 2], dot[h]);
+          dot[h] = fmaf(kk.w, s_q[h][4 * c + 3], dot[h]);
         }
       }
     }
 #pragma unroll
-    for (int h = 0; h < kMaxHeads; ++h)
-      if (h < nh) s_p[h][i] = dot[h] * a.scale_log2;
+    for (int h = 0; h < NH; ++h) s_p[h][i] = dot[h] * a.scale_log2;
   }
   __syncthreads();
 
   // phase 2: per-head max and exponentials (log2 domain)
-  float m[kMaxHeads], l[kMaxHeads];
+  float m[NH], l[NH];
 #pragma unroll
-  for (int h = 0; h < kMaxHeads; ++h) {
-    m[h] = -INFINITY;
-    l[h] = 0.f;
-    if (h < nh) {
-      float mx = -INFINITY;
-      for (int i = lane; i < n; i += 64) mx = fmaxf(mx, s_p[h][i]);
-      mx = wave_max(mx);
-      const float mu = (mx == -INFINITY) ? 0.f : mx;
-      float sum = 0.f;
-      for (int i = lane; i < n; i += 64) {
-        const float p = __builtin_amdgcn_exp2f(s_p[h][i] - mu);
-        s_p[h][i] = p;
-        sum += p;
-      }
-      m[h] = mx;
-      l[h] = wave_sum(sum);
+  for (int h = 0; h < NH; ++h) {
+    float mx = -INFINITY;
+    for (int i = lane; i < n; i += 64) mx = fmaxf(mx, s_p[h][i]);
+    mx = wave_max(mx);
+    const float mu = (mx == -INFINITY) ? 0.f : mx;
+    float sum = 0.f;
+    for (int i = lane; i < n; i += 64) {
+      const float p = __builtin_amdgcn_exp2f(s_p[h][i] - mu);
+      s_p[h][i] = p;
+      sum += p;
     }
+    m[h] = mx;
+    l[h] = wave_sum(sum);
   }
   __syncthreads();
 
   // phase 3: weighted values; lane owns dims lane*PER .. +PER
-  float acc[kMaxHeads][PER];
+  float acc[NH][PER];
 #pragma unroll
-  for (int h = 0; h < kMaxHeads; ++h)
+  for (int h = 0; h < NH; ++h)
 #pragma unroll
     for (int e = 0; e < PER; ++e) acc[h][e] = 0.f;
-  // 16 tokens per batch: their value loads are all in flight together
-  constexpr int kBatch = 16;
+  // 32 tokens per batch (16 when many heads' accumulators fill the
+  // registers), their value loads all in flight together: every load is
+  // issued (a token past the end, or on a block outside the pool -- flagged
+  // in phase 1 -- reads block 0 and its value is then zeroed), so no branch
+  // separates them
+  constexpr int kBatch = NH * PER >= 16 ? 16 : 32;
   for (int i0 = 0; i0 < n; i0 += kBatch) {
     float v[kBatch][PER];
 #pragma unroll
     for (int k = 0; k < kBatch; ++k) {
       const int i = i0 + k;
       const int phys = i < n ? s_phys[i] : -1;
+      const bool ok = phys >= 0 && phys < a.NB;
+      const float* vr = vbase + (static_cast<int64_t>(ok ? phys : 0) * B + (t_begin + i) % B) * row +
+                        lane * PER;
 #pragma unroll
-      for (int e = 0; e < PER; ++e) v[k][e] = 0.f;
-      if (phys >= 0 && phys < a.NB) {  // a bad block was flagged in phase 1
-        const float* vr = vbase + (static_cast<int64_t>(phys) * B + (t_begin + i) % B) * row + lane * PER;
+      for (int e = 0; e < PER; ++e) v[k][e] = vr[e];
 #pragma unroll
-        for (int e = 0; e < PER; ++e) v[k][e] = vr[e];
-      }
+      for (int e = 0; e < PER; ++e) v[k][e] = ok ? v[k][e] : 0.f;
     }
+    // tokens past the end have zero values (and weights never read past n)
 #pragma unroll
     for (int k = 0; k < kBatch; ++k) {
-      if (i0 + k >= n) break;
 #pragma unroll
-      for (int h = 0; h < kMaxHeads; ++h)
-        if (h < nh) {
-          const float p = s_p[h][i0 + k];
+      for (int h = 0; h < NH; ++h) {
+        const float p = i0 + k < n ? s_p[h][i0 + k] : 0.f;
 #pragma unroll
-          for (int e = 0; e < PER; ++e) acc[h][e] = fmaf(p, v[k][e], acc[h][e]);
-        }
+        for (int e = 0; e < PER; ++e) acc[h][e] = fmaf(p, v[k][e], acc[h][e]);
+      }
     }
   }
 
@@ -148,7 +147,7 @@ __global__ void __launch_bounds__(64) attention_f32_kernel(AttnArgs a) {
   // without a workspace (one partition per sequence) results always go to out
   const bool single = nparts == 1 || a.max_parts == 1;
 #pragma unroll
-  for (int h = 0; h < kMaxHeads; ++h) {
+  for (int h = 0; h < NH; ++h) {
     if (h >= nh) continue;
     const float inv = l[h] > 0.f ? 1.f / l[h] : 0.f;
     const int hq = h0 + h;
@@ -185,13 +184,29 @@ int launch_attention_f32(const AttnArgs& a, hipStream_t stream) {
   const int G = a.Hq / a.Hkv;
   const int chunks = (G + kMaxHeads - 1) / kMaxHeads;
   dim3 grid(a.max_parts, a.Hkv * chunks, a.S);
-  if (a.D == 64) {
-    attention_f32_kernel<64><<<grid, dim3(64), 0, stream>>>(a);
-  } else if (a.D == 128) {
-    attention_f32_kernel<128><<<grid, dim3(64), 0, stream>>>(a);
-  } else {
+  if (a.D != 64 && a.D != 128) {
     set_error("paged attention (fp32): head_size %d is not built", a.D);
     return PKV_ERR_UNSUPPORTED;
+  }
+  const int nh = G < kMaxHeads ? G : kMaxHeads;
+  const int NH = nh <= 1 ? 1 : nh <= 2 ? 2 : nh <= 4 ? 4 : nh <= 8 ? 8 : 16;
+  auto go = [&](auto kern) { kern<<<grid, dim3(64), 0, stream>>>(a); };
+  if (a.D == 64) {
+    switch (NH) {
+      case 1: go(attention_f32_kernel<64, 1>); break;
+      case 2: go(attention_f32_kernel<64, 2>); break;
+      case 4: go(attention_f32_kernel<64, 4>); break;
+      case 8: go(attention_f32_kernel<64, 8>); break;
+      default: go(attention_f32_kernel<64, 16>); break;
+    }
+  } else {
+    switch (NH) {
+      case 1: go(attention_f32_kernel<128, 1>); break;
+      case 2: go(attention_f32_kernel<128, 2>); break;
+      case 4: go(attention_f32_kernel<128, 4>); break;
+      case 8: go(attention_f32_kernel<128, 8>); break;
+      default: go(attention_f32_kernel<128, 16>); break;
+    }
   }
   return check_launch("paged attention (fp32)");
 }

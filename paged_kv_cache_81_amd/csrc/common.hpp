@@ -58,6 +58,10 @@ int launch_slot_mapping(int64_t* slot_mapping, const int32_t* tables, int width,
                         int NB, hipStream_t stream);
 int launch_write(const void* key, const void* value, void* kv, const int64_t* slots, int T, int NB,
                  int B, int Hkv, int D, int elem_bytes, hipStream_t stream);
+int launch_write_positions(const void* key, const void* value, void* kv, const int32_t* tables,
+                           int width, const int32_t* seq_ids, const int32_t* positions,
+                           int64_t* slots_out, int T, int S, int NB, int B, int Hkv, int D,
+                           int elem_bytes, hipStream_t stream);
 int launch_copy_blocks(void* dst, int dst_nb, const void* src, int src_nb, const int32_t* src_ids,
                        const int32_t* dst_ids, int n, int64_t half_bytes, hipStream_t stream);
 int launch_gather(void* k_out, void* v_out, const void* kv, const int32_t* tables, int width,

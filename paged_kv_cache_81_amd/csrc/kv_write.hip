@@ -46,6 +46,38 @@ __global__ void __launch_bounds__(256) write_kernel(
   kv[num_slots * chunks + dst] = vv;
 }
 
+// Slot derivation and write in one pass: thread (t, c) finds token t's slot
+// from its table and position (as slot_mapping_kernel does) and moves piece c
+// of its K and V; the thread with c == 0 also records the slot.
+__global__ void __launch_bounds__(256) write_positions_kernel(
+    const uint4* __restrict__ key, const uint4* __restrict__ value, uint4* __restrict__ kv,
+    const int32_t* __restrict__ tables, int width, const int32_t* __restrict__ seq_ids,
+    const int32_t* __restrict__ positions, int64_t* __restrict__ slots_out, int64_t total,
+    int chunks, int S, int B, int NB) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= total) return;
+  const int64_t t = i / chunks;
+  const int64_t c = i - t * chunks;
+  const int s = seq_ids ? seq_ids[t] : static_cast<int>(t);
+  const int p = positions[t];
+  int64_t slot = -1;
+  if (p >= 0 && s >= 0 && s < S) {
+    const int lb = p / B;
+    if (lb < width) {
+      const int phys = tables[static_cast<int64_t>(s) * width + lb];
+      if (phys >= 0 && phys < NB) slot = static_cast<int64_t>(phys) * B + (p - lb * B);
+    }
+  }
+  if (slots_out && c == 0) slots_out[t] = slot;
+  if (slot < 0) return;
+  const int64_t num_slots = static_cast<int64_t>(NB) * B;
+  const int64_t dst = slot * chunks + c;
+  const uint4 kk = key[i];
+  const uint4 vv = value[i];
+  kv[dst] = kk;
+  kv[num_slots * chunks + dst] = vv;
+}
+
 __global__ void __launch_bounds__(256) gather_kernel(
     uint4* __restrict__ k_out, uint4* __restrict__ v_out, const uint4* __restrict__ kv,
     const int32_t* __restrict__ tables, int width, const int32_t* __restrict__ lens, int B,
@@ -96,6 +128,19 @@ int launch_write(const void* key, const void* value, void* kv, const int64_t* sl
       static_cast<const uint4*>(key), static_cast<const uint4*>(value), static_cast<uint4*>(kv),
       slots, total, chunks, static_cast<int64_t>(NB) * B);
   return check_launch("kv write");
+}
+
+int launch_write_positions(const void* key, const void* value, void* kv, const int32_t* tables,
+                           int width, const int32_t* seq_ids, const int32_t* positions,
+                           int64_t* slots_out, int T, int S, int NB, int B, int Hkv, int D,
+                           int elem_bytes, hipStream_t stream) {
+  if (T == 0) return PKV_OK;
+  const int chunks = Hkv * D * elem_bytes / 16;
+  const int64_t total = static_cast<int64_t>(T) * chunks;
+  write_positions_kernel<<<dim3(static_cast<unsigned>(cdiv64(total, 256))), dim3(256), 0, stream>>>(
+      static_cast<const uint4*>(key), static_cast<const uint4*>(value), static_cast<uint4*>(kv),
+      tables, width, seq_ids, positions, slots_out, total, chunks, S, B, NB);
+  return check_launch("kv write (positions)");
 }
 
 int launch_gather(void* k_out, void* v_out, const void* kv, const int32_t* tables, int width,

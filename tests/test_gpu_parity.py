@@ -71,6 +71,51 @@ def test_slot_mapping_and_write_exact(name):
     assert np.array_equal(got, ref_kv), "pool differs from the oracle's write"
 
 
+@pytest.mark.parametrize("name", NAMES)
+def test_write_positions_exact(name):
+    """Slot derivation and write in one launch: the same pool, bit for bit,
+    and the same slots as the oracle's slot mapping and write."""
+    w = full(name)
+    say(f"[write positions] {name}: S={w.num_seqs} cached={w.cached_k.shape[0]}")
+    ref_kv, ref_cached, ref_new = oracle_pool(w)
+    st = H.upload(w, fill=False, step=False)
+    dev = st.kv.device
+    slots = torch.empty(w.cached_k.shape[0], dtype=torch.int64, device=dev)
+    pkv.write_positions(H.to_torch(w.cached_k, w.dtype, dev), H.to_torch(w.cached_v, w.dtype, dev),
+                        st.kv, st.tables, torch.from_numpy(w.cached_pos).to(dev),
+                        seq_ids=torch.from_numpy(w.cached_seq).to(dev), slot_mapping=slots)
+    assert np.array_equal(slots.cpu().numpy(), ref_cached)
+    new = torch.empty(w.num_seqs, dtype=torch.int64, device=dev)
+    pkv.write_positions(st.new_k, st.new_v, st.kv, st.tables, st.new_pos, slot_mapping=new)
+    assert np.array_equal(new.cpu().numpy(), ref_new)
+    got = H.to_numpy(st.kv)
+    if w.dtype == "f32":
+        got, ref_kv = got.view(np.uint32), ref_kv.view(np.uint32)
+    assert np.array_equal(got, ref_kv), "pool differs from the oracle's write"
+
+
+def test_write_positions_edge_cases():
+    """Tokens whose slot is -1 (negative position, entry out of range,
+    sequence absent, block past the table) write nothing."""
+    dev = torch.device("cuda:0")
+    tables = torch.tensor([[3, 5, -2**31], [7, -1, 99]], dtype=torch.int32, device=dev)
+    seq = torch.tensor([0, 0, 0, 1, 1, 1, 2, -1, 0, 0], dtype=torch.int32, device=dev)
+    pos = torch.tensor([0, 17, -1, 15, 16, 40, 0, 0, 48, 20], dtype=torch.int32, device=dev)
+    kv = torch.full((2, 10, 16, 2, 64), float("nan"), dtype=torch.bfloat16, device=dev)
+    k = torch.randn((10, 2, 64), device=dev).to(torch.bfloat16)
+    v = torch.randn((10, 2, 64), device=dev).to(torch.bfloat16)
+    slots = torch.empty(10, dtype=torch.int64, device=dev)
+    pkv.write_positions(k, v, kv, tables, pos, seq_ids=seq, slot_mapping=slots)
+    assert slots.cpu().tolist() == [48, 81, -1, 127, -1, -1, -1, -1, -1, 84]
+    ref = torch.full_like(kv, float("nan"))
+    flat = ref.view(2, 160, 2, 64)
+    for t, sl in enumerate(slots.cpu().tolist()):
+        if sl >= 0:
+            flat[0, sl] = k[t]
+            flat[1, sl] = v[t]
+    assert torch.equal(kv.view(torch.int16), ref.view(torch.int16))
+
+
 def test_slot_mapping_edge_cases():
     dev = torch.device("cuda:0")
     tables = torch.tensor([[3, 5, -2**31], [7, -1, 99]], dtype=torch.int32, device=dev)
