@@ -305,10 +305,23 @@ prefill_bf16_kernel(PrefillArgs a) {
     if (nsteps > 1) load_table(1);
     stage(lds, kend);
   }
+  // The query fragments arrive before the loop: otherwise the compiler,
+  // allowing for their loads still being in flight on the first pass, makes
+  // every step's first score wait for the oldest K/V loads of the next step.
+#pragma unroll
+  for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+    for (int c = 0; c < QC; ++c) asm volatile("" : "+v"(qf[cb][c]));
   __syncthreads();
   for (int q = 0; q < nsteps; ++q) {
     const char* cur = lds + (q & 1) * Gm::BUF;
-    if (q + 1 < nsteps) issue();
+    // The next step's loads are issued on every pass, the last included (its
+    // table entries are stale but in the pool, and nothing stages them): a
+    // path skipping them left the table loads possibly pending where the
+    // paths meet, and the compiler then waited for every outstanding load --
+    // these K/V loads too -- before the next table loads, so they never
+    // overlapped the computation.
+    issue();
     if (q + 2 < nsteps) load_table(q + 2);
     const int k0 = q * kPKeys;
     // keys past every row of the wave need no work; a step reaching past
