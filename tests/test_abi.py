@@ -116,3 +116,55 @@ def test_host_checks_reject_bad_arguments(lib):
     assert lib.paged_kv_write(None, p, p, p, 4, 10, 16, 2, 128, BF16, None) == -1
     assert lib.paged_kv_slot_mapping(p, p, 0, None, p, 4, 4, 16, 10, None) == -1
     assert lib.paged_kv_gather(p, p, p, p, 4, p, 2, 2, 128, 16, 10, 64, 7, None) == -1
+
+
+def test_shared_prefix_host_checks(lib):
+    """Argument checks of the shared-prefix decode and the fused write, all
+    made before anything is launched."""
+    p = ctypes.c_void_p(0x1000)  # never dereferenced: the checks fail first
+    F32, BF16 = 0, 1
+    args = dict(out=p, out_dtype=0, query=p, kv=p, tables=p, width=4, lens=p, gs=p, pl=p, ng=2,
+                S=4, Hq=8, Hkv=2, D=128, B=16, NB=10, scale=0.1, max_len=64, max_prefix=32, P=0,
+                ws=p, ws_bytes=1 << 30, dtype=BF16, flags=0, stream=None)
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return lib.paged_attention_decode_shared(
+            a["out"], a["out_dtype"], a["query"], a["kv"], a["tables"], a["width"], a["lens"],
+            a["gs"], a["pl"], a["ng"], a["S"], a["Hq"], a["Hkv"], a["D"], a["B"], a["NB"],
+            a["scale"], a["max_len"], a["max_prefix"], a["P"], a["ws"], a["ws_bytes"], a["dtype"],
+            a["flags"], a["stream"])
+    assert call(dtype=F32) == -2                # bf16 only
+    assert call(D=96) == -2
+    assert call(B=12) == -2
+    assert call(S=600) == -2                    # more than 512 sequences
+    assert call(Hq=7) == -1
+    assert call(ng=0) == -1 and call(ng=5) == -1   # 1 <= groups <= sequences
+    assert call(gs=None) == -1 and call(pl=None) == -1
+    assert call(max_prefix=-1) == -1
+    assert call(P=48) == -1                     # not a multiple of 32
+    assert call(ws_bytes=16) == -3
+    assert call(flags=2) == -1
+    assert call(out=ctypes.c_void_p(0x1004)) == -1
+    assert call(S=0) == 0
+    # the automatic partition is a multiple of the unit; a request is checked
+    assert lib.paged_attention_shared_partition_size(256, 32, 8, 128, 16, 32, 1024, 512) == 512
+    assert lib.paged_attention_shared_partition_size(256, 32, 8, 128, 64, 32, 1024, 96) == -1
+    assert lib.paged_attention_shared_partition_size(8, 8, 2, 128, 16, 8, 0, 0) == 256
+    # workspace: parts = ceil(prefix / P) + ceil(len / P), [parts][S][Hq][D] floats,
+    # their (m, l), then int32 [4][S]
+    S, Hq, D, L, Lp, P = 8, 8, 128, 1000, 512, 256
+    parts = 2 + 4
+    up = lambda b: (b + 255) // 256 * 256
+    want = up(parts * S * Hq * D * 4) + up(parts * S * Hq * 8) + up(4 * S * 4)
+    assert lib.paged_attention_shared_workspace_bytes(S, Hq, 2, D, 16, 2, L, Lp, P) == want
+
+    # the fused slot derivation + write
+    assert lib.paged_kv_write_positions(p, p, p, p, 4, None, p, None, 0, 4, 10, 16, 2, 128, BF16,
+                                        None) == 0
+    assert lib.paged_kv_write_positions(p, p, p, p, 4, None, p, None, 4, 4, 10, 16, 2, 4, BF16,
+                                        None) == -2
+    assert lib.paged_kv_write_positions(p, p, p, None, 4, None, p, None, 4, 4, 10, 16, 2, 128,
+                                        BF16, None) == -1
+    assert lib.paged_kv_write_positions(p, p, p, p, 0, None, p, None, 4, 4, 10, 16, 2, 128, BF16,
+                                        None) == -1
