@@ -90,10 +90,11 @@ def _is_prefill(workload: str) -> bool:
     return workload.startswith("prefill_")
 
 
-def measured_traffic(workload: str, block_size=None):
+def measured_traffic(workload: str, block_size=None, kernel=None):
     """HBM bytes per attention launch from the committed rocprofv3 counter
-    summary, if it was taken on the current kernel source and block size;
-    else None."""
+    summary, if it was taken on the current kernel source and block size (and
+    on the kernel named, e.g. "attention_bf16_stream_kernel<128,16>"); else
+    None."""
     path = os.path.join(ROOT, "profiles", "attention_traffic.json")
     if not os.path.exists(path):
         return None
@@ -103,6 +104,8 @@ def measured_traffic(workload: str, block_size=None):
     if not rec or rec.get("kernel_source_sha") != kernel_source_sha(sources):
         return None
     if block_size is not None and rec.get("block_size", block_size) != block_size:
+        return None
+    if kernel is not None and kernel.split("<")[0] + "<" not in rec.get("kernel", ""):
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -765,7 +768,7 @@ def main() -> int:
     kname = (f"attention_f32_kernel<{D}>" if not dt else
              f"attention_bf16_shared_kernel<{D},{B}>" if grouped else
              f"attention_bf16_stream_kernel<{D},{B}>" if P == 0 else f"attention_bf16_kernel<{D},{B}>")
-    traffic = measured_traffic(w.name, B)
+    traffic = measured_traffic(w.name, B, kname)
 
     result = {
         "metric": METRIC,

@@ -155,6 +155,11 @@ def _check_rows(got, ref, tol, what):
     assert worst <= tol, f"{what}: worst row rel err {worst:.3e} > {tol}"
 
 
+# fixed partition sizes checked besides the library's choice: the
+# long-context shape's natural split into 512-token partitions
+EXTRA_PARTITIONS = {"long_context": (512,)}
+
+
 @pytest.mark.parametrize("name", NAMES)
 def test_attention_small_full_oracle(name):
     w = SMALL[name]()
@@ -162,19 +167,21 @@ def test_attention_small_full_oracle(name):
     ref = oracle.paged_attention_ref(w.query, ref_kv, w.block_tables, w.context_lens, w.scale, w.dtype)
     st = H.upload(w)
     unit = 32 if w.block_size <= 32 else w.block_size
-    for P in sorted({w.partition_size, unit, 2 * unit, 0}):
+    for P in sorted({w.partition_size, unit, 2 * unit, 0, *EXTRA_PARTITIONS.get(name, ())}):
         got = H.attend(st, partition_size=P).cpu().numpy()
         _check_rows(got, ref, H.tolerance(w), f"{name} P={P}")
 
 
 @pytest.mark.parametrize("name", NAMES)
 def test_attention_full_size_sampled(name):
-    """Full-size workload in the benchmark's launch configuration; the oracle
-    computes a sample of sequences (longest, shortest, and random ones)."""
+    """Full-size workload in the benchmark's launch configuration (and at the
+    extra fixed partition sizes); the oracle computes a sample of sequences
+    (longest, shortest, and random ones)."""
     w = full(name)
     say(f"[attention] {name}: S={w.num_seqs} max_len={w.max_context_len}")
     st = H.upload(w)
-    got = H.attend(st).cpu().numpy()
+    outs = {P: H.attend(st, partition_size=P).cpu().numpy()
+            for P in (w.partition_size, *EXTRA_PARTITIONS.get(name, ()))}
     rng = np.random.default_rng(0)
     L = w.context_lens
     sample = sorted({int(np.argmax(L)), int(np.argmin(L)),
@@ -183,8 +190,10 @@ def test_attention_full_size_sampled(name):
         k, v = w.logical_kv(s)
         ref = oracle.attention_ref(oracle.to_f64(w.query[s], w.dtype), oracle.to_f64(k, w.dtype),
                                    oracle.to_f64(v, w.dtype), w.scale)
-        _check_rows(got[s], ref, H.tolerance(w), f"{name} seq {s} (L={L[s]})")
-    assert np.all(np.isfinite(got))
+        for P, got in outs.items():
+            _check_rows(got[s], ref, H.tolerance(w), f"{name} P={P} seq {s} (L={L[s]})")
+    for got in outs.values():
+        assert np.all(np.isfinite(got))
 
 
 EDGE_LENS = [0, 1, 2, 15, 16, 17, 31, 32, 33, 63, 64, 65, 511, 512, 513, 1024, 1025, 1500]

@@ -103,5 +103,5 @@ def test_opt13b_reduced(kw):
 
 def test_long_context_reduced():
     w = workloads.long_context(num_seqs=2, context_len=2048)
-    assert w.num_blocks == 2 * 64 and w.block_size == 32 and w.partition_size == 512
+    assert w.num_blocks == 2 * 64 and w.block_size == 32 and w.partition_size == 0
     _check_structure(w)

@@ -336,8 +336,12 @@ def shared_prefix(seed: int = 81003, num_prompts: int = 32, prompt_len: int = 10
 
 
 def long_context(seed: int = 81004, num_seqs: int = 16, context_len: int = 32768,
-                 partition_size: int = 512) -> Workload:
-    """16 sequences of 32768 tokens, GQA 64/8, D 128, B 32, bf16, fully shuffled pool."""
+                 partition_size: int = 0) -> Workload:
+    """16 sequences of 32768 tokens, GQA 64/8, D 128, B 32, bf16, fully shuffled pool.
+
+    The natural split is 64 partitions of 512 tokens per sequence
+    (``partition_size=512``); by default the library chooses, which on this
+    shape is the balanced stream schedule."""
     rng = np.random.Generator(np.random.PCG64(seed))
     lens = np.full(num_seqs, context_len, dtype=np.int64)
     needed = int(_blocks_to_hold(lens, 32).sum())
