@@ -17,7 +17,7 @@
 // Work items are numbered group by group (prefix items first, then suffix
 // items sequence by sequence); a persistent grid of resident workgroups walks
 // them, HG waves (adjacent kv heads, reading each token as HG*D*2 contiguous
-// bytes) per item.  The column blocks of one prefix partition are numbered
+// bytes) per item, round by round, every other round in reverse.  The column blocks of one prefix partition are numbered
 // next to each other and placed on the same XCD, so the second reads the
 // shared rows from that XCD's L2.
 #include "attention_bf16_wave.hpp"
@@ -249,7 +249,13 @@ attention_bf16_shared_kernel(AttnArgs a) {
 
   Wv w;
   w.init(a, reinterpret_cast<char*>(wave_lds));
-  for (int it = b * NSLOT + slot; it < total; it += nwg * NSLOT) {
+  // Items are dealt out in rounds of one per item slot of the grid; odd
+  // rounds are dealt in reverse, so the slots that drew the long prefix items
+  // (which come first) draw the short items at the end of the next round.
+  const int stride = nwg * NSLOT;
+  for (int it0 = b * NSLOT + slot, round = 0; it0 < total + stride; it0 += stride, ++round) {
+    const int it = (round & 1) ? (2 * round + 1) * stride - 1 - it0 : it0;
+    if (it >= total) continue;
     int part, seq, kvh, hbase, t0, t1, nh, col0, tab;
     int64_t qrow;
     if (it < t_pre) {
