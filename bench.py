@@ -50,6 +50,7 @@ DEFAULT_LAYERS = {"opt13b_mha": 40, "qwen2_gqa": 24, "shared_prefix": 8, "long_c
 KERNEL_SOURCES = ["paged_kv_cache_81_amd/csrc/api.hip",
                   "paged_kv_cache_81_amd/csrc/attention_bf16.hip",
                   "paged_kv_cache_81_amd/csrc/attention_bf16_stream.hip",
+                  "paged_kv_cache_81_amd/csrc/attention_bf16_shared.hip",
                   "paged_kv_cache_81_amd/csrc/attention_bf16_wave.hpp",
                   "paged_kv_cache_81_amd/csrc/attention_f32.hip",
                   "paged_kv_cache_81_amd/csrc/common.hpp"]
