@@ -2,9 +2,12 @@
 """One-GPU benchmark of the paged decode step.
 
 A step is one pass of the whole hot path over one batch for one attention
-layer: the slot of each sequence's new token (slot mapping) and the KV write
-(one launch, paged_kv_write_positions), the attention pass over the paged
-cache and the log-sum-exp merge of context partitions.  A model has many layers, each with its own cache pool indexed by
+layer: the slot of each sequence's new token (slot mapping) and the KV write,
+the attention pass over the paged cache and the log-sum-exp merge of context
+partitions.  The write goes into the attention launch
+(paged_attention_append_partitions) where every sequence appends a token;
+otherwise, or with ``--separate-write``, it is a launch of its own
+(paged_kv_write_positions).  A model has many layers, each with its own cache pool indexed by
 the same block tables; consecutive steps here cycle through ``--layers`` such
 pools, as the layers of a decode step do, so no step finds its K/V still in a
 cache from the previous one.  Inputs are resident in HBM before timing starts;
@@ -503,6 +506,9 @@ def main() -> int:
                     help="derive the new tokens' slots and write their K/V in two launches "
                          "(paged_kv_slot_mapping, paged_kv_write) instead of one "
                          "(paged_kv_write_positions)")
+    ap.add_argument("--separate-write", action="store_true",
+                    help="write the new tokens in a launch of their own (paged_kv_write_positions) "
+                         "instead of inside the attention launch")
     ap.add_argument("--no-shared-prefix", action="store_true",
                     help="forked workloads: read the shared prompt per sequence (the ordinary "
                          "decode) instead of once per group")
@@ -604,6 +610,16 @@ def main() -> int:
         log(f"[bench] shared-prefix decode: {n_groups} groups, longest prefix {g_maxp}, "
             f"partition {P}")
 
+    # the write goes into the attention launch (paged_attention_append_partitions)
+    # when every sequence's new token sits at its last position, the library
+    # stores it inside that launch for this batch, and the separate launches
+    # were not asked for
+    fused_write = (not grouped and not args.separate_write and not args.separate_slot_mapping
+                   and bool(np.all(w.new_pos == np.where(w.context_lens > 0,
+                                                         w.context_lens - 1, -1)))
+                   and lib.paged_attention_append_in_launch(S, Hq, Hkv, D, B, w.max_context_len,
+                                                            P, dt) == 1)
+
     # one cache pool per layer, all indexed by the same block tables
     nl = args.layers if args.layers is not None else DEFAULT_LAYERS.get(w.name, 4)
     free, _ = torch.cuda.mem_get_info(dev)
@@ -647,6 +663,14 @@ def main() -> int:
         attn_a = (out.data_ptr(), 0, st.query.data_ptr(), kv.data_ptr(), st.tables.data_ptr(),
                   w.table_width, st.lens.data_ptr(), S, Hq, Hkv, D, B, NB, w.scale,
                   w.max_context_len, P, ws.data_ptr(), ws.numel(), dt, flags, stream_handle)
+        if fused_write:
+            # each sequence's new token is written by the attention launch itself
+            app_a = attn_a[:3] + (st.new_k.data_ptr(), st.new_v.data_ptr()) + attn_a[3:]
+            return {
+                "attention": lambda: check(lib.paged_attention_append_partitions(*app_a),
+                                           "attention (with the write)"),
+                "merge": lambda: check(lib.paged_attention_merge(*attn_a), "merge"),
+            }
         return {
             **write_step,
             "attention": lambda: check(lib.paged_attention_partitions(*attn_a), "attention"),
@@ -801,6 +825,8 @@ def main() -> int:
             "kv_flags": "cached" if flags & lib_mod.PKV_ATTN_CACHED_KV else "streamed",
             "attention_path": ("shared prefix (groups read their prompt once)" if grouped else
                                "per sequence"),
+            "kv_write": ("inside the attention launch" if fused_write else
+                         "separate launch" + ("es" if args.separate_slot_mapping else "")),
             **({"groups": n_groups, "max_prefix_len": g_maxp} if grouped else {}),
         },
         "roofline": {

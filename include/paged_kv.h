@@ -256,6 +256,62 @@ int paged_attention_merge(void* out, pkv_dtype out_dtype, const void* query,
                           hipStream_t stream);
 
 /*
+ * paged_attention_decode_append -- a whole decode step in one call: each
+ * sequence's newly generated key and value are stored into its KV block
+ * (studying-code.tistory.com vLLM review, section "디코딩 과정" (decoding)) and
+ * its query attends over all its tokens, the new one included (section
+ * "PagedAttention").  Sequence s with context_lens[s] >= 1 appends key[s] and
+ * value[s] at position context_lens[s] - 1, in the slot
+ *     table[s][(L - 1) / B] * B + (L - 1) % B            (L = context_lens[s])
+ * (itan.pw walk-through, "ブロックアロケーションの基本概念", slot_mapping; the
+ * same -1 cases as paged_kv_write_positions: nothing is written), then
+ * everything is as paged_attention_decode.  Cache and output are
+ * bit-identical to paged_kv_write_positions (positions L - 1) followed by
+ * paged_attention_decode.  Under the stream schedule, when few of its pieces
+ * hold a sequence's last step, the write happens inside the attention launch
+ * (the wave that reads a sequence's last step stores the new row first, then
+ * reads it back like the rest: one launch less); otherwise the library
+ * launches the write first.  Sequences whose last token is
+ * already cached (e.g. a fork still on its shared prompt) must use the
+ * separate calls.
+ *
+ *   key, value    dtype [num_seqs][num_kv_heads][head_size], 16-byte aligned
+ *   kv_cache      dtype [2][num_blocks][block_size][num_kv_heads][head_size]   (in/out)
+ *   other arguments as paged_attention_decode (same workspace size)
+ */
+int paged_attention_decode_append(void* out, pkv_dtype out_dtype, const void* query,
+                                  const void* key, const void* value, void* kv_cache,
+                                  const int32_t* block_tables, int table_width,
+                                  const int32_t* context_lens, int num_seqs, int num_q_heads,
+                                  int num_kv_heads, int head_size, int block_size, int num_blocks,
+                                  float scale, int max_context_len, int partition_size,
+                                  void* workspace, size_t workspace_bytes, pkv_dtype dtype,
+                                  unsigned flags, hipStream_t stream);
+
+/*
+ * Whether paged_attention_decode_append with these arguments stores the new
+ * tokens inside its attention launch (1) or launches the write first (0);
+ * -1 for inconsistent head counts or when the device cannot be queried.
+ * Needs the device the call will run on to be current.  Host only.
+ */
+int paged_attention_append_in_launch(int num_seqs, int num_q_heads, int num_kv_heads,
+                                     int head_size, int block_size, int max_context_len,
+                                     int partition_size, pkv_dtype dtype);
+
+/*
+ * The attention pass of paged_attention_decode_append alone (with the write);
+ * follow it with paged_attention_merge given the same decode arguments.
+ */
+int paged_attention_append_partitions(void* out, pkv_dtype out_dtype, const void* query,
+                                      const void* key, const void* value, void* kv_cache,
+                                      const int32_t* block_tables, int table_width,
+                                      const int32_t* context_lens, int num_seqs, int num_q_heads,
+                                      int num_kv_heads, int head_size, int block_size,
+                                      int num_blocks, float scale, int max_context_len,
+                                      int partition_size, void* workspace, size_t workspace_bytes,
+                                      pkv_dtype dtype, unsigned flags, hipStream_t stream);
+
+/*
  * paged_attention_prefix_groups -- find groups of consecutive sequences that
  * share their first blocks.  HOST pointers; host only.
  *

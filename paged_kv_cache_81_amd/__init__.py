@@ -19,6 +19,7 @@ import torch
 from ._lib import PKV_ATTN_CACHED_KV, PKV_BF16, PKV_F32, PagedKVError, check, lib
 
 __all__ = ["slot_mapping", "write", "gather", "copy_blocks", "partition_size", "workspace_bytes",
+           "attention_decode_append", "attention_append_partitions",
            "attention_decode", "attention_partitions", "attention_merge", "attention_prefill",
            "PagedKVError"]
 
@@ -273,6 +274,43 @@ def attention_merge(*a, **k) -> torch.Tensor:
     """Second launch of attention_decode (log-sum-exp merge); same arguments."""
     out, args = _decode_args(*_norm(*a, **k))
     check(lib.paged_attention_merge(*args), "paged_attention_merge")
+    return out
+
+
+def _append_args(key, value, query, kv_cache, args):
+    """Decode arguments with the new tokens' key and value inserted."""
+    shape = (query.shape[0], kv_cache.shape[3], kv_cache.shape[4])
+    for t, name in ((key, "key"), (value, "value")):
+        _need(t, name, kv_cache.dtype, 3, kv_cache.device)
+        if tuple(t.shape) != shape:
+            raise ValueError(f"{name} must be [S, Hkv, D] = {list(shape)}")
+    return args[:3] + (key.data_ptr(), value.data_ptr()) + args[3:]
+
+
+def attention_decode_append(query: torch.Tensor, key: torch.Tensor, value: torch.Tensor,
+                            kv_cache: torch.Tensor, block_tables: torch.Tensor,
+                            context_lens: torch.Tensor, scale: float, max_context_len: int,
+                            partition_size: int = 0, out: Optional[torch.Tensor] = None,
+                            out_dtype: torch.dtype = torch.float32,
+                            workspace: Optional[torch.Tensor] = None,
+                            shared_blocks: bool = False) -> torch.Tensor:
+    """A decode step in one call: sequence s's new ``key[s]``/``value[s]``
+    ([S, Hkv, D]) go to position ``context_lens[s] - 1`` of its blocks, then
+    its query attends over all its tokens.  Returns ``out`` [S, Hq, D]."""
+    out, args = _decode_args(query, kv_cache, block_tables, context_lens, scale, max_context_len,
+                             partition_size, out, out_dtype, workspace, shared_blocks)
+    check(lib.paged_attention_decode_append(*_append_args(key, value, query, kv_cache, args)),
+          "paged_attention_decode_append")
+    return out
+
+
+def attention_append_partitions(query, key, value, *a, **k) -> torch.Tensor:
+    """First launch of attention_decode_append (write + attention pass); follow it
+    with attention_merge given the same decode arguments."""
+    n = _norm(query, *a, **k)
+    out, args = _decode_args(*n)
+    check(lib.paged_attention_append_partitions(*_append_args(key, value, query, n[1], args)),
+          "paged_attention_append_partitions")
     return out
 
 

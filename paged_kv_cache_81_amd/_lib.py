@@ -41,6 +41,11 @@ SIGNATURES = {
                                         _i, _i, _p, _sz, _i, _u, _p]),
     "paged_attention_merge": (_i, [_p, _i, _p, _p, _p, _i, _p, _i, _i, _i, _i, _i, _i, _f,
                                    _i, _i, _p, _sz, _i, _u, _p]),
+    "paged_attention_append_in_launch": (_i, [_i, _i, _i, _i, _i, _i, _i, _i]),
+    "paged_attention_decode_append": (_i, [_p, _i, _p, _p, _p, _p, _p, _i, _p, _i, _i, _i, _i,
+                                           _i, _i, _f, _i, _i, _p, _sz, _i, _u, _p]),
+    "paged_attention_append_partitions": (_i, [_p, _i, _p, _p, _p, _p, _p, _i, _p, _i, _i, _i,
+                                               _i, _i, _i, _f, _i, _i, _p, _sz, _i, _u, _p]),
     "paged_attention_prefix_groups": (_i, [_p, _i, _p, _i, _i, _i, _p, _p, _p, _p]),
     "paged_attention_shared_partition_size": (_i, [_i, _i, _i, _i, _i, _i, _i, _i]),
     "paged_attention_shared_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i, _i, _i, _i]),

@@ -142,6 +142,17 @@ bool uses_stream(int S, int Hq, int Hkv, int max_len, int req, pkv_dtype dtype) 
   return steps < (int64_t{1} << 31);
 }
 
+// Under the stream schedule, new tokens are stored by the attention launch
+// itself when few of its pieces hold a sequence's last step: each such piece
+// stores the row and reads it back mid-piece, which cost the OPT-13B-shaped
+// batch (most pieces hold one) more than the write launch it saves, while
+// the Qwen2-shaped one (one piece in six) gains that launch.
+bool stream_writes_in_launch(int S, int Hq, int Hkv, int waves) {
+  const int HG = bf16_heads_per_group(Hkv);
+  const int64_t units = static_cast<int64_t>(S) * (Hkv / HG) * ((Hq / Hkv + 15) / 16);
+  return 2 * units <= waves / HG;
+}
+
 // Waves of the stream schedule's persistent grid on the current device.
 int stream_waves(int D) {
   int dev = 0, cus = 0;
@@ -249,7 +260,7 @@ int paged_kv_write_positions(const void* key, const void* value, void* kv_cache,
     return PKV_ERR_INVALID;
   }
   return launch_write_positions(key, value, kv_cache, block_tables, table_width, seq_ids, positions,
-                                slot_mapping, num_tokens, num_seqs, num_blocks, block_size,
+                                0, slot_mapping, num_tokens, num_seqs, num_blocks, block_size,
                                 num_kv_heads, head_size, eb, stream);
 }
 
@@ -363,7 +374,7 @@ int decode_stream(int phases, void* out, pkv_dtype out_dtype, const void* query,
                   const int32_t* context_lens, int num_seqs, int num_q_heads, int num_kv_heads,
                   int head_size, int block_size, int num_blocks, float scale, int max_context_len,
                   void* workspace, size_t workspace_bytes, pkv_dtype dtype, unsigned flags,
-                  hipStream_t stream) {
+                  hipStream_t stream, const void* key_new, const void* value_new) {
   const int waves = stream_waves(head_size);
   if (waves <= 0) {
     set_error("cannot query the current device");
@@ -397,6 +408,20 @@ int decode_stream(int phases, void* out, pkv_dtype out_dtype, const void* query,
   a.nontemporal = (flags & PKV_ATTN_CACHED_KV) ? 0 : 1;
   a.k_via_lds = static_cast<int64_t>(num_kv_heads) * head_size * elem_bytes(dtype) >= 4096;
   a.max_len = max_context_len;
+  // New tokens: stored by the attention launch itself or by a write launch
+  // first (stream_writes_in_launch).
+  if (key_new) {
+    if (stream_writes_in_launch(num_seqs, num_q_heads, num_kv_heads, waves)) {
+      a.k_new = key_new;
+      a.v_new = value_new;
+    } else if (phases & kAttend) {
+      const int rc = launch_write_positions(key_new, value_new, const_cast<void*>(kv_cache),
+                                            block_tables, table_width, nullptr, context_lens, -1,
+                                            nullptr, num_seqs, num_seqs, num_blocks, block_size,
+                                            num_kv_heads, head_size, elem_bytes(dtype), stream);
+      if (rc != PKV_OK) return rc;
+    }
+  }
   a.stream = 1;
   a.stream_waves = waves;
   stream_lds_plan(num_q_heads / num_kv_heads, head_size, a.k_via_lds != 0, &a.stream_slots,
@@ -418,7 +443,8 @@ int decode_impl(int phases, void* out, pkv_dtype out_dtype, const void* query,
                 const int32_t* context_lens, int num_seqs, int num_q_heads, int num_kv_heads,
                 int head_size, int block_size, int num_blocks, float scale, int max_context_len,
                 int partition_size, void* workspace, size_t workspace_bytes, pkv_dtype dtype,
-                unsigned flags, hipStream_t stream) {
+                unsigned flags, hipStream_t stream, const void* key_new = nullptr,
+                const void* value_new = nullptr) {
   clear_error();
   if (!shape_ok(num_seqs, num_q_heads, num_kv_heads, head_size, block_size, max_context_len, dtype))
     return PKV_ERR_INVALID;
@@ -456,11 +482,21 @@ int decode_impl(int phases, void* out, pkv_dtype out_dtype, const void* query,
     set_error("out, query and kv_cache must be 16-byte aligned");
     return PKV_ERR_INVALID;
   }
+  if (key_new || value_new) {
+    if (!key_new || !value_new) {
+      set_error("key and value of the new tokens: null pointer");
+      return PKV_ERR_INVALID;
+    }
+    if (!aligned16(key_new) || !aligned16(value_new)) {
+      set_error("key and value of the new tokens must be 16-byte aligned");
+      return PKV_ERR_INVALID;
+    }
+  }
   if (uses_stream(num_seqs, num_q_heads, num_kv_heads, max_context_len, partition_size, dtype))
     return decode_stream(phases, out, out_dtype, query, kv_cache, block_tables, table_width,
                          context_lens, num_seqs, num_q_heads, num_kv_heads, head_size, block_size,
                          num_blocks, scale, max_context_len, workspace, workspace_bytes, dtype,
-                         flags, stream);
+                         flags, stream, key_new, value_new);
   const int P = resolve_partition(num_seqs, num_q_heads, num_kv_heads, head_size, block_size,
                                   max_context_len, partition_size, dtype);
   if (P <= 0) {
@@ -534,6 +570,15 @@ int decode_impl(int phases, void* out, pkv_dtype out_dtype, const void* query,
                                        (rows * head_size * 4 + 255) / 256 * 256);
   }
   if (phases & kAttend) {
+    // the other schedules write the new tokens first (each sequence's at
+    // position context_lens[s] - 1), then read them like the rest
+    if (key_new) {
+      const int rc = launch_write_positions(key_new, value_new, const_cast<void*>(kv_cache),
+                                            block_tables, table_width, nullptr, context_lens, -1,
+                                            nullptr, num_seqs, num_seqs, num_blocks, block_size,
+                                            num_kv_heads, head_size, elem_bytes(dtype), stream);
+      if (rc != PKV_OK) return rc;
+    }
     const int rc = dtype == PKV_BF16 ? launch_attention_bf16(a, stream) : launch_attention_f32(a, stream);
     if (rc != PKV_OK) return rc;
   }
@@ -627,6 +672,33 @@ int paged_attention_decode(PKV_DECODE_PARAMS) { return decode_impl(kAttend | kMe
 int paged_attention_partitions(PKV_DECODE_PARAMS) { return decode_impl(kAttend, PKV_DECODE_ARGS); }
 
 int paged_attention_merge(PKV_DECODE_PARAMS) { return decode_impl(kMerge, PKV_DECODE_ARGS); }
+
+#define PKV_APPEND_PARAMS                                                                      \
+  void *out, pkv_dtype out_dtype, const void *query, const void *key, const void *value,      \
+      void *kv_cache, const int32_t *block_tables, int table_width, const int32_t *context_lens, \
+      int num_seqs, int num_q_heads, int num_kv_heads, int head_size, int block_size,          \
+      int num_blocks, float scale, int max_context_len, int partition_size, void *workspace,   \
+      size_t workspace_bytes, pkv_dtype dtype, unsigned flags, hipStream_t stream
+
+int paged_attention_append_in_launch(int num_seqs, int num_q_heads, int num_kv_heads,
+                                     int head_size, int block_size, int max_context_len,
+                                     int partition_size, pkv_dtype dtype) {
+  (void)block_size;
+  if (num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0 || num_seqs < 0) return -1;
+  if (!uses_stream(num_seqs, num_q_heads, num_kv_heads, max_context_len, partition_size, dtype))
+    return 0;
+  const int waves = stream_waves(head_size);
+  if (waves <= 0) return -1;
+  return stream_writes_in_launch(num_seqs, num_q_heads, num_kv_heads, waves) ? 1 : 0;
+}
+
+int paged_attention_decode_append(PKV_APPEND_PARAMS) {
+  return decode_impl(kAttend | kMerge, PKV_DECODE_ARGS, key, value);
+}
+
+int paged_attention_append_partitions(PKV_APPEND_PARAMS) {
+  return decode_impl(kAttend, PKV_DECODE_ARGS, key, value);
+}
 
 }  // extern "C"
 

@@ -149,14 +149,60 @@ attention_bf16_stream_kernel(AttnArgs a) {
     float* srow = rows + i * nhs * SROW;
     float* sml = mls + 2 * i * nhs;
     const int L = a.lens[s];
+    // With new tokens given (and the in-launch write chosen), each sequence's
+    // token L - 1 is stored into the cache by the piece that reads the
+    // sequence's last step (one row per kv head; every query-head chunk's
+    // wave stores the same bytes) before that piece reads it back like the
+    // others: a wave's own store precedes its later loads of the address, and
+    // no other piece of this launch reads the row.  The slot rule and its -1
+    // cases are the write kernel's; phys is the token's table entry.  Returns
+    // false when it is out of range.  The rows are loaded first (their
+    // latency overlaps the table lookup).
+    uint4 kk = make_uint4(0, 0, 0, 0), vv = kk;
+    auto load_new = [&]() {
+      if (lane < D / 8) {
+        const int64_t nrow = (static_cast<int64_t>(s) * a.Hkv + kvh) * D + 8 * lane;
+        kk = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.k_new) + nrow);
+        vv = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.v_new) + nrow);
+      }
+    };
+    auto store_new = [&](int phys) -> bool {
+      if (phys < 0 || phys >= a.NB) return false;
+      if (lane < D / 8) {
+        const int64_t dst = (static_cast<int64_t>(phys) * B + (L - 1) % B) * a.Hkv * D +
+                            static_cast<int64_t>(kvh) * D + 8 * lane;
+        uint16_t* cache = static_cast<uint16_t*>(const_cast<void*>(a.kv));
+        *reinterpret_cast<uint4*>(cache + dst) = kk;
+        *reinterpret_cast<uint4*>(cache + static_cast<int64_t>(a.NB) * B * a.Hkv * D + dst) = vv;
+      }
+      return true;
+    };
     if (L < 0 || L > a.max_len || (L + B - 1) / B > a.width) {
-      // an invalid sequence is one step, so always whole: NaN output
+      // an invalid sequence is one step, so always whole: NaN output (its
+      // new token is still stored, as the write kernel would)
+      if (a.k_new != nullptr && L > 0 && (L - 1) / B < a.width) {
+        load_new();
+        store_new(a.tables[static_cast<int64_t>(s) * a.width + (L - 1) / B]);
+      }
       for (int e = lane; e < nh * SROW; e += 64) srow[e] = NAN;
     } else {
       const int t0 = st0 * kStep;
       const int t1 = min(L, st1 * kStep);
+      const bool append = a.k_new != nullptr && L > 0 && t1 == L;
+      if (append) load_new();
       w.begin(a, s, kvh, h0, nh, t0, t1);
+      bool bad_new = false;
+      if (append) {
+        // the new token's table entry: from the window begin() loaded (the
+        // run's first WIN steps), else from the table
+        const int qn = (L - 1 - t0) / kStep;
+        const int pn = ((L - 1 - t0) % kStep) / (kStep / Wv::EPS);
+        const int phys = qn < Wv::WIN ? __builtin_amdgcn_readlane(w.win, Wv::EPS * qn + pn)
+                                      : a.tables[static_cast<int64_t>(s) * a.width + (L - 1) / B];
+        bad_new = !store_new(phys);
+      }
       w.run((t1 - t0 + kStep - 1) / kStep, [](int) {});
+      if (bad_new) w.bad_blk = true;  // (the step reading it flags it too)
       w.finish(srow, sml, nh);
     }
     // whole pairs go to out; a piece of a cut pair goes to workspace slot

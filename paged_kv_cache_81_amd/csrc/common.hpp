@@ -60,8 +60,8 @@ int launch_write(const void* key, const void* value, void* kv, const int64_t* sl
                  int B, int Hkv, int D, int elem_bytes, hipStream_t stream);
 int launch_write_positions(const void* key, const void* value, void* kv, const int32_t* tables,
                            int width, const int32_t* seq_ids, const int32_t* positions,
-                           int64_t* slots_out, int T, int S, int NB, int B, int Hkv, int D,
-                           int elem_bytes, hipStream_t stream);
+                           int pos_offset, int64_t* slots_out, int T, int S, int NB, int B,
+                           int Hkv, int D, int elem_bytes, hipStream_t stream);
 int launch_copy_blocks(void* dst, int dst_nb, const void* src, int src_nb, const int32_t* src_ids,
                        const int32_t* dst_ids, int n, int64_t half_bytes, hipStream_t stream);
 int launch_gather(void* k_out, void* v_out, const void* kv, const int32_t* tables, int width,
@@ -102,6 +102,11 @@ struct AttnArgs {
   int max_prefix;               // longest valid prefix (longer ones give NaN)
   int* ws_seq;                  // [4][S]: parts of each sequence (or -1), its group's
                                 // first sequence, its prefix length, table mismatch
+  // decode step with its write (stream schedule): sequence s's new token,
+  // rows [s][Hkv][D] of k_new and v_new, sits at position lens[s] - 1; it is
+  // written to the cache and folded in from these rows (nullptr: none)
+  const void* k_new;
+  const void* v_new;
 };
 
 // Stream schedule: wave w of W reads stream steps [start(w), start(w + 1))

@@ -47,19 +47,21 @@ __global__ void __launch_bounds__(256) write_kernel(
 }
 
 // Slot derivation and write in one pass: thread (t, c) finds token t's slot
-// from its table and position (as slot_mapping_kernel does) and moves piece c
-// of its K and V; the thread with c == 0 also records the slot.
+// from its table and position (positions[t] + pos_offset, as
+// slot_mapping_kernel does) and moves piece c of its K and V; the thread with
+// c == 0 also records the slot.  With the context lengths as positions and
+// an offset of -1 it writes each sequence's last token.
 __global__ void __launch_bounds__(256) write_positions_kernel(
     const uint4* __restrict__ key, const uint4* __restrict__ value, uint4* __restrict__ kv,
     const int32_t* __restrict__ tables, int width, const int32_t* __restrict__ seq_ids,
-    const int32_t* __restrict__ positions, int64_t* __restrict__ slots_out, int64_t total,
-    int chunks, int S, int B, int NB) {
+    const int32_t* __restrict__ positions, int pos_offset, int64_t* __restrict__ slots_out,
+    int64_t total, int chunks, int S, int B, int NB) {
   const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
   if (i >= total) return;
   const int64_t t = i / chunks;
   const int64_t c = i - t * chunks;
   const int s = seq_ids ? seq_ids[t] : static_cast<int>(t);
-  const int p = positions[t];
+  const int p = positions[t] + pos_offset;
   int64_t slot = -1;
   if (p >= 0 && s >= 0 && s < S) {
     const int lb = p / B;
@@ -132,14 +134,14 @@ int launch_write(const void* key, const void* value, void* kv, const int64_t* sl
 
 int launch_write_positions(const void* key, const void* value, void* kv, const int32_t* tables,
                            int width, const int32_t* seq_ids, const int32_t* positions,
-                           int64_t* slots_out, int T, int S, int NB, int B, int Hkv, int D,
-                           int elem_bytes, hipStream_t stream) {
+                           int pos_offset, int64_t* slots_out, int T, int S, int NB, int B,
+                           int Hkv, int D, int elem_bytes, hipStream_t stream) {
   if (T == 0) return PKV_OK;
   const int chunks = Hkv * D * elem_bytes / 16;
   const int64_t total = static_cast<int64_t>(T) * chunks;
   write_positions_kernel<<<dim3(static_cast<unsigned>(cdiv64(total, 256))), dim3(256), 0, stream>>>(
       static_cast<const uint4*>(key), static_cast<const uint4*>(value), static_cast<uint4*>(kv),
-      tables, width, seq_ids, positions, slots_out, total, chunks, S, B, NB);
+      tables, width, seq_ids, positions, pos_offset, slots_out, total, chunks, S, B, NB);
   return check_launch("kv write (positions)");
 }
 

@@ -168,3 +168,34 @@ def test_shared_prefix_host_checks(lib):
                                         BF16, None) == -1
     assert lib.paged_kv_write_positions(p, p, p, p, 0, None, p, None, 4, 4, 10, 16, 2, 128, BF16,
                                         None) == -1
+
+
+def test_decode_append_host_checks(lib):
+    """Argument checks of the decode step with its write, made before
+    anything is launched (the new tokens' key and value must both be given
+    and 16-byte aligned; the rest is checked as for the plain decode)."""
+    p = ctypes.c_void_p(0x1000)  # never dereferenced: the checks fail first
+    args = dict(out=p, out_dtype=0, query=p, key=p, value=p, kv=p, tables=p, width=4, lens=p,
+                S=4, Hq=8, Hkv=2, D=128, B=16, NB=10, scale=0.1, max_len=64, P=0, ws=p,
+                ws_bytes=1 << 30, dtype=1, flags=0, stream=None)
+
+    def call(fn, **kw):
+        a = dict(args, **kw)
+        return fn(a["out"], a["out_dtype"], a["query"], a["key"], a["value"], a["kv"], a["tables"],
+                  a["width"], a["lens"], a["S"], a["Hq"], a["Hkv"], a["D"], a["B"], a["NB"],
+                  a["scale"], a["max_len"], a["P"], a["ws"], a["ws_bytes"], a["dtype"], a["flags"],
+                  a["stream"])
+    for fn in (lib.paged_attention_decode_append, lib.paged_attention_append_partitions):
+        assert call(fn, value=None) == -1
+        assert call(fn, key=None) == -1
+        assert call(fn, key=ctypes.c_void_p(0x1008)) == -1     # misaligned
+        assert call(fn, value=ctypes.c_void_p(0x1004)) == -1
+        assert call(fn, D=96) == -2
+        assert call(fn, Hq=7) == -1
+        assert call(fn, flags=4) == -1
+        assert call(fn, S=0) == 0
+    # where the write goes: only the stream schedule (bf16, automatic
+    # partitioning) can store it inside the attention launch
+    assert lib.paged_attention_append_in_launch(4, 7, 2, 128, 16, 64, 0, 1) == -1
+    assert lib.paged_attention_append_in_launch(4, 8, 2, 128, 16, 64, 0, 0) == 0   # fp32
+    assert lib.paged_attention_append_in_launch(4, 8, 2, 128, 16, 64, 64, 1) == 0  # fixed
