@@ -10,7 +10,9 @@
 // same number of K/V bytes whatever the mix of context lengths.  A unit
 // lying inside one piece is finished there and written to out; a unit cut
 // into several pieces leaves one partial result per piece in consecutive
-// workspace slots, combined afterwards by the log-sum-exp merge.
+// workspace slots, combined afterwards by the log-sum-exp merge.  Given the
+// step's new key/value rows, the launch also stores each sequence's new token
+// (the decode step's write) before reading it back with the rest.
 #include "attention_bf16_wave.hpp"
 
 namespace pkv {

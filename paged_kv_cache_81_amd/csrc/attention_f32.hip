@@ -43,11 +43,6 @@ __global__ void __launch_bounds__(64) attention_f32_kernel(AttnArgs a) {
 
   const int nh = min(NH, G - chunk * kMaxHeads);
   const int h0 = kvh * G + chunk * kMaxHeads;
-  const float* q = static_cast<const float*>(a.query);
-  for (int i = lane; i < NH * D; i += 64)
-    s_q[i / D][i % D] = i < nh * D ? q[(static_cast<int64_t>(s) * a.Hq + h0) * D + i] : 0.f;
-  __syncthreads();
-
   const int t_begin = part * P;
   const int t_end = bad_seq ? t_begin : min(L, t_begin + P);
   const int n = max(0, t_end - t_begin);
@@ -57,10 +52,18 @@ __global__ void __launch_bounds__(64) attention_f32_kernel(AttnArgs a) {
   const int32_t* trow = a.tables + static_cast<int64_t>(s) * a.width;
   bool bad = bad_seq;
 
+  // the table entry of the lane's first token is loaded together with the
+  // query rows, so the key loads wait for one round trip, not two
+  const int phys_first = lane < n ? trow[(t_begin + lane) / B] : 0;
+  const float* q = static_cast<const float*>(a.query);
+  for (int i = lane; i < NH * D; i += 64)
+    s_q[i / D][i % D] = i < nh * D ? q[(static_cast<int64_t>(s) * a.Hq + h0) * D + i] : 0.f;
+  __syncthreads();
+
   // phase 1: scores
   for (int i = lane; i < n; i += 64) {
     const int t = t_begin + i;
-    const int phys = trow[t / B];
+    const int phys = i == lane ? phys_first : trow[t / B];
     s_phys[i] = phys;
     float dot[NH];
 #pragma unroll
@@ -84,6 +87,30 @@ __global__ void __launch_bounds__(64) attention_f32_kernel(AttnArgs a) {
     for (int h = 0; h < NH; ++h) s_p[h][i] = dot[h] * a.scale_log2;
   }
   __syncthreads();
+
+  // 64 tokens per batch of value loads when one head's accumulators are all
+  // a lane holds, 32 for a few heads, 16 when many heads' accumulators fill
+  // the registers.  Every load of a batch is issued (a token past the end, or
+  // on a block outside the pool -- flagged in phase 1 -- reads block 0 and
+  // its value is then zeroed), so no branch separates them; the first batch
+  // is issued before phase 2, whose arithmetic then covers its latency.
+  constexpr int kBatch = NH * PER == 1 ? 64 : (NH * PER >= 16 ? 16 : 32);
+  float v[kBatch][PER];
+  auto load_batch = [&](int i0) {
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) {
+      const int i = i0 + k;
+      const int phys = i < n ? s_phys[i] : -1;
+      const bool ok = phys >= 0 && phys < a.NB;
+      const float* vr = vbase + (static_cast<int64_t>(ok ? phys : 0) * B + (t_begin + i) % B) * row +
+                        lane * PER;
+#pragma unroll
+      for (int e = 0; e < PER; ++e) v[k][e] = vr[e];
+#pragma unroll
+      for (int e = 0; e < PER; ++e) v[k][e] = ok ? v[k][e] : 0.f;
+    }
+  };
+  load_batch(0);  // unconditional: a branch here would make the compiler wait for it at once
 
   // phase 2: per-head max and exponentials (log2 domain)
   float m[NH], l[NH];
@@ -110,26 +137,8 @@ __global__ void __launch_bounds__(64) attention_f32_kernel(AttnArgs a) {
   for (int h = 0; h < NH; ++h)
 #pragma unroll
     for (int e = 0; e < PER; ++e) acc[h][e] = 0.f;
-  // 32 tokens per batch (16 when many heads' accumulators fill the
-  // registers), their value loads all in flight together: every load is
-  // issued (a token past the end, or on a block outside the pool -- flagged
-  // in phase 1 -- reads block 0 and its value is then zeroed), so no branch
-  // separates them
-  constexpr int kBatch = NH * PER >= 16 ? 16 : 32;
   for (int i0 = 0; i0 < n; i0 += kBatch) {
-    float v[kBatch][PER];
-#pragma unroll
-    for (int k = 0; k < kBatch; ++k) {
-      const int i = i0 + k;
-      const int phys = i < n ? s_phys[i] : -1;
-      const bool ok = phys >= 0 && phys < a.NB;
-      const float* vr = vbase + (static_cast<int64_t>(ok ? phys : 0) * B + (t_begin + i) % B) * row +
-                        lane * PER;
-#pragma unroll
-      for (int e = 0; e < PER; ++e) v[k][e] = vr[e];
-#pragma unroll
-      for (int e = 0; e < PER; ++e) v[k][e] = ok ? v[k][e] : 0.f;
-    }
+    if (i0 > 0) load_batch(i0);
     // tokens past the end have zero values (and weights never read past n)
 #pragma unroll
     for (int k = 0; k < kBatch; ++k) {
