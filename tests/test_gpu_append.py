@@ -152,3 +152,28 @@ def test_write_placement_for_the_benchmark_shapes():
             w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_size, w.block_size,
             w.max_context_len, w.partition_size, 1 if w.dtype == "bf16" else 0)
         assert got == exp, (name, got)
+
+
+def test_two_launch_form_when_the_write_goes_first():
+    """On a batch where the library launches the write before the attention
+    (many units per piece), the two-launch form still equals the one call and
+    the separate calls."""
+    w = workloads.opt13b_mha(num_seqs=64)
+    assert pkv.lib.paged_attention_append_in_launch(
+        w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_size, w.block_size,
+        w.max_context_len, 0, 1) == 0
+    a = H.upload(w, step=False)
+    b = H.upload(w, step=False)
+    one = pkv.attention_decode_append(a.query, a.new_k, a.new_v, a.kv, a.tables, a.lens,
+                                      w.scale, w.max_context_len)
+    ws = torch.empty(pkv.workspace_bytes(w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_size,
+                                         w.block_size, w.max_context_len, 0, b.kv.dtype),
+                     dtype=torch.uint8, device=b.kv.device)
+    two = torch.empty_like(one)
+    pkv.attention_append_partitions(b.query, b.new_k, b.new_v, b.kv, b.tables, b.lens, w.scale,
+                                    w.max_context_len, out=two, workspace=ws)
+    pkv.attention_merge(b.query, b.kv, b.tables, b.lens, w.scale, w.max_context_len, out=two,
+                        workspace=ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(_bits(a.kv), _bits(b.kv))
+    assert np.array_equal(_bits(one), _bits(two))
