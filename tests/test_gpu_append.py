@@ -177,3 +177,29 @@ def test_two_launch_form_when_the_write_goes_first():
     torch.cuda.synchronize()
     assert np.array_equal(_bits(a.kv), _bits(b.kv))
     assert np.array_equal(_bits(one), _bits(two))
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_append_random_batches(seed):
+    """Seeded random batches (batch size, length mix, head grouping, head and
+    block size): cache and output bit-identical to the separate calls, and a
+    sample of sequences against the oracle."""
+    rng = np.random.default_rng(9400 + seed)
+    hq, hkv = [(8, 8), (14, 2), (32, 8), (40, 2), (12, 4), (16, 1)][seed % 6]
+    D = [64, 128][seed % 2]
+    B = [8, 16, 32][seed % 3]
+    S = int(rng.integers(1, 300))
+    lens = np.maximum(1, np.round(rng.lognormal(np.log(300), 1.2, size=S))).astype(int)
+    lens = np.minimum(lens, 4000)
+    lens[rng.random(S) < 0.1] = 1
+    w = workloads.custom(9500 + seed, lens.tolist(), num_q_heads=hq, num_kv_heads=hkv,
+                         head_size=D, block_size=B)
+    say(f"[append] random seed={seed} S={S} hq={hq} hkv={hkv} D={D} B={B} "
+        f"in_launch={pkv.lib.paged_attention_append_in_launch(S, hq, hkv, D, B, w.max_context_len, 0, 1)}")
+    got = _compare(w, oracle_check=False).cpu().numpy()
+    for s in sorted({int(np.argmax(w.context_lens)), int(rng.integers(0, S))}):
+        k, v = w.logical_kv(s)
+        ref = oracle.attention_ref(oracle.to_f64(w.query[s], w.dtype), oracle.to_f64(k, w.dtype),
+                                   oracle.to_f64(v, w.dtype), w.scale)
+        err = float(H.row_rel_err(got[s], ref).max())
+        assert err <= H.tolerance(w), (s, err)
