@@ -173,27 +173,22 @@ def test_attention_small_full_oracle(name):
 
 
 @pytest.mark.parametrize("name", NAMES)
-def test_attention_full_size_sampled(name):
+def test_attention_full_size_every_row(name):
     """Full-size workload in the benchmark's launch configuration (and at the
-    extra fixed partition sizes); the oracle computes a sample of sequences
-    (longest, shortest, and random ones)."""
+    extra fixed partition sizes): every output row of every sequence against
+    the float64 oracle run over the oracle's own pool."""
     w = full(name)
     say(f"[attention] {name}: S={w.num_seqs} max_len={w.max_context_len}")
     st = H.upload(w)
     outs = {P: H.attend(st, partition_size=P).cpu().numpy()
             for P in (w.partition_size, *EXTRA_PARTITIONS.get(name, ()))}
-    rng = np.random.default_rng(0)
-    L = w.context_lens
-    sample = sorted({int(np.argmax(L)), int(np.argmin(L)),
-                     *rng.choice(w.num_seqs, size=min(6, w.num_seqs), replace=False).tolist()})
-    for s in sample:
-        k, v = w.logical_kv(s)
-        ref = oracle.attention_ref(oracle.to_f64(w.query[s], w.dtype), oracle.to_f64(k, w.dtype),
-                                   oracle.to_f64(v, w.dtype), w.scale)
-        for P, got in outs.items():
-            _check_rows(got[s], ref, H.tolerance(w), f"{name} P={P} seq {s} (L={L[s]})")
-    for got in outs.values():
-        assert np.all(np.isfinite(got))
+    del st
+    ref_kv, _, _ = oracle_pool(w)
+    ref = oracle.paged_attention_ref(w.query, ref_kv, w.block_tables, w.context_lens, w.scale,
+                                     w.dtype)
+    del ref_kv
+    for P, got in outs.items():
+        _check_rows(got, ref, H.tolerance(w), f"{name} full size P={P}, all {w.num_seqs} sequences")
 
 
 EDGE_LENS = [0, 1, 2, 15, 16, 17, 31, 32, 33, 63, 64, 65, 511, 512, 513, 1024, 1025, 1500]
