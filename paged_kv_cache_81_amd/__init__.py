@@ -263,16 +263,31 @@ def attention_decode(query: torch.Tensor, kv_cache: torch.Tensor, block_tables: 
     return out
 
 
+def _split_call_buffers(n) -> None:
+    """The two launches of a split call communicate through ``out`` and
+    ``workspace``: both must be the caller's, the same for both calls."""
+    if n[7] is None:
+        raise ValueError("split decode calls need out= (the same tensor for both calls)")
+    if n[9] is None:
+        raise ValueError("split decode calls need workspace= (the same tensor for both calls)")
+
+
 def attention_partitions(*a, **k) -> torch.Tensor:
-    """First launch of attention_decode (attention pass); same arguments."""
-    out, args = _decode_args(*_norm(*a, **k))
+    """First launch of attention_decode (attention pass); same arguments, and
+    ``out`` and ``workspace`` must be given (the merge reads them)."""
+    n = _norm(*a, **k)
+    _split_call_buffers(n)
+    out, args = _decode_args(*n)
     check(lib.paged_attention_partitions(*args), "paged_attention_partitions")
     return out
 
 
 def attention_merge(*a, **k) -> torch.Tensor:
-    """Second launch of attention_decode (log-sum-exp merge); same arguments."""
-    out, args = _decode_args(*_norm(*a, **k))
+    """Second launch of attention_decode (log-sum-exp merge); same arguments,
+    including the ``out`` and ``workspace`` the attention pass wrote."""
+    n = _norm(*a, **k)
+    _split_call_buffers(n)
+    out, args = _decode_args(*n)
     check(lib.paged_attention_merge(*args), "paged_attention_merge")
     return out
 
@@ -306,8 +321,10 @@ def attention_decode_append(query: torch.Tensor, key: torch.Tensor, value: torch
 
 def attention_append_partitions(query, key, value, *a, **k) -> torch.Tensor:
     """First launch of attention_decode_append (write + attention pass); follow it
-    with attention_merge given the same decode arguments."""
+    with attention_merge given the same decode arguments (``out`` and
+    ``workspace`` included)."""
     n = _norm(query, *a, **k)
+    _split_call_buffers(n)
     out, args = _decode_args(*n)
     check(lib.paged_attention_append_partitions(*_append_args(key, value, query, n[1], args)),
           "paged_attention_append_partitions")
@@ -316,12 +333,13 @@ def attention_append_partitions(query, key, value, *a, **k) -> torch.Tensor:
 
 def attention_prefill(query: torch.Tensor, kv_cache: torch.Tensor, block_tables: torch.Tensor,
                       context_lens: torch.Tensor, query_start: torch.Tensor, scale: float,
-                      max_query_len: Optional[int] = None, out_dtype=torch.float32,
+                      max_query_len: int, out_dtype=torch.float32,
                       out: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Causal attention of each sequence's chunk of query rows
     (``query[query_start[s]:query_start[s+1]]``, the last tokens of sequence
     ``s``, whose K/V is already cached) over its paged K/V.  ``[T, Hq, D]``.
-    Without ``max_query_len`` the chunk lengths are read back to the host."""
+    ``max_query_len``: the longest chunk (a host int, as the caller's
+    scheduler knows it); a longer chunk gives NaN rows."""
     nb, b, hkv, d = _cache_dims(kv_cache)
     dev = kv_cache.device
     _need(query, "query", kv_cache.dtype, 3, dev)
@@ -334,8 +352,6 @@ def attention_prefill(query: torch.Tensor, kv_cache: torch.Tensor, block_tables:
     S = context_lens.shape[0]
     if block_tables.shape[0] != S or query_start.shape[0] != S + 1:
         raise ValueError("block_tables, context_lens and query_start disagree on the batch")
-    if max_query_len is None:
-        max_query_len = int((query_start[1:] - query_start[:-1]).max().item()) if S else 0
     if out is None:
         out = torch.empty((T, hq, d), dtype=out_dtype, device=dev)
     _need(out, "out", None, 3, dev)

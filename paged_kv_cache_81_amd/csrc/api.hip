@@ -3,9 +3,13 @@
 #include "common.hpp"
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
+#include <mutex>
 #include <string>
+#include <utility>
+#include <vector>
 
 namespace pkv {
 
@@ -28,6 +32,28 @@ int check_launch(const char* what) {
     set_error("%s: launch failed: %s", what, hipGetErrorString(e));
     return PKV_ERR_HIP;
   }
+  return PKV_OK;
+}
+
+int raise_lds_limit(const void* kern, int bytes) {
+  if (bytes <= 0) bytes = static_cast<int>(bf16_lds_limit());
+  // (kernel, device) pairs already raised; few, so a short list
+  static std::mutex mu;
+  static std::vector<std::pair<const void*, int>> done;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    set_error("cannot query the current device");
+    return PKV_ERR_HIP;
+  }
+  std::lock_guard<std::mutex> lock(mu);
+  for (const auto& d : done)
+    if (d.first == kern && d.second == dev) return PKV_OK;
+  if (hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, bytes) != hipSuccess) {
+    (void)hipGetLastError();
+    set_error("cannot raise a kernel's LDS limit to %d bytes", bytes);
+    return PKV_ERR_HIP;
+  }
+  done.emplace_back(kern, dev);
   return PKV_OK;
 }
 
@@ -153,15 +179,27 @@ bool stream_writes_in_launch(int S, int Hq, int Hkv, int waves) {
   return 2 * units <= waves / HG;
 }
 
-// Waves of the stream schedule's persistent grid on the current device.
-int stream_waves(int D) {
-  int dev = 0, cus = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+// Compute units of the current device (0 if it cannot be queried), asked of
+// the runtime once per device.
+int device_cus() {
+  constexpr int kDevices = 64;
+  static std::atomic<int> cached[kDevices];  // 0: not yet asked
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (dev >= 0 && dev < kDevices) {
+    const int c = cached[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
       cus <= 0)
     return 0;
-  return cus * stream_wgs_per_cu(D) * 4;
+  if (dev >= 0 && dev < kDevices) cached[dev].store(cus, std::memory_order_relaxed);
+  return cus;
 }
+
+// Waves of the stream schedule's persistent grid on the current device.
+int stream_waves(int D) { return device_cus() * stream_wgs_per_cu(D) * 4; }
 
 // Workspace of the stream schedule: one partial-result slot (nhs rows of D
 // floats and their (m, l)) per wave and per (sequence, kv head, query-head
@@ -709,14 +747,7 @@ namespace {
 
 // Workgroups of the shared-prefix kernel resident at once on the current
 // device (0 if it cannot be queried).
-int shared_resident_wgs() {
-  int dev = 0, cus = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-      cus <= 0)
-    return 0;
-  return cus * kSharedWgsPerCu;
-}
+int shared_resident_wgs() { return device_cus() * kSharedWgsPerCu; }
 
 // Items of a group's prefix partition: (kv-head groups) x (16-column blocks
 // of its members' query heads); estimated for groups of equal size.

@@ -209,17 +209,6 @@ attention_bf16_kernel(AttnArgs a) {
 
 // ---------------------------------------------------------------- launchers
 
-template <typename K>
-int raise_lds_limit(K kern) {
-  if (hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                          hipFuncAttributeMaxDynamicSharedMemorySize,
-                          static_cast<int>(bf16_lds_limit())) != hipSuccess) {
-    set_error("paged attention (bf16): cannot raise the LDS limit");
-    return PKV_ERR_HIP;
-  }
-  return PKV_OK;
-}
-
 // Workgroups of this kernel that one CU holds with `lds` bytes of dynamic LDS.
 template <typename K>
 int resident_per_cu(K kern, size_t lds) {
@@ -241,11 +230,7 @@ int resident_per_cu(K kern, size_t lds) {
 template <int D, int B, int HG, bool NT, bool KL, bool CMP>
 int launch_one(const AttnArgs& a, dim3 grid, size_t lds, hipStream_t stream) {
   auto kern = attention_bf16_kernel<D, B, HG, NT, KL, CMP>;
-  static bool attr_set = false;  // allow dynamic LDS up to the per-workgroup maximum
-  if (!attr_set) {
-    if (const int rc = raise_lds_limit(kern)) return rc;
-    attr_set = true;
-  }
+  if (const int rc = raise_lds_limit(reinterpret_cast<const void*>(kern))) return rc;
   if constexpr (CMP) {
     // one round of resident workgroups walks the item list (never more
     // workgroups than the dense grid has)

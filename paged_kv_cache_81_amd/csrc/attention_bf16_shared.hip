@@ -322,25 +322,10 @@ attention_bf16_shared_kernel(AttnArgs a) {
   flush();
 }
 
-template <typename Kern>
-int raise_lds_limit(Kern kern) {
-  if (hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                          hipFuncAttributeMaxDynamicSharedMemorySize,
-                          static_cast<int>(bf16_lds_limit())) != hipSuccess) {
-    set_error("paged attention (bf16, shared prefix): cannot raise the LDS limit");
-    return PKV_ERR_HIP;
-  }
-  return PKV_OK;
-}
-
 template <int D, int B, int HG, bool NT, bool KL>
 int launch_one(const AttnArgs& a, hipStream_t stream) {
   auto kern = attention_bf16_shared_kernel<D, B, HG, NT, KL>;
-  static bool attr_set = false;
-  if (!attr_set) {
-    if (const int rc = raise_lds_limit(kern)) return rc;
-    attr_set = true;
-  }
+  if (const int rc = raise_lds_limit(reinterpret_cast<const void*>(kern))) return rc;
   const size_t lds = static_cast<size_t>(kWaves) * a.stream_wave_floats * sizeof(float);
   kern<<<dim3(a.stream_waves / kWaves), dim3(kThreads), lds, stream>>>(a);
   return check_launch("paged attention (bf16, shared prefix)");

@@ -155,8 +155,9 @@ attention_bf16_stream_kernel(AttnArgs a) {
     // token L - 1 is stored into the cache by the piece that reads the
     // sequence's last step (one row per kv head; every query-head chunk's
     // wave stores the same bytes) before that piece reads it back like the
-    // others: a wave's own store precedes its later loads of the address, and
-    // no other piece of this launch reads the row.  The slot rule and its -1
+    // others (the fences in store_new order the storing lanes' stores before
+    // the loading lanes' loads), and no other piece of this launch reads the
+    // row.  The slot rule and its -1
     // cases are the write kernel's; phys is the token's table entry.  Returns
     // false when it is out of range.  The rows are loaded first (their
     // latency overlaps the table lookup).
@@ -177,6 +178,12 @@ attention_bf16_stream_kernel(AttnArgs a) {
         *reinterpret_cast<uint4*>(cache + dst) = kk;
         *reinterpret_cast<uint4*>(cache + static_cast<int64_t>(a.NB) * B * a.Hkv * D + dst) = vv;
       }
+      // Other lanes of this wave read the rows just stored: a wavefront-scope
+      // release/acquire orders the stores before those loads.  (gfx950 needs
+      // no instruction for it -- a wavefront's memory operations are performed
+      // in order -- so the fences only bind the compiler.)
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
       return true;
     };
     if (L < 0 || L > a.max_len || (L + B - 1) / B > a.width) {
@@ -222,25 +229,10 @@ attention_bf16_stream_kernel(AttnArgs a) {
 
 }
 
-template <typename K>
-int raise_lds_limit(K kern) {
-  if (hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                          hipFuncAttributeMaxDynamicSharedMemorySize,
-                          static_cast<int>(bf16_lds_limit())) != hipSuccess) {
-    set_error("paged attention (bf16): cannot raise the LDS limit");
-    return PKV_ERR_HIP;
-  }
-  return PKV_OK;
-}
-
 template <int D, int B, int HG, bool NT, bool KL>
 int launch_stream_one(const AttnArgs& a, hipStream_t stream) {
   auto kern = attention_bf16_stream_kernel<D, B, HG, NT, KL>;
-  static bool attr_set = false;
-  if (!attr_set) {
-    if (const int rc = raise_lds_limit(kern)) return rc;
-    attr_set = true;
-  }
+  if (const int rc = raise_lds_limit(reinterpret_cast<const void*>(kern))) return rc;
   const size_t lds = static_cast<size_t>(kWaves) * a.stream_wave_floats * sizeof(float);
   kern<<<dim3(a.stream_waves / kWaves), dim3(kThreads), lds, stream>>>(a);
   return check_launch("paged attention (bf16, stream schedule)");

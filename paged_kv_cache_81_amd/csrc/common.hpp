@@ -20,6 +20,10 @@ void clear_error();
 // Turns the last launch error into PKV_ERR_HIP (or PKV_OK).
 int check_launch(const char* what);
 
+// Lets kernel kern use `bytes` of dynamic LDS (default bf16_lds_limit()) on
+// the current device (once per kernel and device; thread-safe).
+int raise_lds_limit(const void* kern, int bytes = 0);
+
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 inline int64_t cdiv64(int64_t a, int64_t b) { return (a + b - 1) / b; }

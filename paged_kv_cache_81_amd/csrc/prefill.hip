@@ -368,6 +368,25 @@ prefill_bf16_kernel(PrefillArgs a) {
       *reinterpret_cast<float4*>(static_cast<float*>(a.out) + off) = o;
     }
   }
+  // A chunk longer than max_query_len has rows past the grid's tiles: the
+  // last tile writes them too (NaN, as for every row of a bad sequence), so
+  // no row of the chunk keeps what the output held before.
+  if (bad_seq && x == a.qtiles - 1 && qlen > a.qtiles * kPRows) {
+    const int rbeg = a.qtiles * kPRows;
+    const int64_t n4 = static_cast<int64_t>(qlen - rbeg) * D4;
+    for (int64_t e = tid; e < n4; e += kPThreads) {
+      const int64_t rr = rbeg + e / D4;
+      const int d = static_cast<int>(e % D4) * 4;
+      const int64_t off = ((q0 + rr) * a.Hq + h) * D + d;
+      if (a.out_bf16) {
+        const uint32_t nn = f32_to_bf16(NAN) | (static_cast<uint32_t>(f32_to_bf16(NAN)) << 16);
+        *reinterpret_cast<wave::u32x2*>(static_cast<uint16_t*>(a.out) + off) = wave::u32x2{nn, nn};
+      } else {
+        *reinterpret_cast<float4*>(static_cast<float*>(a.out) + off) =
+            make_float4(NAN, NAN, NAN, NAN);
+      }
+    }
+  }
 }
 
 // fp32: one wave per (query row, query head)
@@ -464,16 +483,7 @@ template <int D, int B>
 int launch_bf16_db(const PrefillArgs& a, hipStream_t stream) {
   auto kern = prefill_bf16_kernel<D, B>;
   const int lds = PGeom<D>::LDS;
-  static bool raised = false;
-  if (!raised) {
-    if (hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, lds) != hipSuccess) {
-      (void)hipGetLastError();
-      set_error("paged prefill: cannot reserve %d bytes of LDS", lds);
-      return PKV_ERR_HIP;
-    }
-    raised = true;
-  }
+  if (const int rc = raise_lds_limit(reinterpret_cast<const void*>(kern), lds)) return rc;
   kern<<<dim3(static_cast<unsigned>(a.items_per_xcd) * kXcds), dim3(kPThreads), lds, stream>>>(a);
   return check_launch("paged prefill (bf16)");
 }

@@ -199,3 +199,26 @@ def test_decode_append_host_checks(lib):
     assert lib.paged_attention_append_in_launch(4, 7, 2, 128, 16, 64, 0, 1) == -1
     assert lib.paged_attention_append_in_launch(4, 8, 2, 128, 16, 64, 0, 0) == 0   # fp32
     assert lib.paged_attention_append_in_launch(4, 8, 2, 128, 16, 64, 64, 1) == 0  # fixed
+
+
+def test_split_calls_need_their_buffers():
+    """The two launches of a split decode share out and workspace, so the
+    binding refuses to make fresh ones for either call (a fresh workspace
+    would leave the merge reading memory nobody wrote)."""
+    import torch
+
+    import paged_kv_cache_81_amd as pkv
+    q = torch.zeros((2, 8, 64), dtype=torch.bfloat16)
+    kv = torch.zeros((2, 4, 16, 2, 64), dtype=torch.bfloat16)
+    tables = torch.zeros((2, 4), dtype=torch.int32)
+    lens = torch.ones(2, dtype=torch.int32)
+    ws = torch.zeros(256, dtype=torch.uint8)
+    out = torch.zeros((2, 8, 64), dtype=torch.float32)
+    for fn in (pkv.attention_partitions, pkv.attention_merge):
+        with pytest.raises(ValueError, match="out="):
+            fn(q, kv, tables, lens, 0.125, 16, workspace=ws)
+        with pytest.raises(ValueError, match="workspace="):
+            fn(q, kv, tables, lens, 0.125, 16, out=out)
+    with pytest.raises(ValueError, match="workspace="):
+        pkv.attention_append_partitions(q, q[:, :2], q[:, :2], kv, tables, lens, 0.125, 16,
+                                        out=out)

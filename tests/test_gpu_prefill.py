@@ -158,3 +158,22 @@ def test_prefill_edge_cases():
     got = out.cpu().numpy()
     assert np.isnan(got[:30]).all()
     assert np.isfinite(got[30:35]).all()
+
+
+def test_chunk_past_the_grid_gives_nan_rows():
+    """A chunk longer than max_query_len by more than the grid's tiles
+    cover: every row of it is NaN, none keeps the output's old contents."""
+    pw = workloads.prefill(971, [0, 100], [300, 20], num_q_heads=4, num_kv_heads=2,
+                           head_size=64)
+    w = pw.cache
+    st = H.upload(w, device=DEV)
+    q = H.to_torch(pw.query, "bf16", DEV)
+    qs = torch.from_numpy(pw.query_start).to(DEV)
+    for dt in (torch.float32, torch.bfloat16):
+        out = torch.full((pw.num_tokens, 4, 64), 7.0, dtype=dt, device=DEV)
+        pkv.attention_prefill(q, st.kv, st.tables, st.lens, qs, w.scale, max_query_len=100,
+                              out=out)
+        torch.cuda.synchronize()
+        got = out.float().cpu().numpy()
+        assert np.isnan(got[:300]).all(), "the 300-row chunk (grid: one 128-row tile)"
+        assert np.isfinite(got[300:]).all()
