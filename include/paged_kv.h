@@ -229,6 +229,28 @@ int paged_attention_decode(void* out, pkv_dtype out_dtype, const void* query,
                            hipStream_t stream);
 
 /*
+ * paged_attention_decode_noalloc -- paged_attention_decode for callers that
+ * cannot allocate memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): the same arguments without the
+ * workspace.  Its workspace is a device array the library holds on every GPU
+ * it runs on, PKV_NOALLOC_SCRATCH_BYTES bytes, from module load until the
+ * process ends; the call allocates nothing (no hipMalloc or hipFree, no host
+ * heap).  A batch whose workspace (paged_attention_workspace_bytes) exceeds
+ * that returns PKV_ERR_WORKSPACE before anything is enqueued.  Every call on
+ * one GPU uses that GPU's one array, so calls whose executions overlap on a
+ * GPU (several streams, several threads) race: serialise them.  Results are
+ * those of paged_attention_decode with the same arguments, bit for bit.
+ */
+#define PKV_NOALLOC_SCRATCH_BYTES (32 << 20)
+int paged_attention_decode_noalloc(void* out, pkv_dtype out_dtype, const void* query,
+                                   const void* kv_cache, const int32_t* block_tables,
+                                   int table_width, const int32_t* context_lens, int num_seqs,
+                                   int num_q_heads, int num_kv_heads, int head_size,
+                                   int block_size, int num_blocks, float scale,
+                                   int max_context_len, int partition_size, pkv_dtype dtype,
+                                   unsigned flags, hipStream_t stream);
+
+/*
  * The two launches paged_attention_decode makes, exposed so that a caller can
  * time or schedule them separately.  paged_attention_partitions runs the
  * attention pass: it writes out[] directly for every sequence that fits in one

@@ -37,6 +37,8 @@ SIGNATURES = {
     "paged_attention_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i, _i, _i]),
     "paged_attention_decode": (_i, [_p, _i, _p, _p, _p, _i, _p, _i, _i, _i, _i, _i, _i, _f,
                                     _i, _i, _p, _sz, _i, _u, _p]),
+    "paged_attention_decode_noalloc": (_i, [_p, _i, _p, _p, _p, _i, _p, _i, _i, _i, _i, _i, _i,
+                                            _f, _i, _i, _i, _u, _p]),
     "paged_attention_partitions": (_i, [_p, _i, _p, _p, _p, _i, _p, _i, _i, _i, _i, _i, _i, _f,
                                         _i, _i, _p, _sz, _i, _u, _p]),
     "paged_attention_merge": (_i, [_p, _i, _p, _p, _p, _i, _p, _i, _i, _i, _i, _i, _i, _f,

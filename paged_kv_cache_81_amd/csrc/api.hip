@@ -7,24 +7,20 @@
 #include <cmath>
 #include <cstdarg>
 #include <mutex>
-#include <string>
-#include <utility>
-#include <vector>
 
 namespace pkv {
 
-static thread_local std::string g_error;
+// (a fixed buffer: reporting an error allocates nothing)
+static thread_local char g_error[512];
 
 void set_error(const char* fmt, ...) {
-  char buf[512];
   va_list ap;
   va_start(ap, fmt);
-  vsnprintf(buf, sizeof buf, fmt, ap);
+  vsnprintf(g_error, sizeof g_error, fmt, ap);
   va_end(ap);
-  g_error = buf;
 }
 
-void clear_error() { g_error.clear(); }
+void clear_error() { g_error[0] = '\0'; }
 
 int check_launch(const char* what) {
   const hipError_t e = hipGetLastError();
@@ -37,23 +33,31 @@ int check_launch(const char* what) {
 
 int raise_lds_limit(const void* kern, int bytes) {
   if (bytes <= 0) bytes = static_cast<int>(bf16_lds_limit());
-  // (kernel, device) pairs already raised; few, so a short list
+  // (kernel, device) pairs already raised, in fixed storage (the launch
+  // path allocates nothing); a pair that finds the table full is raised
+  // again on every launch, which is correct, only slower
+  struct Done {
+    const void* kern;
+    int dev;
+  };
+  constexpr int kMaxDone = 1024;
+  static Done done[kMaxDone];
+  static int ndone = 0;
   static std::mutex mu;
-  static std::vector<std::pair<const void*, int>> done;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) {
     set_error("cannot query the current device");
     return PKV_ERR_HIP;
   }
   std::lock_guard<std::mutex> lock(mu);
-  for (const auto& d : done)
-    if (d.first == kern && d.second == dev) return PKV_OK;
+  for (int i = 0; i < ndone; ++i)
+    if (done[i].kern == kern && done[i].dev == dev) return PKV_OK;
   if (hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, bytes) != hipSuccess) {
     (void)hipGetLastError();
     set_error("cannot raise a kernel's LDS limit to %d bytes", bytes);
     return PKV_ERR_HIP;
   }
-  done.emplace_back(kern, dev);
+  if (ndone < kMaxDone) done[ndone++] = Done{kern, dev};
   return PKV_OK;
 }
 
@@ -228,7 +232,7 @@ using namespace pkv;
 
 extern "C" {
 
-const char* pkv_last_error(void) { return g_error.c_str(); }
+const char* pkv_last_error(void) { return g_error; }
 
 int paged_kv_slot_mapping(int64_t* slot_mapping, const int32_t* block_tables, int table_width,
                           const int32_t* seq_ids, const int32_t* positions, int num_tokens,
@@ -706,6 +710,78 @@ int paged_attention_prefill(void* out, pkv_dtype out_dtype, const void* query,
 }
 
 int paged_attention_decode(PKV_DECODE_PARAMS) { return decode_impl(kAttend | kMerge, PKV_DECODE_ARGS); }
+
+}  // extern "C"
+
+// ---------------------------------------------------------------- no allocation
+
+namespace pkv {
+namespace {
+
+// The workspace of paged_attention_decode_noalloc: a device array of the
+// library's own, present on every GPU the library runs on from module load
+// to process end.  Host code never uses its name as an address (on the host
+// that names a stand-in, not device memory): the array's device address is
+// looked up once per device and kept in scratch_ptr.
+__device__ __align__(256) char scratch[PKV_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+
+// The array's address on the current device (nullptr, with the error set,
+// if it cannot be found).
+void* scratch_on_device() {
+  static void* ptr[kMaxDevices];
+  static std::mutex mu;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    set_error("no-allocation decode: cannot query the current device");
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(mu);
+  if (ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) {
+      (void)hipGetLastError();
+      set_error("no-allocation decode: cannot find the scratch array on device %d", dev);
+      return nullptr;
+    }
+    ptr[dev] = p;
+  }
+  return ptr[dev];
+}
+
+}  // namespace
+}  // namespace pkv
+
+extern "C" {
+
+int paged_attention_decode_noalloc(void* out, pkv_dtype out_dtype, const void* query,
+                                   const void* kv_cache, const int32_t* block_tables,
+                                   int table_width, const int32_t* context_lens, int num_seqs,
+                                   int num_q_heads, int num_kv_heads, int head_size,
+                                   int block_size, int num_blocks, float scale,
+                                   int max_context_len, int partition_size, pkv_dtype dtype,
+                                   unsigned flags, hipStream_t stream) {
+  clear_error();
+  const size_t need = paged_attention_workspace_bytes(num_seqs, num_q_heads, num_kv_heads,
+                                                      head_size, block_size, max_context_len,
+                                                      partition_size, dtype);
+  if (need > static_cast<size_t>(PKV_NOALLOC_SCRATCH_BYTES)) {
+    set_error("no-allocation decode: this batch needs %zu bytes of workspace, above the %d the "
+              "library holds; use paged_attention_decode with a workspace",
+              need, PKV_NOALLOC_SCRATCH_BYTES);
+    return PKV_ERR_WORKSPACE;
+  }
+  void* ws = nullptr;
+  if (need > 0) {
+    ws = scratch_on_device();
+    if (ws == nullptr) return PKV_ERR_HIP;
+  }
+  return decode_impl(kAttend | kMerge, out, out_dtype, query, kv_cache, block_tables, table_width,
+                     context_lens, num_seqs, num_q_heads, num_kv_heads, head_size, block_size,
+                     num_blocks, scale, max_context_len, partition_size, ws,
+                     static_cast<size_t>(PKV_NOALLOC_SCRATCH_BYTES), dtype, flags, stream);
+}
 
 int paged_attention_partitions(PKV_DECODE_PARAMS) { return decode_impl(kAttend, PKV_DECODE_ARGS); }
 
