@@ -13,16 +13,23 @@ pools, as the layers of a decode step do, so no step finds its K/V still in a
 cache from the previous one.  Inputs are resident in HBM before timing starts;
 the K timed steps are captured in one HIP graph and replayed once.
 
-Prints one JSON line.  ``value`` is the KV-read throughput of the step: the
+Prints one JSON line for the headline workload (``--workload``, default the
+OPT-13B-shaped batch).  ``value`` is the KV-read throughput of the step: the
 bytes the queries read through their block tables (sum over sequences of
 L * 2 * num_kv_heads * head_size * element bytes) divided by the step time.
 ``roofline`` relates the attention kernel alone (its average launch duration:
 HIP events on the launch stream around a graph of consecutive launches) to
-the MI355X HBM peak; ``cpu_baseline`` times
-the CPU oracle on a bounded sample of the same workload; ``block_ops`` times
-the copy-on-write and swap block copies at the workload's block geometry.
+the MI355X HBM peak; ``*_dist`` give p10/p50/p90 over repeated replays;
+``cpu_baseline`` times the CPU oracle on a bounded sample of the same
+workload on one thread and (``all_cores``) on the host's cores, naming the
+CPU; ``block_ops`` times the copy-on-write and swap block copies at the
+workload's block geometry.  ``ceiling`` is the streaming-read rate of a
+plain read kernel (pkv_read_ceiling) over 2 GiB and at the headline's bytes
+per launch, and ``frac_of_ceiling`` the attention kernel's share of the
+latter.  ``configs`` holds the same figures (step, kernels, roofline,
+size-matched ceiling, CPU baselines) for all five decode workloads.
 
-Usage: python bench.py [--steps K] [--warmup W] [--workload NAME] [--layers N]
+Usage: python bench.py [--steps K] [--warmup W] [--workload NAME] [--only] [--layers N]
 """
 from __future__ import annotations
 
@@ -135,7 +142,8 @@ def summarize_counters(d: str, workload: str) -> int:
     import workloads
 
     csv_of = lambda c: os.path.join(d, c, "run_counter_collection.csv")
-    part = "prefill_bf16" if _is_prefill(workload) else "attention_bf16"
+    part = ("prefill_bf16" if _is_prefill(workload) else
+            "attention_f32" if workload == "tiny" else "attention_bf16")
     fetch, n, kname = _counter_means(csv_of("FETCH_SIZE"), part)
     write, _, _ = _counter_means(csv_of("WRITE_SIZE"), part)
     # the 1 GiB copies (smaller copies of the same kernel in the run are ignored)
@@ -175,11 +183,76 @@ def summarize_counters(d: str, workload: str) -> int:
     return 0
 
 
-def cpu_baseline(w, seconds: float) -> dict:
-    """The CPU oracle, one thread, on a bounded sample of the workload's
-    sequences: slot mapping + write of the new token, gather through the
-    table, float64 attention."""
+def cpu_model() -> str:
+    """The host CPU's model name (from /proc/cpuinfo)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_share() -> int:
+    """Host cores this process may use: its CPU affinity, at most 16 (the
+    share of one GPU on a shared host)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+# state the forked CPU-baseline workers read (set before they are forked)
+_CPU_JOB = {}
+
+
+def _oracle_step(s: int) -> int:
+    """One sequence's decode step through the oracle, as it is: slot mapping
+    and write of the new token (idempotent; sequences write disjoint slots),
+    gather through the table, float64 attention.  Returns the KV bytes read."""
     import numpy as np
+
+    import oracle
+    w, pool, per_tok = _CPU_JOB["w"], _CPU_JOB["pool"], _CPU_JOB["per_tok"]
+    slot = oracle.slot_mapping_ref(w.block_tables, np.array([s]), w.new_pos[s:s + 1], w.block_size)
+    oracle.write_ref(pool, w.new_k[s:s + 1], w.new_v[s:s + 1], slot)
+    L = int(w.context_lens[s])
+    k, v = oracle.gather_ref(pool, w.block_tables[s], L)
+    oracle.attention_ref(oracle.to_f64(w.query[s], w.dtype), oracle.to_f64(k, w.dtype),
+                         oracle.to_f64(v, w.dtype), w.scale)
+    return L * per_tok
+
+
+def _oracle_worker(args):
+    """A forked worker: sequences first, first + stride, ... of the batch,
+    repeated, until `seconds` have passed; (bytes, steps, seconds)."""
+    from threadpoolctl import threadpool_limits
+    first, stride, seconds = args
+    n_seq = _CPU_JOB["w"].num_seqs
+    done = n = 0
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        s = first
+        while time.perf_counter() - t0 < seconds:
+            done += _oracle_step(s % n_seq)
+            n += 1
+            s += stride
+        dt = time.perf_counter() - t0
+    return done, n, dt
+
+
+def cpu_baseline(w, seconds: float, processes: int = 1) -> dict:
+    """The CPU oracle on a bounded sample of the workload's sequences: per
+    sequence, slot mapping + write of the new token, gather through the
+    table, float64 attention -- the oracle's functions as they are, one
+    sequence at a time (numpy's own thread pool held to one thread), passes
+    over the batch repeated for about ``seconds``; with ``processes`` > 1,
+    that many forked processes take every processes-th sequence each.  Call
+    it before the GPU is initialised (the workers are forked)."""
+    import multiprocessing
     from threadpoolctl import threadpool_limits
 
     import oracle
@@ -190,29 +263,23 @@ def cpu_baseline(w, seconds: float) -> dict:
         oracle.write_ref(pool, w.cached_k, w.cached_v,
                          oracle.slot_mapping_ref(w.block_tables, w.cached_seq, w.cached_pos,
                                                  w.block_size))
-        per_tok = 2 * w.num_kv_heads * w.head_size * w.elem_bytes
-        done = 0
-        n = 0
-        t0 = time.perf_counter()
-        # sequence by sequence, passes over the batch repeated (the write of
-        # the new token is idempotent) until about `seconds` have passed
-        while time.perf_counter() - t0 < seconds:
-            s = n % w.num_seqs
-            slot = oracle.slot_mapping_ref(w.block_tables, np.array([s]), w.new_pos[s:s + 1],
-                                           w.block_size)
-            oracle.write_ref(pool, w.new_k[s:s + 1], w.new_v[s:s + 1], slot)
-            L = int(w.context_lens[s])
-            k, v = oracle.gather_ref(pool, w.block_tables[s], L)
-            oracle.attention_ref(oracle.to_f64(w.query[s], w.dtype), oracle.to_f64(k, w.dtype),
-                                 oracle.to_f64(v, w.dtype), w.scale)
-            done += L * per_tok
-            n += 1
-        dt = time.perf_counter() - t0
-    return {"value": round(done / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+    _CPU_JOB.update(w=w, pool=pool, per_tok=2 * w.num_kv_heads * w.head_size * w.elem_bytes)
+    if processes <= 1:
+        done, n, dt = _oracle_worker((0, 1, seconds))
+    else:
+        with multiprocessing.get_context("fork").Pool(processes) as mp:
+            parts = mp.map(_oracle_worker, [(i, processes, seconds) for i in range(processes)])
+        done = sum(p[0] for p in parts)
+        n = sum(p[1] for p in parts)
+        dt = max(p[2] for p in parts)
+    _CPU_JOB.clear()
+    return {"value": round(done / dt / 1e9, 4), "unit": "GB/s", "cores": processes,
+            "kind": "oracle", "cpu": cpu_model(),
             "sample": f"{n} sequence decode steps of {w.name} ({n / w.num_seqs:.2f} passes over "
                       f"its {w.num_seqs} sequences, {done / 1e6:.1f} MB of KV), float64 numpy, "
-                      f"one thread, {dt:.1f} s",
-            "us_per_step_extrapolated": round(dt / n * w.num_seqs * 1e6, 1)}
+                      + (f"{processes} processes" if processes > 1 else "one thread")
+                      + f", {dt:.1f} s",
+            "us_per_step_extrapolated": round(dt / n * processes * w.num_seqs * 1e6, 1)}
 
 
 def block_ops(w, dev, reps: int = 10) -> dict:
@@ -489,56 +556,84 @@ def _block_kw(args) -> dict:
     return {"block_size": args.block_size} if args.block_size else {}
 
 
-def main() -> int:
-    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
-    ap.add_argument("--partition-size", type=int, default=None)
-    ap.add_argument("--block-size", type=int, default=None,
-                    help="tokens per block (default: the workload's own, 16 or 32)")
-    ap.add_argument("--layers", type=int, default=None, help="layer cache pools to cycle through")
-    ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying a graph")
-    ap.add_argument("--flush", action="store_true",
-                    help="also evict caches before every per-kernel timing launch")
-    ap.add_argument("--separate-slot-mapping", action="store_true",
-                    help="derive the new tokens' slots and write their K/V in two launches "
-                         "(paged_kv_slot_mapping, paged_kv_write) instead of one "
-                         "(paged_kv_write_positions)")
-    ap.add_argument("--separate-write", action="store_true",
-                    help="write the new tokens in a launch of their own (paged_kv_write_positions) "
-                         "instead of inside the attention launch")
-    ap.add_argument("--no-shared-prefix", action="store_true",
-                    help="forked workloads: read the shared prompt per sequence (the ordinary "
-                         "decode) instead of once per group")
-    ap.add_argument("--kv-flags", choices=["auto", "streamed", "cached"], default="auto",
-                    help="K/V loads: nontemporal streaming or through the caches (auto: cached "
-                         "for forked workloads, whose shared blocks are read by several "
-                         "workgroups, else streamed)")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-block-ops", action="store_true",
-                    help="skip the copy-on-write and swap copy timings")
-    ap.add_argument("--copy-calibration", action="store_true",
-                    help="only run a plain 1 GiB device-to-device copy (known bytes), for "
-                         "scaling hardware byte counters")
-    ap.add_argument("--summarize-counters", metavar="DIR",
-                    help="no GPU: turn rocprofv3 FETCH_SIZE / WRITE_SIZE passes of this workload "
-                         "and of --copy-calibration (DIR/{FETCH_SIZE,WRITE_SIZE,cal_FETCH_SIZE,"
-                         "cal_WRITE_SIZE}) into HBM bytes per attention launch in "
-                         "profiles/attention_traffic.json")
-    args = ap.parse_args()
+# the five decode workloads, in the order their shapes are listed
+ALL_DECODE = ["tiny", "opt13b_mha", "qwen2_gqa", "shared_prefix", "long_context"]
 
-    if args.summarize_counters:
-        return summarize_counters(args.summarize_counters, args.workload)
 
-    world = int(os.environ.get("WORLD_SIZE", "1"))
-    if args.gpus != 1 or world != 1:
-        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}): "
-              "the decode path runs on a single MI355X.", file=sys.stderr)
-        return 2
+def _graph_avg_us(dev, fns, reps: int, replays: int = 1):
+    """Average launch duration (us) of ``reps`` consecutive launches of the
+    callables ``fns[r % len(fns)]`` (each given the capturing stream's
+    handle), captured in one HIP graph: HIP events on the launch stream
+    around each replay, divided by ``reps``.  One value per replay."""
+    import torch
+    cur = torch.cuda.current_stream(dev)
+    g = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream(device=dev)
+    cap.wait_stream(cur)
+    with torch.cuda.stream(cap):
+        fns[0](cap.cuda_stream)
+        cap.synchronize()
+        with torch.cuda.graph(g, stream=cap):
+            for r in range(reps):
+                fns[r % len(fns)](cap.cuda_stream)
+    cur.wait_stream(cap)
+    torch.cuda.synchronize()
+    g.replay()  # untimed
+    out = []
+    for _ in range(replays):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(cur)
+        g.replay()
+        b.record(cur)
+        torch.cuda.synchronize()
+        out.append(a.elapsed_time(b) * 1e3 / reps)
+    del g
+    return out
 
+
+def _dist(xs) -> dict:
+    import numpy as np
+    return {"p10": round(float(np.percentile(xs, 10)), 2), "p50": round(float(np.percentile(xs, 50)), 2),
+            "p90": round(float(np.percentile(xs, 90)), 2), "samples": len(xs)}
+
+
+def read_ceiling(dev, nbytes: int) -> dict:
+    """Best streaming-read rate (GB/s) of ``pkv_read_ceiling`` over a sweep
+    of grids and loads in flight, reading ``nbytes`` per launch: a graph of
+    launches cycling distinct buffers (at least 1 GiB in all, so no launch
+    finds its bytes in the 256 MB memory-side cache, for sizes from 16 MB)."""
+    import torch
+
+    from paged_kv_cache_81_amd._lib import check, lib
+    nbytes = max(16, nbytes // 16 * 16)
+    # (at most 64 buffers: below ~16 MB a launch is bound by its own start and
+    # end, not by where its bytes come from)
+    nbuf = min(64, max(2, -(-(1 << 30) // nbytes)))
+    bufs = [torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(i % 200 + 1)
+            for i in range(nbuf)]
+    sink = torch.empty(1 << 16, dtype=torch.int32, device=dev)
+    reps = max(nbuf, min(100, max(10, (2 << 30) // nbytes)))
+    best = None
+    for grid in (512, 768, 1024, 1536, 2048, 3072):
+        for per in (2, 4):
+            fns = [(lambda sh, b=b, grid=grid, per=per: check(
+                lib.pkv_read_ceiling(b.data_ptr(), nbytes, grid, per, sink.data_ptr(), sh),
+                "read ceiling")) for b in bufs]
+            us = min(_graph_avg_us(dev, fns, reps, replays=3))
+            gbps = nbytes / (us * 1e-6) / 1e9
+            if best is None or gbps > best["GBps"]:
+                best = {"GBps": round(gbps, 1), "us": round(us, 2), "grid": grid,
+                        "loads_in_flight": per}
+    del bufs, sink
+    torch.cuda.empty_cache()
+    best["bytes"] = nbytes
+    return best
+
+
+def decode_bench(name, args, dev, headline: bool) -> dict:
+    """One decode workload: the timed steps (write + attention + merge,
+    cycling layer pools, in one graph), each kernel alone, and the
+    headline's block copies.  Returns the result line's fields for it."""
     import numpy as np
     import torch
 
@@ -548,37 +643,13 @@ def main() -> int:
     from paged_kv_cache_81_amd._lib import check, lib
     from tests import gpu_harness as H
 
-    if not torch.cuda.is_available():
-        log("no GPU visible")
-        return 1
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    if args.copy_calibration:
-        src = torch.full((1 << 30,), 7, dtype=torch.uint8, device=dev)
-        dst = torch.empty_like(src)
-        for _ in range(5):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        print(json.dumps({"copy_bytes_read": 1 << 30, "copy_bytes_written": 1 << 30, "launches": 5}))
-        return 0
-
-    if args.workload in workloads.PREFILL:
-        result = prefill_bench(args, dev)
-        if not args.no_cpu_baseline:
-            log("[bench] timing the CPU oracle")
-            result["cpu_baseline"] = prefill_cpu_baseline(
-                workloads.PREFILL[args.workload](**_block_kw(args)), args.cpu_seconds)
-        print(json.dumps(result), flush=True)
-        return 0
-
     t = time.time()
-    w = workloads.make(args.workload, **_block_kw(args))
+    w = workloads.make(name, **_block_kw(args))
     log(f"[bench] workload {w.name}: S={w.num_seqs} Hq={w.num_q_heads} Hkv={w.num_kv_heads} "
         f"D={w.head_size} B={w.block_size} NB={w.num_blocks} sumL={int(w.context_lens.sum())} "
         f"(generated in {time.time() - t:.1f} s)")
     st = H.upload(w, device=dev)
     torch.cuda.synchronize()
-    log("[bench] inputs resident, pool filled")
 
     S, B, NB = w.num_seqs, w.block_size, w.num_blocks
     Hq, Hkv, D = w.num_q_heads, w.num_kv_heads, w.head_size
@@ -714,6 +785,7 @@ def main() -> int:
         run_steps()  # one untimed replay
         torch.cuda.synchronize()
 
+    # exactly K steps between two synchronisations: the step time
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -724,23 +796,34 @@ def main() -> int:
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     ms_per_step = t0.elapsed_time(t1) / args.steps
-    log(f"[bench] {args.steps} steps: {ms_per_step * 1e3:.1f} us/step (wall {wall / args.steps * 1e6:.1f} us)")
+    log(f"[bench] {w.name}: {args.steps} steps: {ms_per_step * 1e3:.1f} us/step "
+        f"(wall {wall / args.steps * 1e6:.1f} us)")
+    # the same replay a few more times, for the spread of the step time
+    step_us = [ms_per_step * 1e3]
+    for _ in range(args.spread_replays):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(cur)
+        run_steps()
+        b.record(cur)
+        torch.cuda.synchronize()
+        step_us.append(a.elapsed_time(b) * 1e3 / args.steps)
     eager_step((args.steps - 1) % nl if nl > 1 else 0)
     torch.cuda.synchronize()
     if not torch.equal(out, ref_out):
-        log("[bench] the timed steps' output differs from the first eager step's")
-        return 1
+        raise SystemExit(f"[bench] {w.name}: the timed steps' output differs from the first "
+                         "eager step's")
 
     # each kernel on its own, `reps` launches in a row cycling through the
     # layer pools: HIP events on the launch stream around one replay of a
     # graph holding those launches, divided by `reps` -- the kernel's average
-    # launch duration, as a kernel trace reports it.  (Event pairs around
-    # single launches add the events' own few microseconds to each.)  With
-    # --flush: eager launches, each after a cache-evicting fill and a spin
-    # that keeps the GPU busy while the host queues the event pair.
+    # launch duration, as a kernel trace reports it (event pairs around
+    # single launches add the events' own few microseconds to each); the
+    # graph is replayed several times for the spread.  With --flush: eager
+    # launches, each after a cache-evicting fill and a spin that keeps the
+    # GPU busy while the host queues the event pair.
     reps = max(10, min(args.steps, 100))
     names = list(eager[0])
-    kernel_us = {}
+    kernel_us, kernel_dist = {}, {}
     if args.flush:
         flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -748,40 +831,29 @@ def main() -> int:
         per = {k: [] for k in names}
         i = 0
         for r in range(reps):
-            for name, f in eager[r % nl].items():
+            for kname_, f in eager[r % nl].items():
                 flush.fill_(r & 0xFF)
                 torch.cuda._sleep(SPIN_CYCLES)
                 ev[i][0].record(cur)
                 f()
                 ev[i][1].record(cur)
-                per[name].append(i)
+                per[kname_].append(i)
                 i += 1
         torch.cuda.synchronize()
-        kernel_us = {k: float(np.mean([ev[j][0].elapsed_time(ev[j][1]) for j in idx])) * 1e3
-                     for k, idx in per.items()}
+        for k, idx in per.items():
+            xs = [ev[j][0].elapsed_time(ev[j][1]) * 1e3 for j in idx]
+            kernel_us[k] = float(np.mean(xs))
+            kernel_dist[k] = _dist(xs)
+        del flush
     else:
-        for name in names:
-            g = torch.cuda.CUDAGraph()
-            cap = torch.cuda.Stream(device=dev)
-            cap.wait_stream(cur)
-            with torch.cuda.stream(cap):
-                fs = [calls(cap.cuda_stream, layer)[name] for layer in range(nl)]
-                fs[0]()
-                cap.synchronize()
-                with torch.cuda.graph(g, stream=cap):
-                    for r in range(reps):
-                        fs[r % nl]()
-            cur.wait_stream(cap)
-            torch.cuda.synchronize()
-            g.replay()  # untimed
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record(cur)
-            g.replay()
-            b.record(cur)
-            torch.cuda.synchronize()
-            kernel_us[name] = a.elapsed_time(b) * 1e3 / reps
-            del g
-    log("[bench] per-kernel us: " + ", ".join(f"{k} {v:.1f}" for k, v in kernel_us.items()))
+        for kname_ in names:
+            fns = [(lambda sh, layer=layer, kname_=kname_: calls(sh, layer)[kname_]())
+                   for layer in range(nl)]
+            xs = _graph_avg_us(dev, fns, reps, replays=1 + args.spread_replays)
+            kernel_us[kname_] = xs[0]
+            kernel_dist[kname_] = _dist(xs)
+    log(f"[bench] {w.name}: per-kernel us: " +
+        ", ".join(f"{k} {v:.1f}" for k, v in kernel_us.items()))
 
     kvb = kv_bytes(w)
     ukvb = unique_kv_bytes(w)
@@ -796,21 +868,12 @@ def main() -> int:
     traffic = measured_traffic(w.name, B, kname)
 
     result = {
-        "metric": METRIC,
         "value": round(value, 2),
-        "unit": "GB/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 5),
         "us_per_step": round(ms_per_step * 1e3, 2),
+        "us_per_step_dist": _dist(step_us),
         "hbm_frac_step": round(value / PEAK_HBM_GBPS, 4),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
         "dtype": "bf16" if dt else "f32",
-        "accumulate": "f32",
-        "data": "synthetic (seeded N(0,1) K/V/q, shuffled block pool)",
         "config": {
             "workload": w.name, "num_seqs": S, "num_q_heads": Hq, "num_kv_heads": Hkv,
             "head_size": D, "block_size": B, "num_blocks": NB,
@@ -847,14 +910,264 @@ def main() -> int:
                        f"cold: launches cycle through {nl} layer pools" if nl > 1 else "warm"),
         },
         "kernel_us": {k: round(v, 2) for k, v in kernel_us.items()},
-        "kernel_source_sha": kernel_source_sha(),
+        "kernel_us_dist": {**kernel_dist,
+                           "what": ("per-launch average over each of several replays of the "
+                                    f"graph of {reps} launches" if not args.flush else
+                                    "single launches")},
     }
-    if not args.no_block_ops:
+    if headline and not args.no_block_ops:
         result["block_ops"] = block_ops(w, dev)
         log(f"[bench] block ops: {result['block_ops']}")
-    if not args.no_cpu_baseline:
-        log("[bench] timing the CPU oracle")
-        result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    del pools, st, ws, out, eager
+    if not args.no_graph:
+        del graph
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return result, w
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD,
+                    help="the line's headline workload (the other decode workloads are "
+                         "reported under configs unless --only)")
+    ap.add_argument("--only", action="store_true",
+                    help="measure the headline workload alone (no configs, no ceiling sweep)")
+    ap.add_argument("--partition-size", type=int, default=None)
+    ap.add_argument("--block-size", type=int, default=None,
+                    help="tokens per block (default: the workload's own, 16 or 32)")
+    ap.add_argument("--layers", type=int, default=None, help="layer cache pools to cycle through")
+    ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying a graph")
+    ap.add_argument("--flush", action="store_true",
+                    help="also evict caches before every per-kernel timing launch")
+    ap.add_argument("--separate-slot-mapping", action="store_true",
+                    help="derive the new tokens' slots and write their K/V in two launches "
+                         "(paged_kv_slot_mapping, paged_kv_write) instead of one "
+                         "(paged_kv_write_positions)")
+    ap.add_argument("--separate-write", action="store_true",
+                    help="write the new tokens in a launch of their own (paged_kv_write_positions) "
+                         "instead of inside the attention launch")
+    ap.add_argument("--no-shared-prefix", action="store_true",
+                    help="forked workloads: read the shared prompt per sequence (the ordinary "
+                         "decode) instead of once per group")
+    ap.add_argument("--kv-flags", choices=["auto", "streamed", "cached"], default="auto",
+                    help="K/V loads: nontemporal streaming or through the caches (auto: cached "
+                         "for forked workloads, whose shared blocks are read by several "
+                         "workgroups, else streamed)")
+    ap.add_argument("--ceilings", metavar="NAME=BYTES,...",
+                    help="only measure the streaming-read ceiling at these bytes per launch "
+                         "(JSON on stdout); the default run asks a child process for it")
+    ap.add_argument("--spread-replays", type=int, default=10,
+                    help="extra replays of each timing graph, for p10/p50/p90")
+    ap.add_argument("--cpu-seconds", type=float, default=6.0,
+                    help="CPU oracle seconds per setting for the headline workload (a third "
+                         "of it for the others)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-block-ops", action="store_true",
+                    help="skip the copy-on-write and swap copy timings")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy (known bytes), for "
+                         "scaling hardware byte counters")
+    ap.add_argument("--summarize-counters", metavar="DIR",
+                    help="no GPU: turn rocprofv3 FETCH_SIZE / WRITE_SIZE passes of this workload "
+                         "and of --copy-calibration (DIR/{FETCH_SIZE,WRITE_SIZE,cal_FETCH_SIZE,"
+                         "cal_WRITE_SIZE}) into HBM bytes per attention launch in "
+                         "profiles/attention_traffic.json")
+    args = ap.parse_args()
+
+    if args.summarize_counters:
+        return summarize_counters(args.summarize_counters, args.workload)
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}): "
+              "the decode path runs on a single MI355X.", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import workloads
+
+    if args.ceilings:
+        if not torch.cuda.is_available():
+            log("no GPU visible")
+            return 1
+        dev = torch.device("cuda:0")
+        torch.cuda.set_device(dev)
+        out = {}
+        for item in args.ceilings.split(","):
+            name, nbytes = item.split("=")
+            out[name] = read_ceiling(dev, int(nbytes))
+            log(f"[bench] ceiling {name}: {out[name]['GBps']} GB/s at {nbytes} bytes")
+        print(json.dumps(out), flush=True)
+        return 0
+
+    # The CPU oracle runs first, before anything initialises the GPU: its
+    # all-core setting forks worker processes, which must not inherit a
+    # live GPU runtime.
+    decode_names = []
+    if args.workload not in workloads.PREFILL and not args.copy_calibration:
+        decode_names = [args.workload] if args.only else \
+            [args.workload] + [n for n in ALL_DECODE if n != args.workload]
+    cpu = {}
+    if not args.no_cpu_baseline and decode_names:
+        cores = cpu_share()
+        for name in decode_names:
+            w = workloads.make(name, **_block_kw(args))
+            secs = args.cpu_seconds if name == args.workload else args.cpu_seconds / 3
+            log(f"[bench] CPU oracle on {name}: 1 process, then {cores}")
+            one = cpu_baseline(w, secs, 1)
+            one["all_cores"] = cpu_baseline(w, secs, cores)
+            cpu[name] = one
+            del w
+
+    if not args.only and decode_names:
+        return all_configs(args, decode_names, cpu)
+
+    if not torch.cuda.is_available():
+        log("no GPU visible")
+        return 1
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    if args.copy_calibration:
+        src = torch.full((1 << 30,), 7, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": 1 << 30, "copy_bytes_written": 1 << 30, "launches": 5}))
+        return 0
+
+    if args.workload in workloads.PREFILL:
+        result = prefill_bench(args, dev)
+        if not args.no_cpu_baseline:
+            log("[bench] timing the CPU oracle")
+            result["cpu_baseline"] = prefill_cpu_baseline(
+                workloads.PREFILL[args.workload](**_block_kw(args)), args.cpu_seconds)
+        print(json.dumps(result), flush=True)
+        return 0
+
+    name = decode_names[0]
+    r, _ = decode_bench(name, args, dev, headline=True)
+    result = line_of(args, r)
+    if name in cpu:
+        result["cpu_baseline"] = cpu[name]
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+def line_of(args, head: dict) -> dict:
+    """The result line's fields for one workload's measurement."""
+    result = {
+        "metric": METRIC,
+        "value": head["value"],
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": head["ms_per_step"],
+        "us_per_step": head["us_per_step"],
+        "hbm_frac_step": head["hbm_frac_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": head["dtype"],
+        "accumulate": "f32",
+        "data": "synthetic (seeded N(0,1) K/V/q, shuffled block pool)",
+        "config": head["config"],
+        "roofline": head["roofline"],
+        "kernel_us": head["kernel_us"],
+        "kernel_us_dist": head["kernel_us_dist"],
+        "us_per_step_dist": head["us_per_step_dist"],
+        "kernel_source_sha": kernel_source_sha(),
+    }
+    if "block_ops" in head:
+        result["block_ops"] = head["block_ops"]
+    return result
+
+
+def _child(args, extra) -> dict:
+    """Run this script in a child process (a fresh GPU context) and parse
+    the JSON line it prints; its progress lines go to our stderr."""
+    import subprocess
+    cmd = [sys.executable, "-u", os.path.abspath(__file__), "--steps", str(args.steps),
+           "--warmup", str(args.warmup), "--spread-replays", str(args.spread_replays)]
+    for flag in ("flush", "no_graph", "separate_write", "separate_slot_mapping",
+                 "no_shared_prefix"):
+        if getattr(args, flag):
+            cmd.append("--" + flag.replace("_", "-"))
+    if args.kv_flags != "auto":
+        cmd += ["--kv-flags", args.kv_flags]
+    if args.block_size:
+        cmd += ["--block-size", str(args.block_size)]
+    p = subprocess.run(cmd + extra, stdout=subprocess.PIPE, text=True)
+    if p.returncode != 0:
+        raise SystemExit(f"[bench] child {' '.join(extra)} failed ({p.returncode})")
+    return json.loads(p.stdout.strip().splitlines()[-1])
+
+
+def all_configs(args, names, cpu) -> int:
+    """Every decode workload, each measured by a child process of its own
+    (what a process did before carries over: the long-context attention
+    measured 4% slower after the other workloads than alone), then the
+    streaming-read ceilings at 2 GiB and at each workload's bytes per launch,
+    assembled into one line headed by args.workload."""
+    runs = {}
+    for name in names:
+        extra = ["--workload", name, "--only", "--no-cpu-baseline"]
+        if name != args.workload or args.no_block_ops:
+            extra.append("--no-block-ops")
+        runs[name] = _child(args, extra)
+    # (each size in a process of its own too: a second 2 GiB sweep in one
+    # process measured 5% below the first)
+    sizes = {"2GiB": 2 << 30}
+    sizes.update({n: r["roofline"]["algorithmic_bytes"] for n, r in runs.items()})
+    ceiling = {}
+    for k, v in sizes.items():
+        ceiling.update(_child(args, ["--ceilings", f"{k}={v}"]))
+
+    result = dict(runs[args.workload])
+    result["ceiling"] = {
+        "GBps_2GiB": ceiling["2GiB"]["GBps"],
+        "frac_of_peak": round(ceiling["2GiB"]["GBps"] / PEAK_HBM_GBPS, 4),
+        "kernel": "pkv_read_ceiling (nontemporal 16-byte grid-stride reads; best of grids "
+                  "512-3072 x 2 or 4 loads in flight)",
+        "size_matched_GBps": ceiling[args.workload]["GBps"],
+    }
+    result["frac_of_ceiling"] = round(result["roofline"]["achieved"] /
+                                      ceiling[args.workload]["GBps"], 4)
+    if args.workload in cpu:
+        result["cpu_baseline"] = cpu[args.workload]
+    configs = {}
+    for name, r in runs.items():
+        roof = r["roofline"]
+        c = {
+            "us_per_step": r["us_per_step"],
+            "us_per_step_dist": r["us_per_step_dist"],
+            "step_GBps": r["value"],
+            "kernel_us": r["kernel_us"],
+            "kernel_us_dist": {k: v for k, v in r["kernel_us_dist"].items() if k != "what"},
+            "attention_GBps": roof["achieved"],
+            "attention_logical_GBps": roof["logical_GBps"],
+            "roofline": {"frac": roof["frac"], "traffic": roof["traffic"],
+                         "kernel": roof["kernel"], "algorithmic_bytes": roof["algorithmic_bytes"],
+                         "logical_bytes": roof["logical_bytes"]},
+            "ceiling_GBps": ceiling[name]["GBps"],
+            "frac_of_ceiling": round(roof["achieved"] / ceiling[name]["GBps"], 4),
+            "config": {k: r["config"][k] for k in ("num_seqs", "num_q_heads", "num_kv_heads",
+                                                   "head_size", "block_size", "kv_write",
+                                                   "attention_path", "kv_flags",
+                                                   "layers_cycled")},
+            "dtype": r["dtype"],
+        }
+        if name in cpu:
+            c["cpu_baseline"] = cpu[name]
+        configs[name] = c
+    result["configs"] = configs
+    result["measured"] = "each workload and the ceilings in a fresh child process"
     print(json.dumps(result), flush=True)
     return 0
 

@@ -609,6 +609,19 @@ int pkv_bm_block_hash(pkv_block_manager* bm, int block, uint8_t* out);
 /* 1 when the prefix cache maps the block's hash to this block */
 int pkv_bm_is_cached(pkv_block_manager* bm, int block);
 
+/*
+ * pkv_read_ceiling -- a measurement utility, not part of the decode path:
+ * read `bytes` (a multiple of 16) of device memory at `buf` (16-byte
+ * aligned) once, with `grid` workgroups of 256 threads each keeping
+ * `loads_in_flight` (1, 2, 4 or 8) nontemporal 16-byte loads in flight, and
+ * write one word per workgroup to sink[0 .. grid) (device).  Timed by the
+ * caller, it gives the streaming-read rate the decode kernels' HBM rates are
+ * compared with at the same bytes per launch.  Errors: PKV_ERR_INVALID (null
+ * pointers, alignment, grid outside [1, 2^20]), PKV_ERR_UNSUPPORTED.
+ */
+int pkv_read_ceiling(const void* buf, size_t bytes, int grid, int loads_in_flight, unsigned* sink,
+                     hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

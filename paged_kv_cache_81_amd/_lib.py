@@ -28,6 +28,7 @@ _SHARED = (_i, [_p, _i, _p, _p, _p, _i, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, 
                 _sz, _i, _u, _p])
 SIGNATURES = {
     "pkv_last_error": (ctypes.c_char_p, []),
+    "pkv_read_ceiling": (_i, [_p, _sz, _i, _i, _p, _p]),
     "paged_kv_slot_mapping": (_i, [_p, _p, _i, _p, _p, _i, _i, _i, _i, _p]),
     "paged_kv_write": (_i, [_p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _p]),
     "paged_kv_write_positions": (_i, [_p, _p, _p, _p, _i, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i,
