@@ -272,6 +272,7 @@ def cpu_baseline(w, seconds: float, processes: int = 1) -> dict:
         done = sum(p[0] for p in parts)
         n = sum(p[1] for p in parts)
         dt = max(p[2] for p in parts)
+    step_bytes = int(w.context_lens.sum()) * _CPU_JOB["per_tok"]
     _CPU_JOB.clear()
     return {"value": round(done / dt / 1e9, 4), "unit": "GB/s", "cores": processes,
             "kind": "oracle", "cpu": cpu_model(),
@@ -279,7 +280,7 @@ def cpu_baseline(w, seconds: float, processes: int = 1) -> dict:
                       f"its {w.num_seqs} sequences, {done / 1e6:.1f} MB of KV), float64 numpy, "
                       + (f"{processes} processes" if processes > 1 else "one thread")
                       + f", {dt:.1f} s",
-            "us_per_step_extrapolated": round(dt / n * processes * w.num_seqs * 1e6, 1)}
+            "us_per_step_extrapolated": round(step_bytes / (done / dt) * 1e6, 1)}
 
 
 def block_ops(w, dev, reps: int = 10) -> dict:
