@@ -699,13 +699,17 @@ int paged_attention_prefill(void* out, pkv_dtype out_dtype, const void* query,
   a.max_q = max_query_len;
   if (dtype == PKV_F32) return launch_prefill_f32(a, stream);
   a.qtiles = static_cast<int>(cdiv64(max_query_len, 128));
-  const int64_t total = static_cast<int64_t>(num_seqs) * num_q_heads * a.qtiles;
+  // One workgroup per (query tile, head).  A chunk has at most qtiles tiles,
+  // and chunks that follow each other in [0, num_tokens) (query_start
+  // non-decreasing) have at most one per 128 rows plus one each.
+  const int64_t tiles = std::min<int64_t>(static_cast<int64_t>(num_seqs) * a.qtiles,
+                                          cdiv64(num_tokens, 128) + num_seqs);
+  const int64_t total = tiles * num_q_heads;
   if (total > (int64_t{1} << 30)) {
     set_error("prefill grid of %lld work items is too large", static_cast<long long>(total));
     return PKV_ERR_UNSUPPORTED;
   }
   a.total = static_cast<int>(total);
-  a.items_per_xcd = static_cast<int>(cdiv64(total, 8));
   return launch_prefill_bf16(a, stream);
 }
 

@@ -214,9 +214,8 @@ struct PrefillArgs {
   float scale_log2;
   int out_bf16;
   int max_q;           // longest chunk the grid covers (longer ones give NaN)
-  int qtiles;          // query tiles per (sequence, head) in the grid
-  int items_per_xcd;   // work items each XCD takes
-  int total;           // work items: S * Hq * qtiles
+  int qtiles;          // query tiles per (sequence, head) at most
+  int total;           // work items (workgroups): tiles x Hq
 };
 
 int launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream);

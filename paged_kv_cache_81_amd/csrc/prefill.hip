@@ -5,18 +5,22 @@
 // of it sits at position lens[s] - chunk_len + i and attends keys 0 .. its
 // position of its own sequence, read through the block table.
 //
-// bf16 caches: a workgroup (4 waves) takes 128 query rows of one query head;
-// wave w takes rows 32w .. 32w + 31 as two 16-row column blocks.  Keys are
-// walked in steps of 64: the workgroup loads a step's K and V rows (through
-// the table) into one of two LDS buffers while the waves compute on the
-// other, so each K/V row is read from memory once per workgroup and 128
-// query rows use it.  Per 32 keys a wave runs, for each column block, the
-// scores S^T = K . Q^T on v_mfma_f32_16x16x32_bf16 (K rows from LDS as the
-// A operand, the query rows as B), the causal mask, an online softmax per
-// query row in the log2 domain, and O^T += V^T . P^T with P split into bf16
-// hi + lo parts and the values transposed in registers (dims permuted so
-// every LDS read is a contiguous piece of a V row).  Rows are finished
-// through LDS so every global store covers whole rows.
+// bf16 caches: a workgroup (4 waves) takes 128 query rows (a tile) of one
+// query head; wave w takes rows 32w .. 32w + 31 as two 16-row column blocks.
+// Workgroups take the tiles longest first (ranked in LDS by the keys they
+// read) with the heads of a tile innermost, so the work of every XCD is the
+// same and the launch ends on short tiles.  Keys are walked in steps of 64:
+// the workgroup loads a step's K and V rows (through the table) into one of
+// two LDS buffers while the waves compute on the other, so each K/V row is
+// read from memory once per workgroup and 128 query rows use it.  Per 32
+// keys a wave runs, for each column block, the scores S^T = K . Q^T on
+// v_mfma_f32_16x16x32_bf16 (K rows from LDS as the A operand, the query rows
+// as B), the causal mask, an online softmax per query row in the log2
+// domain whose reference max moves only in jumps (few accumulator
+// rescales), and O^T += V^T . P^T with P split into bf16 hi + lo parts and
+// the V^T operand read from the row-major V tile by gfx950's transposing LDS
+// read.  Rows are finished through LDS so every global store covers whole
+// rows.
 //
 // fp32 caches: one wave per (query row, head), keys in batches of 64 with an
 // online softmax (vector ALU; a reference-precision path).
@@ -30,16 +34,20 @@ namespace {
 constexpr int kPThreads = 256;
 constexpr int kPRows = 128;  // query rows per workgroup (4 waves x 32)
 constexpr int kPKeys = 64;   // keys per LDS step
-constexpr int kXcds = 8;
+// tile costs (64-key steps) the launch orders its work by, counted exactly below this
+constexpr int kRankBins = 1024;
+// how far (log2 units) a row's max may pass its reference before a rescale
+constexpr float kLazyLog2 = 8.f;
 
 template <int D>
 struct PGeom {
   static constexpr int QC = D / 32;   // score MFMAs per 16 x 16 tile
   static constexpr int NV = D / 16;   // output blocks; dims per lane per V row
-  static constexpr int NW = NV / 2;   // 32-bit words per lane per V row
   static constexpr int NCH = D / 8;   // 16-byte chunks per row
   static constexpr int KROW = 2 * D;  // LDS bytes per K row (chunks skewed)
-  static constexpr int VROW = 2 * D + 16;  // LDS bytes per V row (padded)
+  // LDS bytes per V row, padded so the 8 rows x 32 bytes of a transposed
+  // read's half-wave fall on distinct banks
+  static constexpr int VROW = 2 * D + 32;
   static constexpr int KBYTES = kPKeys * KROW;
   static constexpr int BUF = KBYTES + kPKeys * VROW;
   static constexpr int CPT = kPKeys * NCH / kPThreads;  // chunks per thread per tensor
@@ -62,39 +70,169 @@ __device__ __forceinline__ float max_xor32(float v) {
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+
+// ds_read_b64_tr_b16 at an LDS byte address given as a generic pointer into
+// the dynamic LDS array
+__device__ __forceinline__ bf16x4 lds_read_tr16(const char* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(const_cast<char*>(p)));
+}
+
 // chunk ch of K row t sits at chunk position (ch + kskew(t)) mod NCH, so both
 // the row-wise stores and the MFMA-layout reads (16 rows, one chunk each)
 // spread over the banks
 template <int NCH>
 __device__ __forceinline__ int kskew(int t) { return (t * NCH / 16) % NCH; }
 
+// A sequence's chunk as the launch sees it: its tiles of up to 128 rows
+// (none when the rows lie outside the output; at most the grid's qtiles),
+// and whether it is bad (its tiles then write NaN rows only).
+struct SeqShape {
+  int q0, qlen, L, ntiles;
+  bool bad;
+};
+
+template <int B>
+__device__ __forceinline__ SeqShape seq_shape(const PrefillArgs& a, int s) {
+  SeqShape r;
+  r.q0 = a.qstart[s];
+  r.qlen = a.qstart[s + 1] - r.q0;
+  r.L = a.lens[s];
+  r.ntiles = 0;
+  r.bad = false;
+  if (r.q0 < 0 || r.qlen < 0 || r.q0 + r.qlen > a.T) return r;  // rows outside the output
+  r.bad = r.L < 0 || (r.L + B - 1) / B > a.width || r.qlen > r.L || r.qlen > a.max_q;
+  r.ntiles = min((r.qlen + kPRows - 1) / kPRows, a.qtiles);
+  return r;
+}
+
+// What tile x of a chunk costs: the 64-key steps it reads (capped; 0 for a
+// bad sequence)
+__device__ __forceinline__ int tile_key(const SeqShape& q, int x) {
+  if (q.bad) return 0;
+  const int row0 = x * kPRows;
+  const int kend = max(0, min(q.L, q.L - q.qlen + row0 + min(kPRows, q.qlen - row0)));
+  return min((kend + kPKeys - 1) / kPKeys, kRankBins - 1);
+}
+
+// Exclusive prefix sum of v over the workgroup; *total gets the sum.  Uses
+// wsum[4]; the caller separates two calls by a barrier.
+__device__ __forceinline__ int block_exclusive_scan(int v, int* wsum, int* total) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int t = __shfl_up(x, d, 64);
+    if (lane >= d) x += t;
+  }
+  if (lane == 63) wsum[wv] = x;
+  __syncthreads();
+  int before = 0, all = 0;
+#pragma unroll
+  for (int w = 0; w < kPThreads / 64; ++w) {
+    const int t = wsum[w];
+    before += w < wv ? t : 0;
+    all += t;
+  }
+  *total = all;
+  return before + x - v;
+}
+
+// The tile of rank r when the launch's tiles are ordered by tile_key,
+// largest first (equal keys: by sequence, then tile).  A counting sort in
+// LDS (sm: kRankBins + 16 ints): the histogram of keys, the bin that holds
+// rank r, then that bin's tiles in order.  Every thread of the workgroup
+// calls it; false (for all of them) when r is past the last tile.
+template <int B>
+__device__ bool tile_of_rank(const PrefillArgs& a, int r, int* sm, int* s_out, int* x_out) {
+  int* hist = sm;
+  int* wsum = sm + kRankBins;
+  int* res = wsum + 8;
+  const int tid = threadIdx.x;
+  for (int i = tid; i < kRankBins; i += kPThreads) hist[i] = 0;
+  __syncthreads();
+  for (int s = tid; s < a.S; s += kPThreads) {
+    const SeqShape q = seq_shape<B>(a, s);
+    for (int x = 0; x < q.ntiles; ++x) atomicAdd(&hist[tile_key(q, x)], 1);
+  }
+  __syncthreads();
+  // thread t holds the bins of keys kRankBins - 1 - PER t - k, k < PER
+  constexpr int PER = kRankBins / kPThreads;
+  int c[PER], mine = 0;
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    c[k] = hist[kRankBins - 1 - (PER * tid + k)];
+    mine += c[k];
+  }
+  int all;
+  const int before = block_exclusive_scan(mine, wsum, &all);
+  if (r >= all) return false;
+  if (r >= before && r < before + mine) {
+    int cum = before;
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      if (r >= cum && r < cum + c[k]) {
+        res[0] = kRankBins - 1 - (PER * tid + k);
+        res[1] = r - cum;
+      }
+      cum += c[k];
+    }
+  }
+  __syncthreads();
+  const int key = res[0], j = res[1];
+  // the j-th tile with that key: thread t counts those of a contiguous run of sequences
+  const int per_s = (a.S + kPThreads - 1) / kPThreads;
+  const int s0 = tid * per_s, s1 = min(a.S, s0 + per_s);
+  int n = 0;
+  for (int s = s0; s < s1; ++s) {
+    const SeqShape q = seq_shape<B>(a, s);
+    for (int x = 0; x < q.ntiles; ++x) n += tile_key(q, x) == key;
+  }
+  int all2;
+  const int b2 = block_exclusive_scan(n, wsum, &all2);
+  if (j >= b2 && j < b2 + n) {
+    int cum = b2;
+    for (int s = s0; s < s1; ++s) {
+      const SeqShape q = seq_shape<B>(a, s);
+      for (int x = 0; x < q.ntiles; ++x) {
+        if (tile_key(q, x) != key) continue;
+        if (cum == j) {
+          res[2] = s;
+          res[3] = x;
+        }
+        ++cum;
+      }
+    }
+  }
+  __syncthreads();
+  *s_out = res[2];
+  *x_out = res[3];
+  return true;
+}
+
 template <int D, int B>
 __global__ void __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(2)))
 prefill_bf16_kernel(PrefillArgs a) {
   using Gm = PGeom<D>;
-  constexpr int QC = Gm::QC, NV = Gm::NV, NW = Gm::NW, NCH = Gm::NCH, CPT = Gm::CPT;
+  constexpr int QC = Gm::QC, NV = Gm::NV, NCH = Gm::NCH, CPT = Gm::CPT;
   extern __shared__ __align__(16) char lds[];
   const int tid = threadIdx.x;
   const int wv = tid >> 6, lane = tid & 63, j = lane & 15, g = lane >> 4;
 
-  // XCD-blocked numbering: XCD b % 8 runs items [b%8 * per, ...), so the
-  // items of one (sequence, kv head) share an L2; within a (sequence, head)
-  // the latest (longest) query tile comes first
+  // Work item: (tile of rank r, head h), heads innermost.  Tiles are ranked
+  // longest first, so the launch ends on short items, and the heads of each
+  // tile spread over the XCDs (workgroup b runs on XCD b % 8), which keeps
+  // the XCDs' shares of the work equal whatever the batch's length mix.
   const int bid = blockIdx.x;
-  const int item = (bid % kXcds) * a.items_per_xcd + bid / kXcds;
-  if (item >= a.total) return;
-  const int xr = item % a.qtiles;
-  const int sh = item / a.qtiles;
-  const int h = sh % a.Hq, s = sh / a.Hq;
-  const int x = a.qtiles - 1 - xr;
-  const int q0 = a.qstart[s];
-  const int qlen = a.qstart[s + 1] - q0;
-  if (q0 < 0 || qlen < 0 || q0 + qlen > a.T) return;  // rows outside the output
+  const int h = bid % a.Hq;
+  int s, x;
+  if (!tile_of_rank<B>(a, bid / a.Hq, reinterpret_cast<int*>(lds + Gm::BUF), &s, &x)) return;
+  const SeqShape sq = seq_shape<B>(a, s);
+  const int q0 = sq.q0, qlen = sq.qlen, L = sq.L;
+  const bool bad_seq = sq.bad;
   const int row0 = x * kPRows;
-  if (row0 >= qlen) return;
-  const int L = a.lens[s];
   const int G = a.Hq / a.Hkv, kvh = h / G;
-  const bool bad_seq = L < 0 || (L + B - 1) / B > a.width || qlen > L || qlen > a.max_q;
   const int tile_rows = min(kPRows, qlen - row0);
   const int P0 = L - qlen + row0;  // position of the tile's first row
   const int kend = bad_seq ? 0 : max(0, min(L, P0 + tile_rows));  // keys [0, kend)
@@ -232,10 +370,19 @@ prefill_bf16_kernel(PrefillArgs a) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) mx = fmaxf(mx, xs[u][r]);
       mx = max_xor32(max_xor16(mx));
-      const float m_new = fmaxf(m_run[cb], mx * sl2);
-      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-      alpha[cb] = wave::fast_exp2(m_run[cb] - m_use);
-      m_run[cb] = m_new;
+      // The reference max m_run moves only when this step's max passes it
+      // by more than kLazyLog2: the weights then stay below 2^kLazyLog2
+      // (still exact to ~16 bits in the hi + lo split, sums far from
+      // overflow) and the accumulators are rescaled on few steps instead of
+      // on almost every one.  A row's first keys set it without a rescale
+      // (nothing is accumulated yet).
+      const float mxs = mx * sl2;
+      alpha[cb] = 1.f;
+      if (mxs > m_run[cb] + kLazyLog2) {
+        if (m_run[cb] != -INFINITY) alpha[cb] = wave::fast_exp2(m_run[cb] - mxs);
+        m_run[cb] = mxs;
+      }
+      const float m_use = (m_run[cb] == -INFINITY) ? 0.f : m_run[cb];
       float psum = 0.f;
 #pragma unroll
       for (int u = 0; u < 2; ++u)
@@ -265,31 +412,18 @@ prefill_bf16_kernel(PrefillArgs a) {
 #pragma unroll
         for (int n = 0; n < NV; ++n) acc[cb][n] *= al[cb];
     }
-    // V rows 4g + r of each 16-key tile: dims NV*j .. NV*j + NV - 1
-    wave::Words<NW> vw[2][4];
-#pragma unroll
-    for (int u = 0; u < 2; ++u)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const char* vp = buf + Gm::KBYTES + (32 * hs + 16 * u + 4 * g + r) * Gm::VROW + 2 * NV * j;
-        if constexpr (NW == 4) {
-          const wave::u32x4 v4 = *reinterpret_cast<const wave::u32x4*>(vp);
-          vw[u][r].w[0] = v4.x; vw[u][r].w[1] = v4.y; vw[u][r].w[2] = v4.z; vw[u][r].w[3] = v4.w;
-        } else {
-          const wave::u32x2 v2 = *reinterpret_cast<const wave::u32x2*>(vp);
-          vw[u][r].w[0] = v2.x; vw[u][r].w[1] = v2.y;
-        }
-      }
+    // O^T += V^T . P^T per 16-dim output block n.  The V^T operand comes
+    // straight from the row-major V tile: ds_read_b64_tr_b16 hands lane j of
+    // each 16-lane group column j of the 4-row x 16-column block its lanes
+    // address (lane j names row j/4, columns 4(j%4) .. +3).  Group g
+    // addresses keys 16u + 4g .. 16u + 4g + 3 of the substep -- the keys
+    // its P slots 4u .. 4u + 3 hold -- and dims 16n .. 16n + 15.
+    const char* vt = buf + Gm::KBYTES + (32 * hs + 4 * g + (j >> 2)) * Gm::VROW + 8 * (j & 3);
 #pragma unroll
     for (int n = 0; n < NV; ++n) {
-      const uint32_t sel = (n & 1) ? 0x07060302u : 0x05040100u;
-      wave::u32x4 va;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int e0 = 2 * e, e1 = 2 * e + 1;  // key slots (u = e/4, r = e%4)
-        va[e] = __builtin_amdgcn_perm(vw[e1 >> 2][e1 & 3].w[n >> 1], vw[e0 >> 2][e0 & 3].w[n >> 1], sel);
-      }
-      const bf16x8 vb = __builtin_bit_cast(bf16x8, va);
+      const bf16x4 v0 = lds_read_tr16(vt + 32 * n);
+      const bf16x4 v1 = lds_read_tr16(vt + 16 * Gm::VROW + 32 * n);
+      const bf16x8 vb = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
 #pragma unroll
       for (int cb = 0; cb < 2; ++cb) {
         f32x4 o = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vb, phi[cb], acc[cb][n], 0, 0, 0);
@@ -343,14 +477,12 @@ prefill_bf16_kernel(PrefillArgs a) {
     const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
     float* dst = rows + (wr0 + 16 * cb + j) * Gm::SROW;
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
-#pragma unroll
-      for (int n0 = 0; n0 < NV; n0 += 4) {
-        float4 o = make_float4(acc[cb][n0][r] * inv, acc[cb][n0 + 1][r] * inv,
-                               acc[cb][n0 + 2][r] * inv, acc[cb][n0 + 3][r] * inv);
-        if (bad) o = make_float4(NAN, NAN, NAN, NAN);
-        *reinterpret_cast<float4*>(dst + NV * (4 * g + r) + n0) = o;
-      }
+    for (int n = 0; n < NV; ++n) {  // dims 16n + 4g .. 16n + 4g + 3
+      float4 o = make_float4(acc[cb][n][0] * inv, acc[cb][n][1] * inv,
+                             acc[cb][n][2] * inv, acc[cb][n][3] * inv);
+      if (bad) o = make_float4(NAN, NAN, NAN, NAN);
+      *reinterpret_cast<float4*>(dst + 16 * n + 4 * g) = o;
+    }
   }
   __syncthreads();
   constexpr int D4 = D / 4;
@@ -484,7 +616,7 @@ int launch_bf16_db(const PrefillArgs& a, hipStream_t stream) {
   auto kern = prefill_bf16_kernel<D, B>;
   const int lds = PGeom<D>::LDS;
   if (const int rc = raise_lds_limit(reinterpret_cast<const void*>(kern), lds)) return rc;
-  kern<<<dim3(static_cast<unsigned>(a.items_per_xcd) * kXcds), dim3(kPThreads), lds, stream>>>(a);
+  kern<<<dim3(static_cast<unsigned>(a.total)), dim3(kPThreads), lds, stream>>>(a);
   return check_launch("paged prefill (bf16)");
 }
 
