@@ -698,13 +698,26 @@ int paged_attention_prefill(void* out, pkv_dtype out_dtype, const void* query,
   a.out_bf16 = out_dtype == PKV_BF16;
   a.max_q = max_query_len;
   if (dtype == PKV_F32) return launch_prefill_f32(a, stream);
-  a.qtiles = static_cast<int>(cdiv64(max_query_len, 128));
-  // One workgroup per (query tile, head).  A chunk has at most qtiles tiles,
+  // One workgroup per (tile, kv head); a tile is 128 query vectors of one
+  // kv head (rows x its G query heads).  A chunk has at most qtiles tiles,
   // and chunks that follow each other in [0, num_tokens) (query_start
-  // non-decreasing) have at most one per 128 rows plus one each.
+  // non-decreasing) have at most one per 128 vectors plus one each.
+  const int64_t G = num_q_heads / num_kv_heads;
+  if (static_cast<int64_t>(num_tokens) * G >= (int64_t{1} << 31) ||
+      static_cast<int64_t>(max_query_len) * G >= (int64_t{1} << 31)) {
+    set_error("prefill: %d tokens x %lld query heads per kv head is too large", num_tokens,
+              static_cast<long long>(G));
+    return PKV_ERR_UNSUPPORTED;
+  }
+  if (num_seqs > prefill_max_seqs(head_size)) {
+    set_error("bf16 prefill takes at most %d sequences per launch (got %d)",
+              prefill_max_seqs(head_size), num_seqs);
+    return PKV_ERR_UNSUPPORTED;
+  }
+  a.qtiles = static_cast<int>(cdiv64(static_cast<int64_t>(max_query_len) * G, 128));
   const int64_t tiles = std::min<int64_t>(static_cast<int64_t>(num_seqs) * a.qtiles,
-                                          cdiv64(num_tokens, 128) + num_seqs);
-  const int64_t total = tiles * num_q_heads;
+                                          cdiv64(static_cast<int64_t>(num_tokens) * G, 128) + num_seqs);
+  const int64_t total = tiles * num_kv_heads;
   if (total > (int64_t{1} << 30)) {
     set_error("prefill grid of %lld work items is too large", static_cast<long long>(total));
     return PKV_ERR_UNSUPPORTED;

@@ -85,16 +85,18 @@ __device__ __forceinline__ bf16x4 lds_read_tr16(const char* p) {
 template <int NCH>
 __device__ __forceinline__ int kskew(int t) { return (t * NCH / 16) % NCH; }
 
-// A sequence's chunk as the launch sees it: its tiles of up to 128 rows
-// (none when the rows lie outside the output; at most the grid's qtiles),
-// and whether it is bad (its tiles then write NaN rows only).
+// A sequence's chunk as the launch sees it.  Per kv head the chunk holds
+// qlen x G query vectors (row i, head kvh G + k is vector G i + k), taken in
+// tiles of 128 consecutive vectors: ntiles of them (none when the rows lie
+// outside the output; at most the grid's qtiles).  A bad sequence's tiles
+// write NaN rows only.
 struct SeqShape {
   int q0, qlen, L, ntiles;
   bool bad;
 };
 
 template <int B>
-__device__ __forceinline__ SeqShape seq_shape(const PrefillArgs& a, int s) {
+__device__ __forceinline__ SeqShape seq_shape(const PrefillArgs& a, int s, int G) {
   SeqShape r;
   r.q0 = a.qstart[s];
   r.qlen = a.qstart[s + 1] - r.q0;
@@ -103,17 +105,30 @@ __device__ __forceinline__ SeqShape seq_shape(const PrefillArgs& a, int s) {
   r.bad = false;
   if (r.q0 < 0 || r.qlen < 0 || r.q0 + r.qlen > a.T) return r;  // rows outside the output
   r.bad = r.L < 0 || (r.L + B - 1) / B > a.width || r.qlen > r.L || r.qlen > a.max_q;
-  r.ntiles = min((r.qlen + kPRows - 1) / kPRows, a.qtiles);
+  r.ntiles = min((r.qlen * G + kPRows - 1) / kPRows, a.qtiles);
   return r;
 }
 
-// What tile x of a chunk costs: the 64-key steps it reads (capped; 0 for a
-// bad sequence)
-__device__ __forceinline__ int tile_key(const SeqShape& q, int x) {
-  if (q.bad) return 0;
-  const int row0 = x * kPRows;
-  const int kend = max(0, min(q.L, q.L - q.qlen + row0 + min(kPRows, q.qlen - row0)));
-  return min((kend + kPKeys - 1) / kPKeys, kRankBins - 1);
+// v / G for 0 <= v < 2^31: a double-precision estimate, then one step of
+// correction either way
+__device__ __forceinline__ int div_g(int v, int G, double rG) {
+  int q = static_cast<int>(static_cast<double>(v) * rG);
+  const int r = v - q * G;
+  q += r >= G ? 1 : 0;
+  q -= r < 0 ? 1 : 0;
+  return q;
+}
+
+// Keys [0, kend) tile x reads: up to the position of its last vector's row
+__device__ __forceinline__ int tile_kend(int qlen, int L, bool bad, int x, int G, double rG) {
+  if (bad) return 0;
+  const int last_row = div_g(min(qlen * G, (x + 1) * kPRows) - 1, G, rG);
+  return max(0, min(L, L - qlen + last_row + 1));
+}
+
+// What tile x costs: the 64-key steps it reads (capped)
+__device__ __forceinline__ int tile_key(int qlen, int L, bool bad, int x, int G, double rG) {
+  return min((tile_kend(qlen, L, bad, x, G, rG) + kPKeys - 1) / kPKeys, kRankBins - 1);
 }
 
 // Exclusive prefix sum of v over the workgroup; *total gets the sum.  Uses
@@ -141,34 +156,83 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* wsum, int* total
 
 // The tile of rank r when the launch's tiles are ordered by tile_key,
 // largest first (equal keys: by sequence, then tile).  A counting sort in
-// LDS (sm: kRankBins + 16 ints): the histogram of keys, the bin that holds
-// rank r, then that bin's tiles in order.  Every thread of the workgroup
-// calls it; false (for all of them) when r is past the last tile.
+// LDS over the flattened list of tiles (sequence by sequence), each thread
+// taking a contiguous run of it: the histogram of keys, the bin that holds
+// rank r, then that bin's tiles in order.  sm holds nints ints (the
+// histogram, a few scalars, and each sequence's first tile, chunk length
+// and context length -- so batches of up to (nints - kRankBins - 16) / 3
+// sequences).  Every thread of the workgroup calls it (it synchronises,
+// and ends with a barrier, so the caller may reuse sm); false, for all of
+// them, when r is past the last tile.
 template <int B>
-__device__ bool tile_of_rank(const PrefillArgs& a, int r, int* sm, int* s_out, int* x_out) {
+__device__ bool tile_of_rank(const PrefillArgs& a, int G, double rG, int r, int* sm, int nints,
+                             int* s_out, int* x_out) {
   int* hist = sm;
   int* wsum = sm + kRankBins;
   int* res = wsum + 8;
+  int* first = res + 8;        // [S + 1]: flattened index of each sequence's first tile
+  int* qlen_of = first + a.S + 1;
+  int* len_of = qlen_of + a.S;  // context length, -1 for a bad sequence
   const int tid = threadIdx.x;
-  for (int i = tid; i < kRankBins; i += kPThreads) hist[i] = 0;
-  __syncthreads();
-  for (int s = tid; s < a.S; s += kPThreads) {
-    const SeqShape q = seq_shape<B>(a, s);
-    for (int x = 0; x < q.ntiles; ++x) atomicAdd(&hist[tile_key(q, x)], 1);
+  if (3 * a.S + 1 + kRankBins + 16 > nints) {  // host checks the batch fits
+    return false;
   }
+  // sequences: a contiguous run per thread
+  const int per_s = (a.S + kPThreads - 1) / kPThreads;
+  const int s0 = min(a.S, tid * per_s), s1 = min(a.S, s0 + per_s);
+  int mine = 0;
+  for (int s = s0; s < s1; ++s) {
+    const SeqShape q = seq_shape<B>(a, s, G);
+    qlen_of[s] = q.qlen;
+    len_of[s] = q.bad ? -1 : q.L;
+    first[s] = q.ntiles;  // count for now
+    mine += q.ntiles;
+  }
+  for (int i = tid; i < kRankBins; i += kPThreads) hist[i] = 0;
+  int ntot;
+  int run0 = block_exclusive_scan(mine, wsum, &ntot);
+  for (int s = s0; s < s1; ++s) {
+    const int n = first[s];
+    first[s] = run0;
+    run0 += n;
+  }
+  if (tid == 0) first[a.S] = ntot;
+  __syncthreads();
+  // flattened tiles: a contiguous run per thread; (sequence, tile) of its first
+  const int per_t = (ntot + kPThreads - 1) / kPThreads;
+  const int i0 = min(ntot, tid * per_t), i1 = min(ntot, i0 + per_t);
+  int sq = 0;
+  {
+    int lo = 0, hi = a.S;  // last sequence with first[s] <= i0
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (first[mid] <= i0) lo = mid; else hi = mid;
+    }
+    sq = lo;
+  }
+  auto walk = [&](auto&& f) {  // f(key, sequence, tile) over this thread's run
+    int s = sq;
+    for (int i = i0; i < i1; ++i) {
+      while (first[s + 1] <= i) ++s;
+      const int x = i - first[s];
+      const int L = len_of[s];
+      f(tile_key(qlen_of[s], L, L < 0, x, G, rG), s, x);
+    }
+  };
+  walk([&](int key, int, int) { atomicAdd(&hist[key], 1); });
   __syncthreads();
   // thread t holds the bins of keys kRankBins - 1 - PER t - k, k < PER
   constexpr int PER = kRankBins / kPThreads;
-  int c[PER], mine = 0;
+  int c[PER], mb = 0;
 #pragma unroll
   for (int k = 0; k < PER; ++k) {
     c[k] = hist[kRankBins - 1 - (PER * tid + k)];
-    mine += c[k];
+    mb += c[k];
   }
   int all;
-  const int before = block_exclusive_scan(mine, wsum, &all);
+  const int before = block_exclusive_scan(mb, wsum, &all);
   if (r >= all) return false;
-  if (r >= before && r < before + mine) {
+  if (r >= before && r < before + mb) {
     int cum = before;
 #pragma unroll
     for (int k = 0; k < PER; ++k) {
@@ -181,33 +245,25 @@ __device__ bool tile_of_rank(const PrefillArgs& a, int r, int* sm, int* s_out, i
   }
   __syncthreads();
   const int key = res[0], j = res[1];
-  // the j-th tile with that key: thread t counts those of a contiguous run of sequences
-  const int per_s = (a.S + kPThreads - 1) / kPThreads;
-  const int s0 = tid * per_s, s1 = min(a.S, s0 + per_s);
+  // the j-th tile with that key, in flattened order
   int n = 0;
-  for (int s = s0; s < s1; ++s) {
-    const SeqShape q = seq_shape<B>(a, s);
-    for (int x = 0; x < q.ntiles; ++x) n += tile_key(q, x) == key;
-  }
+  walk([&](int k, int, int) { n += k == key; });
   int all2;
-  const int b2 = block_exclusive_scan(n, wsum, &all2);
-  if (j >= b2 && j < b2 + n) {
-    int cum = b2;
-    for (int s = s0; s < s1; ++s) {
-      const SeqShape q = seq_shape<B>(a, s);
-      for (int x = 0; x < q.ntiles; ++x) {
-        if (tile_key(q, x) != key) continue;
-        if (cum == j) {
-          res[2] = s;
-          res[3] = x;
-        }
-        ++cum;
+  int cum = block_exclusive_scan(n, wsum, &all2);
+  if (j >= cum && j < cum + n) {
+    walk([&](int k, int s, int x) {
+      if (k != key) return;
+      if (cum == j) {
+        res[2] = s;
+        res[3] = x;
       }
-    }
+      ++cum;
+    });
   }
   __syncthreads();
   *s_out = res[2];
   *x_out = res[3];
+  __syncthreads();
   return true;
 }
 
@@ -220,38 +276,44 @@ prefill_bf16_kernel(PrefillArgs a) {
   const int tid = threadIdx.x;
   const int wv = tid >> 6, lane = tid & 63, j = lane & 15, g = lane >> 4;
 
-  // Work item: (tile of rank r, head h), heads innermost.  Tiles are ranked
-  // longest first, so the launch ends on short items, and the heads of each
-  // tile spread over the XCDs (workgroup b runs on XCD b % 8), which keeps
-  // the XCDs' shares of the work equal whatever the batch's length mix.
+  // Work item: (tile of rank r, kv head), kv heads innermost.  Tiles are
+  // ranked longest first, so the launch ends on short items, and the kv
+  // heads of a tile spread over the XCDs (workgroup b runs on XCD b % 8),
+  // which keeps the XCDs' shares of the work equal whatever the batch's
+  // length mix.  A tile's 128 columns are query vectors of one kv head: its
+  // G query heads at consecutive rows, so the K/V staged for it serve G
+  // heads, and short chunks still fill the tile.
   const int bid = blockIdx.x;
-  const int h = bid % a.Hq;
+  const int G = a.Hq / a.Hkv, kvh = bid % a.Hkv;
   int s, x;
-  if (!tile_of_rank<B>(a, bid / a.Hq, reinterpret_cast<int*>(lds + Gm::BUF), &s, &x)) return;
-  const SeqShape sq = seq_shape<B>(a, s);
+  const double rG = 1.0 / G;
+  if (!tile_of_rank<B>(a, G, rG, bid / a.Hkv, reinterpret_cast<int*>(lds), Gm::LDS / 4, &s, &x))
+    return;
+  const SeqShape sq = seq_shape<B>(a, s, G);
   const int q0 = sq.q0, qlen = sq.qlen, L = sq.L;
   const bool bad_seq = sq.bad;
-  const int row0 = x * kPRows;
-  const int G = a.Hq / a.Hkv, kvh = h / G;
-  const int tile_rows = min(kPRows, qlen - row0);
-  const int P0 = L - qlen + row0;  // position of the tile's first row
-  const int kend = bad_seq ? 0 : max(0, min(L, P0 + tile_rows));  // keys [0, kend)
+  const int nvec = qlen * G;
+  const int v0 = x * kPRows;                       // the tile's first vector
+  const int tile_vecs = min(kPRows, nvec - v0);
+  const int P0 = L - qlen;                         // position of the chunk's first row
+  const int kend = tile_kend(qlen, L, bad_seq, x, G, rG);  // keys [0, kend)
   const int nsteps = (kend + kPKeys - 1) / kPKeys;
 
-  // this wave's rows: column j of block cb is tile row 32 wv + 16 cb + j
+  // this wave's vectors: column j of block cb is tile vector 32 wv + 16 cb + j
   const int wr0 = 32 * wv;
-  const int wave_rows = max(0, min(32, tile_rows - wr0));
-  const int wmin = P0 + wr0;  // position of the wave's first row
-  const int wmax = wave_rows > 0 ? P0 + wr0 + wave_rows - 1 : -1;  // ... and of its last
+  const int wave_vecs = max(0, min(32, tile_vecs - wr0));
+  const int wmin = P0 + div_g(v0 + wr0, G, rG);    // position of the wave's first row
+  const int wmax = wave_vecs > 0 ? P0 + div_g(v0 + wr0 + wave_vecs - 1, G, rG) : -1;  // ... and of its last
   int pos[2];
   bf16x8 qf[2][QC];
   const uint16_t* qb = static_cast<const uint16_t*>(a.query);
 #pragma unroll
   for (int cb = 0; cb < 2; ++cb) {
-    const int r = wr0 + 16 * cb + j;
-    const bool live = r < tile_rows;
-    pos[cb] = live ? P0 + r : kend - 1;
-    const uint16_t* qp = qb + (static_cast<int64_t>(q0 + row0 + r) * a.Hq + h) * D + 8 * g;
+    const int lv = wr0 + 16 * cb + j;
+    const bool live = lv < tile_vecs;
+    const int vv = v0 + lv, row = div_g(vv, G, rG), head = kvh * G + (vv - row * G);
+    pos[cb] = live ? P0 + row : kend - 1;
+    const uint16_t* qp = qb + (static_cast<int64_t>(q0 + row) * a.Hq + head) * D + 8 * g;
 #pragma unroll
     for (int c = 0; c < QC; ++c) qf[cb][c] = live ? wave::load_bf16x8<false>(qp + 32 * c) : bf16x8{};
   }
@@ -487,11 +549,12 @@ prefill_bf16_kernel(PrefillArgs a) {
   __syncthreads();
   constexpr int D4 = D / 4;
   for (int e = lane; e < 32 * D4; e += 64) {
-    const int rr = wr0 + e / D4;
-    if (rr >= tile_rows) break;
+    const int lv = wr0 + e / D4;
+    if (lv >= tile_vecs) break;
     const int d = (e % D4) * 4;
-    const float4 o = *reinterpret_cast<const float4*>(rows + rr * Gm::SROW + d);
-    const int64_t off = (static_cast<int64_t>(q0 + row0 + rr) * a.Hq + h) * D + d;
+    const float4 o = *reinterpret_cast<const float4*>(rows + lv * Gm::SROW + d);
+    const int vv = v0 + lv, row = div_g(vv, G, rG), head = kvh * G + (vv - row * G);
+    const int64_t off = (static_cast<int64_t>(q0 + row) * a.Hq + head) * D + d;
     if (a.out_bf16) {
       const uint32_t lo = f32_to_bf16(o.x) | (static_cast<uint32_t>(f32_to_bf16(o.y)) << 16);
       const uint32_t hi = f32_to_bf16(o.z) | (static_cast<uint32_t>(f32_to_bf16(o.w)) << 16);
@@ -500,16 +563,17 @@ prefill_bf16_kernel(PrefillArgs a) {
       *reinterpret_cast<float4*>(static_cast<float*>(a.out) + off) = o;
     }
   }
-  // A chunk longer than max_query_len has rows past the grid's tiles: the
-  // last tile writes them too (NaN, as for every row of a bad sequence), so
-  // no row of the chunk keeps what the output held before.
-  if (bad_seq && x == a.qtiles - 1 && qlen > a.qtiles * kPRows) {
-    const int rbeg = a.qtiles * kPRows;
-    const int64_t n4 = static_cast<int64_t>(qlen - rbeg) * D4;
+  // A chunk longer than max_query_len has vectors past the grid's tiles:
+  // the last tile writes them too (NaN, as for every row of a bad
+  // sequence), so no row of the chunk keeps what the output held before.
+  if (bad_seq && x == a.qtiles - 1 && nvec > a.qtiles * kPRows) {
+    const int vbeg = a.qtiles * kPRows;
+    const int64_t n4 = static_cast<int64_t>(nvec - vbeg) * D4;
     for (int64_t e = tid; e < n4; e += kPThreads) {
-      const int64_t rr = rbeg + e / D4;
+      const int vv = vbeg + static_cast<int>(e / D4);
       const int d = static_cast<int>(e % D4) * 4;
-      const int64_t off = ((q0 + rr) * a.Hq + h) * D + d;
+      const int row = div_g(vv, G, rG), head = kvh * G + (vv - row * G);
+      const int64_t off = (static_cast<int64_t>(q0 + row) * a.Hq + head) * D + d;
       if (a.out_bf16) {
         const uint32_t nn = f32_to_bf16(NAN) | (static_cast<uint32_t>(f32_to_bf16(NAN)) << 16);
         *reinterpret_cast<wave::u32x2*>(static_cast<uint16_t*>(a.out) + off) = wave::u32x2{nn, nn};
@@ -633,6 +697,11 @@ int launch_bf16_d(const PrefillArgs& a, hipStream_t stream) {
 }
 
 }  // namespace
+
+int prefill_max_seqs(int D) {
+  const int nints = (D == 64 ? PGeom<64>::LDS : PGeom<128>::LDS) / 4;
+  return (nints - kRankBins - 16 - 1) / 3;
+}
 
 int launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream) {
   if (a.total == 0) return PKV_OK;

@@ -118,6 +118,22 @@ def test_host_checks_reject_bad_arguments(lib):
     assert lib.paged_kv_gather(p, p, p, p, 4, p, 2, 2, 128, 16, 10, 64, 7, None) == -1
 
 
+def test_prefill_host_checks(lib):
+    """Prefill argument checks, made before anything is launched: the bf16
+    kernel ranks a launch's work in LDS, which bounds the sequences per call."""
+    p = ctypes.c_void_p(0x1000)  # never dereferenced: the checks fail first
+    BF16 = 1
+
+    def call(S, D=128, Hq=8, Hkv=2, T=4096, maxq=64):
+        return lib.paged_attention_prefill(p, 0, p, p, T, maxq, p, p, 4, p, S, Hq, Hkv, D, 16, 10,
+                                           0.1, BF16, None)
+    assert call(5456) == -2 and b"at most 5455" in lib.pkv_last_error()
+    assert call(2726, D=64) == -2 and b"at most 2725" in lib.pkv_last_error()
+    assert call(1, Hq=7) == -1
+    assert call(1, T=1 << 30) == -2             # tokens x 4 heads per kv head overflows
+    assert call(0) == 0                          # nothing to do
+
+
 def test_shared_prefix_host_checks(lib):
     """Argument checks of the shared-prefix decode and the fused write, all
     made before anything is launched."""

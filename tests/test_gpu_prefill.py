@@ -69,6 +69,9 @@ SMALL = [
     ("bf16", 14, 2, 64, 8, [0, 33, 0], [200, 64, 129]),
     ("bf16", 8, 8, 128, 32, [7, 0], [300, 31]),
     ("bf16", 4, 1, 64, 64, [64, 0, 190], [65, 128, 2]),
+    # tiles of 128 query vectors whose G heads of a row straddle tile edges
+    ("bf16", 12, 1, 128, 16, [3, 0, 50], [40, 11, 300]),
+    ("bf16", 20, 4, 64, 32, [0, 90], [7, 77]),
     ("f32", 4, 4, 64, 16, [0, 20, 3], [40, 90, 1]),
     ("f32", 8, 2, 128, 5, [11, 0], [37, 64]),
 ]
@@ -175,5 +178,5 @@ def test_chunk_past_the_grid_gives_nan_rows():
                               out=out)
         torch.cuda.synchronize()
         got = out.float().cpu().numpy()
-        assert np.isnan(got[:300]).all(), "the 300-row chunk (grid: one 128-row tile)"
+        assert np.isnan(got[:300]).all(), "the 300-row chunk (grid: 2 tiles of 128 query vectors)"
         assert np.isfinite(got[300:]).all()
