@@ -477,8 +477,8 @@ int paged_attention_shared_merge(void* out, pkv_dtype out_dtype, const void* que
  *   kv_cache, block_tables, table_width, context_lens, num_blocks: as for
  *                paged_attention_decode
  * Supported: head_size 64 or 128; bf16: block_size 8, 16, 32 or 64 (matrix
- * cores; scores and the weighted sum accumulate in fp32), at most 2725
- * (head_size 64) or 5455 (head_size 128) sequences per call, else
+ * cores; scores and the weighted sum accumulate in fp32), at most 5453
+ * (head_size 64) or 10914 (head_size 128) sequences per call, else
  * PKV_ERR_UNSUPPORTED; fp32: any block_size (vector ALU).  Needs no workspace
  * and no clearing.
  */

@@ -698,10 +698,10 @@ int paged_attention_prefill(void* out, pkv_dtype out_dtype, const void* query,
   a.out_bf16 = out_dtype == PKV_BF16;
   a.max_q = max_query_len;
   if (dtype == PKV_F32) return launch_prefill_f32(a, stream);
-  // One workgroup per (tile, kv head); a tile is 128 query vectors of one
-  // kv head (rows x its G query heads).  A chunk has at most qtiles tiles,
-  // and chunks that follow each other in [0, num_tokens) (query_start
-  // non-decreasing) have at most one per 128 vectors plus one each.
+  // One workgroup per (tile, kv head); a tile is a run of query vectors of
+  // one kv head (rows x its G query heads).  A chunk has at most qtiles
+  // tiles, and chunks that follow each other in [0, num_tokens) (query_start
+  // non-decreasing) have at most one per tile's vectors plus one each.
   const int64_t G = num_q_heads / num_kv_heads;
   if (static_cast<int64_t>(num_tokens) * G >= (int64_t{1} << 31) ||
       static_cast<int64_t>(max_query_len) * G >= (int64_t{1} << 31)) {
@@ -714,9 +714,10 @@ int paged_attention_prefill(void* out, pkv_dtype out_dtype, const void* query,
               prefill_max_seqs(head_size), num_seqs);
     return PKV_ERR_UNSUPPORTED;
   }
-  a.qtiles = static_cast<int>(cdiv64(static_cast<int64_t>(max_query_len) * G, 128));
+  const int tile = prefill_tile_vectors(head_size);
+  a.qtiles = static_cast<int>(cdiv64(static_cast<int64_t>(max_query_len) * G, tile));
   const int64_t tiles = std::min<int64_t>(static_cast<int64_t>(num_seqs) * a.qtiles,
-                                          cdiv64(static_cast<int64_t>(num_tokens) * G, 128) + num_seqs);
+                                          cdiv64(static_cast<int64_t>(num_tokens) * G, tile) + num_seqs);
   const int64_t total = tiles * num_kv_heads;
   if (total > (int64_t{1} << 30)) {
     set_error("prefill grid of %lld work items is too large", static_cast<long long>(total));

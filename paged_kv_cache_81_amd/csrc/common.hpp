@@ -214,13 +214,15 @@ struct PrefillArgs {
   float scale_log2;
   int out_bf16;
   int max_q;           // longest chunk the grid covers (longer ones give NaN)
-  int qtiles;          // tiles of 128 query vectors per (sequence, kv head) at most
+  int qtiles;          // tiles of query vectors per (sequence, kv head) at most
   int total;           // work items (workgroups): tiles x Hkv
 };
 
 int launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream);
 // most sequences one bf16 prefill launch takes (its work ranking lives in LDS)
 int prefill_max_seqs(int head_size);
+// query vectors per bf16 prefill tile (one workgroup each)
+int prefill_tile_vectors(int head_size);
 int launch_prefill_f32(const PrefillArgs& a, hipStream_t stream);
 
 int launch_attention_bf16(const AttnArgs& a, hipStream_t stream);

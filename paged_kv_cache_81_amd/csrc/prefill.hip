@@ -5,14 +5,14 @@
 // of it sits at position lens[s] - chunk_len + i and attends keys 0 .. its
 // position of its own sequence, read through the block table.
 //
-// bf16 caches: a workgroup (4 waves) takes 128 query rows (a tile) of one
-// query head; wave w takes rows 32w .. 32w + 31 as two 16-row column blocks.
-// Workgroups take the tiles longest first (ranked in LDS by the keys they
-// read) with the heads of a tile innermost, so the work of every XCD is the
-// same and the launch ends on short tiles.  Keys are walked in steps of 64:
+// bf16 caches: a workgroup (8 waves) takes a tile of 256 query vectors of
+// one kv head (rows x its query heads); wave w takes vectors 32w .. 32w + 31
+// as two 16-column blocks.  Workgroups take the tiles longest first (ranked
+// in LDS by the keys they read) with the kv heads of a tile innermost, so
+// the work of every XCD is the same and the launch ends on short tiles.  Keys are walked in steps of 64:
 // the workgroup loads a step's K and V rows (through the table) into one of
 // two LDS buffers while the waves compute on the other, so each K/V row is
-// read from memory once per workgroup and 128 query rows use it.  Per 32
+// read from memory once per workgroup and 256 query vectors use it.  Per 32
 // keys a wave runs, for each column block, the scores S^T = K . Q^T on
 // v_mfma_f32_16x16x32_bf16 (K rows from LDS as the A operand, the query rows
 // as B), the causal mask, an online softmax per query row in the log2
@@ -31,16 +31,29 @@
 namespace pkv {
 namespace {
 
-constexpr int kPThreads = 256;
-constexpr int kPRows = 128;  // query rows per workgroup (4 waves x 32)
+// Waves per workgroup: 8 (one workgroup per CU; at head size 128 two waves
+// per SIMD, at 64 up to three).  A wave takes 32 query vectors, a workgroup
+// a tile of 32 x waves: each K/V step staged in LDS serves 256 vectors, and
+// the per-tile costs (ranking, first loads, output) come once per 256.
+// Measured against 4 waves: 6% faster at head size 128, 2-3% at 64.
+#ifndef PKV_PREFILL_WAVES_128
+#define PKV_PREFILL_WAVES_128 8
+#endif
+#ifndef PKV_PREFILL_WAVES_64
+#define PKV_PREFILL_WAVES_64 8
+#endif
+template <int D>
+constexpr int kPWaves = D == 128 ? PKV_PREFILL_WAVES_128 : PKV_PREFILL_WAVES_64;
 constexpr int kPKeys = 64;   // keys per LDS step
 // tile costs (64-key steps) the launch orders its work by, counted exactly below this
 constexpr int kRankBins = 1024;
 // how far (log2 units) a row's max may pass its reference before a rescale
 constexpr float kLazyLog2 = 8.f;
 
-template <int D>
+template <int D, int NW>
 struct PGeom {
+  static constexpr int THREADS = 64 * NW;
+  static constexpr int ROWS = 32 * NW;  // query vectors per tile
   static constexpr int QC = D / 32;   // score MFMAs per 16 x 16 tile
   static constexpr int NV = D / 16;   // output blocks; dims per lane per V row
   static constexpr int NCH = D / 8;   // 16-byte chunks per row
@@ -50,9 +63,9 @@ struct PGeom {
   static constexpr int VROW = 2 * D + 32;
   static constexpr int KBYTES = kPKeys * KROW;
   static constexpr int BUF = KBYTES + kPKeys * VROW;
-  static constexpr int CPT = kPKeys * NCH / kPThreads;  // chunks per thread per tensor
+  static constexpr int CPT = kPKeys * NCH / THREADS;  // chunks per thread per tensor
   static constexpr int SROW = D + 4;  // floats per finished row in LDS
-  static constexpr int LDS = 2 * BUF > kPRows * SROW * 4 ? 2 * BUF : kPRows * SROW * 4;
+  static constexpr int LDS = 2 * BUF > ROWS * SROW * 4 ? 2 * BUF : ROWS * SROW * 4;
 };
 
 // max(v[l], v[l ^ 16]) and max(v[l], v[l ^ 32]) without LDS: the permlane
@@ -87,7 +100,7 @@ __device__ __forceinline__ int kskew(int t) { return (t * NCH / 16) % NCH; }
 
 // A sequence's chunk as the launch sees it.  Per kv head the chunk holds
 // qlen x G query vectors (row i, head kvh G + k is vector G i + k), taken in
-// tiles of 128 consecutive vectors: ntiles of them (none when the rows lie
+// tiles of consecutive vectors: ntiles of them (none when the rows lie
 // outside the output; at most the grid's qtiles).  A bad sequence's tiles
 // write NaN rows only.
 struct SeqShape {
@@ -95,7 +108,7 @@ struct SeqShape {
   bool bad;
 };
 
-template <int B>
+template <int B, int ROWS>
 __device__ __forceinline__ SeqShape seq_shape(const PrefillArgs& a, int s, int G) {
   SeqShape r;
   r.q0 = a.qstart[s];
@@ -105,7 +118,7 @@ __device__ __forceinline__ SeqShape seq_shape(const PrefillArgs& a, int s, int G
   r.bad = false;
   if (r.q0 < 0 || r.qlen < 0 || r.q0 + r.qlen > a.T) return r;  // rows outside the output
   r.bad = r.L < 0 || (r.L + B - 1) / B > a.width || r.qlen > r.L || r.qlen > a.max_q;
-  r.ntiles = min((r.qlen * G + kPRows - 1) / kPRows, a.qtiles);
+  r.ntiles = min((r.qlen * G + ROWS - 1) / ROWS, a.qtiles);
   return r;
 }
 
@@ -120,19 +133,22 @@ __device__ __forceinline__ int div_g(int v, int G, double rG) {
 }
 
 // Keys [0, kend) tile x reads: up to the position of its last vector's row
+template <int ROWS>
 __device__ __forceinline__ int tile_kend(int qlen, int L, bool bad, int x, int G, double rG) {
   if (bad) return 0;
-  const int last_row = div_g(min(qlen * G, (x + 1) * kPRows) - 1, G, rG);
+  const int last_row = div_g(min(qlen * G, (x + 1) * ROWS) - 1, G, rG);
   return max(0, min(L, L - qlen + last_row + 1));
 }
 
 // What tile x costs: the 64-key steps it reads (capped)
+template <int ROWS>
 __device__ __forceinline__ int tile_key(int qlen, int L, bool bad, int x, int G, double rG) {
-  return min((tile_kend(qlen, L, bad, x, G, rG) + kPKeys - 1) / kPKeys, kRankBins - 1);
+  return min((tile_kend<ROWS>(qlen, L, bad, x, G, rG) + kPKeys - 1) / kPKeys, kRankBins - 1);
 }
 
 // Exclusive prefix sum of v over the workgroup; *total gets the sum.  Uses
-// wsum[4]; the caller separates two calls by a barrier.
+// wsum[NW]; the caller separates two calls by a barrier.
+template <int NW>
 __device__ __forceinline__ int block_exclusive_scan(int v, int* wsum, int* total) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   int x = v;
@@ -145,7 +161,7 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* wsum, int* total
   __syncthreads();
   int before = 0, all = 0;
 #pragma unroll
-  for (int w = 0; w < kPThreads / 64; ++w) {
+  for (int w = 0; w < NW; ++w) {
     const int t = wsum[w];
     before += w < wv ? t : 0;
     all += t;
@@ -160,37 +176,39 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* wsum, int* total
 // taking a contiguous run of it: the histogram of keys, the bin that holds
 // rank r, then that bin's tiles in order.  sm holds nints ints (the
 // histogram, a few scalars, and each sequence's first tile, chunk length
-// and context length -- so batches of up to (nints - kRankBins - 16) / 3
+// and context length -- so batches of up to (nints - kRankBins - 25) / 3
 // sequences).  Every thread of the workgroup calls it (it synchronises,
 // and ends with a barrier, so the caller may reuse sm); false, for all of
 // them, when r is past the last tile.
-template <int B>
+template <int B, int NW>
 __device__ bool tile_of_rank(const PrefillArgs& a, int G, double rG, int r, int* sm, int nints,
                              int* s_out, int* x_out) {
+  constexpr int THREADS = 64 * NW, ROWS = 32 * NW;
+  static_assert(kRankBins % THREADS == 0 && NW <= 16, "bins split evenly over the threads");
   int* hist = sm;
-  int* wsum = sm + kRankBins;
-  int* res = wsum + 8;
+  int* wsum = sm + kRankBins;  // [16]
+  int* res = wsum + 16;        // [8]
   int* first = res + 8;        // [S + 1]: flattened index of each sequence's first tile
   int* qlen_of = first + a.S + 1;
   int* len_of = qlen_of + a.S;  // context length, -1 for a bad sequence
   const int tid = threadIdx.x;
-  if (3 * a.S + 1 + kRankBins + 16 > nints) {  // host checks the batch fits
+  if (3 * a.S + 1 + kRankBins + 24 > nints) {  // host checks the batch fits
     return false;
   }
   // sequences: a contiguous run per thread
-  const int per_s = (a.S + kPThreads - 1) / kPThreads;
+  const int per_s = (a.S + THREADS - 1) / THREADS;
   const int s0 = min(a.S, tid * per_s), s1 = min(a.S, s0 + per_s);
   int mine = 0;
   for (int s = s0; s < s1; ++s) {
-    const SeqShape q = seq_shape<B>(a, s, G);
+    const SeqShape q = seq_shape<B, ROWS>(a, s, G);
     qlen_of[s] = q.qlen;
     len_of[s] = q.bad ? -1 : q.L;
     first[s] = q.ntiles;  // count for now
     mine += q.ntiles;
   }
-  for (int i = tid; i < kRankBins; i += kPThreads) hist[i] = 0;
+  for (int i = tid; i < kRankBins; i += THREADS) hist[i] = 0;
   int ntot;
-  int run0 = block_exclusive_scan(mine, wsum, &ntot);
+  int run0 = block_exclusive_scan<NW>(mine, wsum, &ntot);
   for (int s = s0; s < s1; ++s) {
     const int n = first[s];
     first[s] = run0;
@@ -199,7 +217,7 @@ __device__ bool tile_of_rank(const PrefillArgs& a, int G, double rG, int r, int*
   if (tid == 0) first[a.S] = ntot;
   __syncthreads();
   // flattened tiles: a contiguous run per thread; (sequence, tile) of its first
-  const int per_t = (ntot + kPThreads - 1) / kPThreads;
+  const int per_t = (ntot + THREADS - 1) / THREADS;
   const int i0 = min(ntot, tid * per_t), i1 = min(ntot, i0 + per_t);
   int sq = 0;
   {
@@ -216,13 +234,13 @@ __device__ bool tile_of_rank(const PrefillArgs& a, int G, double rG, int r, int*
       while (first[s + 1] <= i) ++s;
       const int x = i - first[s];
       const int L = len_of[s];
-      f(tile_key(qlen_of[s], L, L < 0, x, G, rG), s, x);
+      f(tile_key<ROWS>(qlen_of[s], L, L < 0, x, G, rG), s, x);
     }
   };
   walk([&](int key, int, int) { atomicAdd(&hist[key], 1); });
   __syncthreads();
   // thread t holds the bins of keys kRankBins - 1 - PER t - k, k < PER
-  constexpr int PER = kRankBins / kPThreads;
+  constexpr int PER = kRankBins / THREADS;
   int c[PER], mb = 0;
 #pragma unroll
   for (int k = 0; k < PER; ++k) {
@@ -230,7 +248,7 @@ __device__ bool tile_of_rank(const PrefillArgs& a, int G, double rG, int r, int*
     mb += c[k];
   }
   int all;
-  const int before = block_exclusive_scan(mb, wsum, &all);
+  const int before = block_exclusive_scan<NW>(mb, wsum, &all);
   if (r >= all) return false;
   if (r >= before && r < before + mb) {
     int cum = before;
@@ -249,7 +267,7 @@ __device__ bool tile_of_rank(const PrefillArgs& a, int G, double rG, int r, int*
   int n = 0;
   walk([&](int k, int, int) { n += k == key; });
   int all2;
-  int cum = block_exclusive_scan(n, wsum, &all2);
+  int cum = block_exclusive_scan<NW>(n, wsum, &all2);
   if (j >= cum && j < cum + n) {
     walk([&](int k, int s, int x) {
       if (k != key) return;
@@ -268,9 +286,11 @@ __device__ bool tile_of_rank(const PrefillArgs& a, int G, double rG, int r, int*
 }
 
 template <int D, int B>
-__global__ void __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ void __launch_bounds__(64 * kPWaves<D>) __attribute__((amdgpu_waves_per_eu(2)))
 prefill_bf16_kernel(PrefillArgs a) {
-  using Gm = PGeom<D>;
+  constexpr int NW = kPWaves<D>;
+  using Gm = PGeom<D, NW>;
+  constexpr int kPThreads = Gm::THREADS, kPRows = Gm::ROWS;
   constexpr int QC = Gm::QC, NV = Gm::NV, NCH = Gm::NCH, CPT = Gm::CPT;
   extern __shared__ __align__(16) char lds[];
   const int tid = threadIdx.x;
@@ -280,23 +300,23 @@ prefill_bf16_kernel(PrefillArgs a) {
   // ranked longest first, so the launch ends on short items, and the kv
   // heads of a tile spread over the XCDs (workgroup b runs on XCD b % 8),
   // which keeps the XCDs' shares of the work equal whatever the batch's
-  // length mix.  A tile's 128 columns are query vectors of one kv head: its
+  // length mix.  A tile's columns are query vectors of one kv head: its
   // G query heads at consecutive rows, so the K/V staged for it serve G
   // heads, and short chunks still fill the tile.
   const int bid = blockIdx.x;
   const int G = a.Hq / a.Hkv, kvh = bid % a.Hkv;
   int s, x;
   const double rG = 1.0 / G;
-  if (!tile_of_rank<B>(a, G, rG, bid / a.Hkv, reinterpret_cast<int*>(lds), Gm::LDS / 4, &s, &x))
+  if (!tile_of_rank<B, NW>(a, G, rG, bid / a.Hkv, reinterpret_cast<int*>(lds), Gm::LDS / 4, &s, &x))
     return;
-  const SeqShape sq = seq_shape<B>(a, s, G);
+  const SeqShape sq = seq_shape<B, kPRows>(a, s, G);
   const int q0 = sq.q0, qlen = sq.qlen, L = sq.L;
   const bool bad_seq = sq.bad;
   const int nvec = qlen * G;
   const int v0 = x * kPRows;                       // the tile's first vector
   const int tile_vecs = min(kPRows, nvec - v0);
   const int P0 = L - qlen;                         // position of the chunk's first row
-  const int kend = tile_kend(qlen, L, bad_seq, x, G, rG);  // keys [0, kend)
+  const int kend = tile_kend<kPRows>(qlen, L, bad_seq, x, G, rG);  // keys [0, kend)
   const int nsteps = (kend + kPKeys - 1) / kPKeys;
 
   // this wave's vectors: column j of block cb is tile vector 32 wv + 16 cb + j
@@ -529,7 +549,7 @@ prefill_bf16_kernel(PrefillArgs a) {
   }
   bad = __syncthreads_or(bad) || bad_seq;
 
-  // finish: normalise, stage rows [128][SROW] in LDS (no wave reads K/V any
+  // finish: normalise, stage rows [kPRows][SROW] in LDS (no wave reads K/V any
   // more), then store whole rows
   float* rows = reinterpret_cast<float*>(lds);
 #pragma unroll
@@ -678,9 +698,10 @@ __global__ void __launch_bounds__(64) prefill_f32_kernel(PrefillArgs a) {
 template <int D, int B>
 int launch_bf16_db(const PrefillArgs& a, hipStream_t stream) {
   auto kern = prefill_bf16_kernel<D, B>;
-  const int lds = PGeom<D>::LDS;
+  using Gm = PGeom<D, kPWaves<D>>;
+  const int lds = Gm::LDS;
   if (const int rc = raise_lds_limit(reinterpret_cast<const void*>(kern), lds)) return rc;
-  kern<<<dim3(static_cast<unsigned>(a.total)), dim3(kPThreads), lds, stream>>>(a);
+  kern<<<dim3(static_cast<unsigned>(a.total)), dim3(Gm::THREADS), lds, stream>>>(a);
   return check_launch("paged prefill (bf16)");
 }
 
@@ -699,9 +720,11 @@ int launch_bf16_d(const PrefillArgs& a, hipStream_t stream) {
 }  // namespace
 
 int prefill_max_seqs(int D) {
-  const int nints = (D == 64 ? PGeom<64>::LDS : PGeom<128>::LDS) / 4;
-  return (nints - kRankBins - 16 - 1) / 3;
+  const int nints = (D == 64 ? PGeom<64, kPWaves<64>>::LDS : PGeom<128, kPWaves<128>>::LDS) / 4;
+  return (nints - kRankBins - 24 - 1) / 3;
 }
+
+int prefill_tile_vectors(int D) { return 32 * (D == 64 ? kPWaves<64> : kPWaves<128>); }
 
 int launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream) {
   if (a.total == 0) return PKV_OK;

@@ -127,8 +127,9 @@ def test_prefill_host_checks(lib):
     def call(S, D=128, Hq=8, Hkv=2, T=4096, maxq=64):
         return lib.paged_attention_prefill(p, 0, p, p, T, maxq, p, p, 4, p, S, Hq, Hkv, D, 16, 10,
                                            0.1, BF16, None)
-    assert call(5456) == -2 and b"at most 5455" in lib.pkv_last_error()
-    assert call(2726, D=64) == -2 and b"at most 2725" in lib.pkv_last_error()
+    for D, most in ((128, 10914), (64, 5453)):   # the limits the header states
+        assert call(most + 1, D=D) == -2
+        assert f"at most {most} sequences".encode() in lib.pkv_last_error()
     assert call(1, Hq=7) == -1
     assert call(1, T=1 << 30) == -2             # tokens x 4 heads per kv head overflows
     assert call(0) == 0                          # nothing to do
