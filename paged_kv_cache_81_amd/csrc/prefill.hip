@@ -7,20 +7,22 @@
 //
 // bf16 caches: a workgroup (8 waves) takes a tile of 256 query vectors of
 // one kv head (rows x its query heads); wave w takes vectors 32w .. 32w + 31
-// as two 16-column blocks.  Workgroups take the tiles longest first (ranked
-// in LDS by the keys they read) with the kv heads of a tile innermost, so
-// the work of every XCD is the same and the launch ends on short tiles.  Keys are walked in steps of 64:
-// the workgroup loads a step's K and V rows (through the table) into one of
-// two LDS buffers while the waves compute on the other, so each K/V row is
-// read from memory once per workgroup and 256 query vectors use it.  Per 32
-// keys a wave runs, for each column block, the scores S^T = K . Q^T on
-// v_mfma_f32_16x16x32_bf16 (K rows from LDS as the A operand, the query rows
-// as B), the causal mask, an online softmax per query row in the log2
-// domain whose reference max moves only in jumps (few accumulator
-// rescales), and O^T += V^T . P^T with P split into bf16 hi + lo parts and
-// the V^T operand read from the row-major V tile by gfx950's transposing LDS
-// read.  Rows are finished through LDS so every global store covers whole
-// rows.
+// as the 32 columns of 32 x 32 matrix-core tiles.  Workgroups take the
+// tiles longest first (ranked in LDS by the keys they read) with the kv
+// heads of a tile innermost, so the work of every XCD is the same and the
+// launch ends on short tiles.  Keys are walked in steps of 64: the
+// workgroup loads a step's K and V rows (through the table) into one of two
+// LDS buffers while the waves compute on the other, so each K/V row is read
+// from memory once per workgroup and 256 query vectors use it.  Per 32 keys
+// a wave runs the scores S^T = K . Q^T on v_mfma_f32_32x32x16_bf16 (K rows
+// from LDS as the A operand, its query vectors as B), the causal mask, an
+// online softmax per vector in the log2 domain whose reference max moves
+// only in jumps (few accumulator rescales), and O^T += V^T . P^T with P
+// split into bf16 hi + lo parts and the V^T operand read from the row-major
+// V tile by gfx950's transposing LDS read.  Rows are finished through LDS so
+// every global store covers whole rows.  (Against 16 x 16 x 32 tiles: the
+// same speed at head size 128, 10% faster at 64, where the kernel then fits
+// in 128 registers and two workgroups share a CU.)
 //
 // fp32 caches: one wave per (query row, head), keys in batches of 64 with an
 // online softmax (vector ALU; a reference-precision path).
@@ -54,13 +56,11 @@ template <int D, int NW>
 struct PGeom {
   static constexpr int THREADS = 64 * NW;
   static constexpr int ROWS = 32 * NW;  // query vectors per tile
-  static constexpr int QC = D / 32;   // score MFMAs per 16 x 16 tile
-  static constexpr int NV = D / 16;   // output blocks; dims per lane per V row
   static constexpr int NCH = D / 8;   // 16-byte chunks per row
   static constexpr int KROW = 2 * D;  // LDS bytes per K row (chunks skewed)
   // LDS bytes per V row, padded so the 8 rows x 32 bytes of a transposed
   // read's half-wave fall on distinct banks
-  static constexpr int VROW = 2 * D + 32;
+  static constexpr int VROW = 2 * D + 64;
   static constexpr int KBYTES = kPKeys * KROW;
   static constexpr int BUF = KBYTES + kPKeys * VROW;
   static constexpr int CPT = kPKeys * NCH / THREADS;  // chunks per thread per tensor
@@ -68,15 +68,10 @@ struct PGeom {
   static constexpr int LDS = 2 * BUF > ROWS * SROW * 4 ? 2 * BUF : ROWS * SROW * 4;
 };
 
-// max(v[l], v[l ^ 16]) and max(v[l], v[l ^ 32]) without LDS: the permlane
-// swaps exchange the two halves of each 32-lane (resp. the 64-lane) group
-// between their two operands, so swapping v with itself leaves one half's
-// values in the first result and the other half's in the second.
-__device__ __forceinline__ float max_xor16(float v) {
-  const uint32_t b = __float_as_uint(v);
-  const auto r = __builtin_amdgcn_permlane16_swap(b, b, false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
+// max(v[l], v[l ^ 32]) without LDS: the permlane swap exchanges the two
+// halves of the wave between its two operands, so swapping v with itself
+// leaves one half's values in the first result and the other half's in the
+// second.
 __device__ __forceinline__ float max_xor32(float v) {
   const uint32_t b = __float_as_uint(v);
   const auto r = __builtin_amdgcn_permlane32_swap(b, b, false, false);
@@ -84,6 +79,7 @@ __device__ __forceinline__ float max_xor32(float v) {
 }
 
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 
 // ds_read_b64_tr_b16 at an LDS byte address given as a generic pointer into
@@ -291,7 +287,7 @@ prefill_bf16_kernel(PrefillArgs a) {
   constexpr int NW = kPWaves<D>;
   using Gm = PGeom<D, NW>;
   constexpr int kPThreads = Gm::THREADS, kPRows = Gm::ROWS;
-  constexpr int QC = Gm::QC, NV = Gm::NV, NCH = Gm::NCH, CPT = Gm::CPT;
+  constexpr int NCH = Gm::NCH, CPT = Gm::CPT;
   extern __shared__ __align__(16) char lds[];
   const int tid = threadIdx.x;
   const int wv = tid >> 6, lane = tid & 63, j = lane & 15, g = lane >> 4;
@@ -324,18 +320,22 @@ prefill_bf16_kernel(PrefillArgs a) {
   const int wave_vecs = max(0, min(32, tile_vecs - wr0));
   const int wmin = P0 + div_g(v0 + wr0, G, rG);    // position of the wave's first row
   const int wmax = wave_vecs > 0 ? P0 + div_g(v0 + wr0 + wave_vecs - 1, G, rG) : -1;  // ... and of its last
-  int pos[2];
-  bf16x8 qf[2][QC];
+  // 32x32 tiles: column c32 = lane % 32 is tile vector 32 wv + c32; lanes
+  // l and l + 32 hold the two halves (h2) of its k range
+  const int h2 = lane >> 5, c32 = lane & 31;
+  constexpr int QK = D / 16;  // score MFMAs (k = 16) per 32 x 32 tile
+  constexpr int NB = D / 32;  // output blocks of 32 dims
+  int pos1;
+  bf16x8 qf[QK];
   const uint16_t* qb = static_cast<const uint16_t*>(a.query);
-#pragma unroll
-  for (int cb = 0; cb < 2; ++cb) {
-    const int lv = wr0 + 16 * cb + j;
+  {
+    const int lv = wr0 + c32;
     const bool live = lv < tile_vecs;
     const int vv = v0 + lv, row = div_g(vv, G, rG), head = kvh * G + (vv - row * G);
-    pos[cb] = live ? P0 + row : kend - 1;
-    const uint16_t* qp = qb + (static_cast<int64_t>(q0 + row) * a.Hq + head) * D + 8 * g;
+    pos1 = live ? P0 + row : kend - 1;
+    const uint16_t* qp = qb + (static_cast<int64_t>(q0 + row) * a.Hq + head) * D + 8 * h2;
 #pragma unroll
-    for (int c = 0; c < QC; ++c) qf[cb][c] = live ? wave::load_bf16x8<false>(qp + 32 * c) : bf16x8{};
+    for (int c = 0; c < QK; ++c) qf[c] = live ? wave::load_bf16x8<false>(qp + 16 * c) : bf16x8{};
   }
 
   const int64_t rowst = static_cast<int64_t>(a.Hkv) * D;  // elements between slots
@@ -394,125 +394,99 @@ prefill_bf16_kernel(PrefillArgs a) {
     }
   };
 
-  float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
-  f32x4 acc[2][NV];
+  // LDS byte offset of this lane's K piece c in a step's first 32 rows (the
+  // skew repeats every 16 rows, so the second 32 are these plus 32 rows)
+  int kofs[QK];
 #pragma unroll
-  for (int cb = 0; cb < 2; ++cb)
+  for (int c = 0; c < QK; ++c) kofs[c] = c32 * Gm::KROW + 16 * ((2 * c + h2 + kskew<NCH>(c32)) % NCH);
+  float m_run = -INFINITY, l_run = 0.f;
+  f32x16 acc[NB];
 #pragma unroll
-    for (int n = 0; n < NV; ++n) acc[cb][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int n = 0; n < NB; ++n) acc[n] = f32x16{};
 
   // fold 32 keys (rows 32 hs .. 32 hs + 31 of the LDS step at buf, first key
-  // kb) into both column blocks.  The causal mask is applied on every step:
-  // a second, unmasked copy of this code costs more in registers (spills)
-  // than the compare and select it saves.
+  // kb) into the wave's 32 vectors with v_mfma_f32_32x32x16_bf16.  Score
+  // register e of lane l is key 8(e/4) + 4 h2 + e%4 of the 32; P operand m
+  // (k = 16) takes registers 8m .. 8m + 7, i.e. keys 16m + 4 h2 + 0..3 and
+  // 16m + 8 + 4 h2 + 0..3, and the V^T operand reads the same keys.
   auto substep = [&](const char* buf, int kb, int hs) {
-    f32x4 sc[2][2];
+    // at head size 128 two independent accumulation chains (even and odd k
+    // blocks), so the matrix core need not wait for each product before the
+    // next (at 64 the second chain's registers would cost occupancy)
+    f32x16 sc0 = {}, sc1 = {};
+    {
+      const char* kb0 = buf + 32 * hs * Gm::KROW;
 #pragma unroll
-    for (int cb = 0; cb < 2; ++cb)
-#pragma unroll
-      for (int u = 0; u < 2; ++u) sc[cb][u] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int t = 32 * hs + 16 * u + j;
-#pragma unroll
-      for (int c = 0; c < QC; ++c) {
-        const bf16x8 kf = __builtin_bit_cast(
-            bf16x8, *reinterpret_cast<const wave::u32x4*>(
-                        buf + t * Gm::KROW + 16 * ((4 * c + g + kskew<NCH>(t)) % NCH)));
-#pragma unroll
-        for (int cb = 0; cb < 2; ++cb)
-          sc[cb][u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[cb][c], sc[cb][u], 0, 0, 0);
+      for (int c = 0; c < QK; ++c) {
+        const bf16x8 kf = __builtin_bit_cast(bf16x8, *reinterpret_cast<const wave::u32x4*>(kb0 + kofs[c]));
+        if ((c & 1) && D == 128) sc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[c], sc1, 0, 0, 0);
+        else sc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[c], sc0, 0, 0, 0);
       }
     }
-    // online softmax per row in the log2 domain: the running max m_run is
-    // in scaled units, the raw scores are scaled inside the exponent
-    // (scale > 0 keeps their order)
+    f32x16 sc = sc0;
+    if constexpr (D == 128) sc += sc1;
     const float sl2 = a.scale_log2;
-    float alpha[2];
+    float xs[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) xs[e] = sc[e];
+    if (kb + 31 > wmin) {  // some key may be past some row of the wave
+      int k = kb + 4 * h2;
+      asm volatile("" : "+v"(k));  // keep the compares inside the branch
+#pragma unroll
+      for (int e = 0; e < 16; ++e)
+        if (k + 8 * (e >> 2) + (e & 3) > pos1) xs[e] = -INFINITY;
+    }
+    float mx = xs[0];
+#pragma unroll
+    for (int e = 1; e < 16; ++e) mx = fmaxf(mx, xs[e]);
+    mx = max_xor32(mx);
+    const float mxs = mx * sl2;
+    float alpha = 1.f;
+    if (mxs > m_run + kLazyLog2) {
+      if (m_run != -INFINITY) alpha = wave::fast_exp2(m_run - mxs);
+      m_run = mxs;
+    }
+    const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+    float psum = 0.f;
     bf16x8 phi[2], plo[2];
 #pragma unroll
-    for (int cb = 0; cb < 2; ++cb) {
-      float xs[2][4];
+    for (int m = 0; m < 2; ++m)
 #pragma unroll
-      for (int u = 0; u < 2; ++u)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) xs[u][r] = sc[cb][u][r];
-      if (kb + 31 > wmin) {  // some key may be past some row of the wave
-        int k = kb + 4 * g;
-        asm volatile("" : "+v"(k));  // keep the compares inside the branch
-#pragma unroll
-        for (int u = 0; u < 2; ++u)
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            if (k + 16 * u + r > pos[cb]) xs[u][r] = -INFINITY;
+      for (int e = 0; e < 8; e += 2) {
+        const float p0 = wave::fast_exp2(fmaf(xs[8 * m + e], sl2, -m_use));
+        const float p1 = wave::fast_exp2(fmaf(xs[8 * m + e + 1], sl2, -m_use));
+        psum += p0 + p1;
+        const bf16x2 hh = __builtin_convertvector(f32x2{p0, p1}, bf16x2);
+        const uint32_t hw = __builtin_bit_cast(uint32_t, hh);
+        const bf16x2 ll = __builtin_convertvector(
+            f32x2{p0 - __uint_as_float(hw << 16), p1 - __uint_as_float(hw & 0xFFFF0000u)}, bf16x2);
+        phi[m][e] = hh.x;
+        phi[m][e + 1] = hh.y;
+        plo[m][e] = ll.x;
+        plo[m][e + 1] = ll.y;
       }
-      float mx = xs[0][0];
+    l_run = l_run * alpha + psum;
+    if (__any(alpha != 1.f)) {
+      float al = alpha;
+      asm volatile("" : "+v"(al));  // keep the multiplies inside the branch
 #pragma unroll
-      for (int u = 0; u < 2; ++u)
+      for (int n = 0; n < NB; ++n) acc[n] *= al;
+    }
+    // V^T operand of output block n (dims 32n .. 32n + 31) for P operand m:
+    // the 16-lane group (h2, half) reads the 4-row x 16-column blocks at
+    // keys 16m + 4 h2 (+ 8) and dims 32n + 16 half, lane j getting column j
+    const char* vt = buf + Gm::KBYTES + (32 * hs + 4 * h2 + ((lane & 15) >> 2)) * Gm::VROW +
+                     32 * ((lane >> 4) & 1) + 8 * (lane & 3);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) mx = fmaxf(mx, xs[u][r]);
-      mx = max_xor32(max_xor16(mx));
-      // The reference max m_run moves only when this step's max passes it
-      // by more than kLazyLog2: the weights then stay below 2^kLazyLog2
-      // (still exact to ~16 bits in the hi + lo split, sums far from
-      // overflow) and the accumulators are rescaled on few steps instead of
-      // on almost every one.  A row's first keys set it without a rescale
-      // (nothing is accumulated yet).
-      const float mxs = mx * sl2;
-      alpha[cb] = 1.f;
-      if (mxs > m_run[cb] + kLazyLog2) {
-        if (m_run[cb] != -INFINITY) alpha[cb] = wave::fast_exp2(m_run[cb] - mxs);
-        m_run[cb] = mxs;
+    for (int n = 0; n < NB; ++n)
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        const bf16x4 w0 = lds_read_tr16(vt + 16 * m * Gm::VROW + 64 * n);
+        const bf16x4 w1 = lds_read_tr16(vt + (16 * m + 8) * Gm::VROW + 64 * n);
+        const bf16x8 vb = __builtin_shufflevector(w0, w1, 0, 1, 2, 3, 4, 5, 6, 7);
+        acc[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vb, phi[m], acc[n], 0, 0, 0);
+        acc[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vb, plo[m], acc[n], 0, 0, 0);
       }
-      const float m_use = (m_run[cb] == -INFINITY) ? 0.f : m_run[cb];
-      float psum = 0.f;
-#pragma unroll
-      for (int u = 0; u < 2; ++u)
-#pragma unroll
-        for (int r = 0; r < 4; r += 2) {
-          const float p0 = wave::fast_exp2(fmaf(xs[u][r], sl2, -m_use));
-          const float p1 = wave::fast_exp2(fmaf(xs[u][r + 1], sl2, -m_use));
-          psum += p0 + p1;
-          // P = hi + lo, both bf16 (pairs converted together)
-          const bf16x2 h = __builtin_convertvector(f32x2{p0, p1}, bf16x2);
-          const uint32_t hw = __builtin_bit_cast(uint32_t, h);
-          const bf16x2 l = __builtin_convertvector(
-              f32x2{p0 - __uint_as_float(hw << 16), p1 - __uint_as_float(hw & 0xFFFF0000u)}, bf16x2);
-          phi[cb][4 * u + r] = h.x;
-          phi[cb][4 * u + r + 1] = h.y;
-          plo[cb][4 * u + r] = l.x;
-          plo[cb][4 * u + r + 1] = l.y;
-        }
-      l_run[cb] = l_run[cb] * alpha[cb] + psum;
-    }
-    // the accumulators need rescaling only when some row's max moved
-    if (__any(alpha[0] != 1.f || alpha[1] != 1.f)) {
-      float al[2] = {alpha[0], alpha[1]};
-      asm volatile("" : "+v"(al[0]), "+v"(al[1]));  // keep the multiplies inside the branch
-#pragma unroll
-      for (int cb = 0; cb < 2; ++cb)
-#pragma unroll
-        for (int n = 0; n < NV; ++n) acc[cb][n] *= al[cb];
-    }
-    // O^T += V^T . P^T per 16-dim output block n.  The V^T operand comes
-    // straight from the row-major V tile: ds_read_b64_tr_b16 hands lane j of
-    // each 16-lane group column j of the 4-row x 16-column block its lanes
-    // address (lane j names row j/4, columns 4(j%4) .. +3).  Group g
-    // addresses keys 16u + 4g .. 16u + 4g + 3 of the substep -- the keys
-    // its P slots 4u .. 4u + 3 hold -- and dims 16n .. 16n + 15.
-    const char* vt = buf + Gm::KBYTES + (32 * hs + 4 * g + (j >> 2)) * Gm::VROW + 8 * (j & 3);
-#pragma unroll
-    for (int n = 0; n < NV; ++n) {
-      const bf16x4 v0 = lds_read_tr16(vt + 32 * n);
-      const bf16x4 v1 = lds_read_tr16(vt + 16 * Gm::VROW + 32 * n);
-      const bf16x8 vb = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
-#pragma unroll
-      for (int cb = 0; cb < 2; ++cb) {
-        f32x4 o = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vb, phi[cb], acc[cb][n], 0, 0, 0);
-        o = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vb, plo[cb], o, 0, 0, 0);
-        acc[cb][n] = o;
-      }
-    }
   };
 
   if (nsteps > 0) {
@@ -525,9 +499,7 @@ prefill_bf16_kernel(PrefillArgs a) {
   // allowing for their loads still being in flight on the first pass, makes
   // every step's first score wait for the oldest K/V loads of the next step.
 #pragma unroll
-  for (int cb = 0; cb < 2; ++cb)
-#pragma unroll
-    for (int c = 0; c < QC; ++c) asm volatile("" : "+v"(qf[cb][c]));
+  for (int c = 0; c < QK; ++c) asm volatile("" : "+v"(qf[c]));
   __syncthreads();
   for (int q = 0; q < nsteps; ++q) {
     const char* cur = lds + (q & 1) * Gm::BUF;
@@ -552,19 +524,19 @@ prefill_bf16_kernel(PrefillArgs a) {
   // finish: normalise, stage rows [kPRows][SROW] in LDS (no wave reads K/V any
   // more), then store whole rows
   float* rows = reinterpret_cast<float*>(lds);
-#pragma unroll
-  for (int cb = 0; cb < 2; ++cb) {
-    float lsum = l_run[cb] + __shfl_xor(l_run[cb], 16, 64);
-    lsum += __shfl_xor(lsum, 32, 64);
+  {
+    const float lsum = l_run + __shfl_xor(l_run, 32, 64);
     const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
-    float* dst = rows + (wr0 + 16 * cb + j) * Gm::SROW;
+    float* dst = rows + (wr0 + c32) * Gm::SROW;
 #pragma unroll
-    for (int n = 0; n < NV; ++n) {  // dims 16n + 4g .. 16n + 4g + 3
-      float4 o = make_float4(acc[cb][n][0] * inv, acc[cb][n][1] * inv,
-                             acc[cb][n][2] * inv, acc[cb][n][3] * inv);
-      if (bad) o = make_float4(NAN, NAN, NAN, NAN);
-      *reinterpret_cast<float4*>(dst + 16 * n + 4 * g) = o;
-    }
+    for (int n = 0; n < NB; ++n)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {  // dims 32n + 8i + 4 h2 .. + 3
+        float4 o = make_float4(acc[n][4 * i] * inv, acc[n][4 * i + 1] * inv,
+                               acc[n][4 * i + 2] * inv, acc[n][4 * i + 3] * inv);
+        if (bad) o = make_float4(NAN, NAN, NAN, NAN);
+        *reinterpret_cast<float4*>(dst + 32 * n + 8 * i + 4 * h2) = o;
+      }
   }
   __syncthreads();
   constexpr int D4 = D / 4;
