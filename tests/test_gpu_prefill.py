@@ -86,6 +86,41 @@ def test_prefill_small_all_rows(case):
     check_rows(pw, run(pw))
 
 
+def test_many_sequences_with_empty_and_bad_chunks():
+    """The launch's work ranking over many sequences: 300 chunks of 0 .. 40
+    rows (a third empty) after 0 .. 600 cached tokens, plus a few long ones,
+    GQA 14/2 at head size 64 -- every row against the oracle; then the same
+    batch with a few sequences made bad (a context shorter than its chunk),
+    whose rows alone turn NaN."""
+    rng = np.random.default_rng(990)
+    S = 300
+    chunks = np.where(rng.random(S) < 0.33, 0, rng.integers(1, 41, size=S))
+    chunks[[7, 150, 299]] = [700, 300, 513]
+    cached = rng.integers(0, 601, size=S)
+    pw = workloads.prefill(990, cached, chunks, num_q_heads=14, num_kv_heads=2, head_size=64)
+    say(f"[prefill] {S} sequences, {pw.num_tokens} rows")
+    got = run(pw)
+    check_rows(pw, got)
+    w = pw.cache
+    st = H.upload(w, device=DEV)
+    q = H.to_torch(pw.query, "bf16", DEV)
+    qs = torch.from_numpy(pw.query_start).to(DEV)
+    bad = [s for s in (7, 40, 41, 150) if chunks[s] > 0]
+    lens_bad = st.lens.clone()
+    for s in bad:
+        lens_bad[s] = int(chunks[s]) - 1
+    out = torch.full((pw.num_tokens, 14, 64), 7.0, device=DEV)
+    pkv.attention_prefill(q, st.kv, st.tables, lens_bad, qs, w.scale,
+                          max_query_len=pw.max_query_len, out=out)
+    torch.cuda.synchronize()
+    got2 = out.cpu().numpy()
+    bad_rows = np.zeros(pw.num_tokens, dtype=bool)
+    for s in bad:
+        bad_rows[pw.query_start[s]:pw.query_start[s + 1]] = True
+    assert np.isnan(got2[bad_rows]).all()
+    assert np.array_equal(got2[~bad_rows], got[~bad_rows])
+
+
 def test_prefill_bf16_output():
     pw = workloads.prefill(950, [10, 0], [150, 70], num_q_heads=8, num_kv_heads=2)
     got32 = run(pw)
