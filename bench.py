@@ -1115,7 +1115,10 @@ def all_configs(args, names, cpu) -> int:
     (what a process did before carries over: the long-context attention
     measured 4% slower after the other workloads than alone), then the
     streaming-read ceilings at 2 GiB and at each workload's bytes per launch,
-    assembled into one line headed by args.workload."""
+    assembled into one line headed by args.workload.  The headline workload
+    goes first: the GPU has been idle during the CPU-oracle phase, while
+    ~20 s of sustained streaming settles it ~4% slower for the runs after
+    (back-to-back processes show the same; 20 s of idle restores it)."""
     runs = {}
     for name in names:
         extra = ["--workload", name, "--only", "--no-cpu-baseline"]

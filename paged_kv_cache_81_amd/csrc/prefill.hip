@@ -315,7 +315,7 @@ prefill_bf16_kernel(PrefillArgs a) {
   const int kend = tile_kend<kPRows>(qlen, L, bad_seq, x, G, rG);  // keys [0, kend)
   const int nsteps = (kend + kPKeys - 1) / kPKeys;
 
-  // this wave's vectors: column j of block cb is tile vector 32 wv + 16 cb + j
+  // this wave's vectors: tile vectors 32 wv .. 32 wv + 31
   const int wr0 = 32 * wv;
   const int wave_vecs = max(0, min(32, tile_vecs - wr0));
   const int wmin = P0 + div_g(v0 + wr0, G, rG);    // position of the wave's first row
