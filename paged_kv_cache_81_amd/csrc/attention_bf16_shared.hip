@@ -38,54 +38,75 @@ struct Plan {
   int glp[kMaxSharedGroups];        // prefix length of group g
   int lp[kMaxCompactSeqs];          // prefix length of s's group, -1 if s gives NaN
   int len[kMaxCompactSeqs];
-  int wsum[kWaves];
   int bad;
   int16_t gs[kMaxSharedGroups + 1];  // group starts (checked to lie in [0, S])
-  int16_t lead[kMaxCompactSeqs];     // first sequence of s's group
+  int16_t order[kMaxCompactSeqs];    // sequences by their own steps, longest first
 };
 
 static_assert(sizeof(Plan) <= kSharedPlanInts * sizeof(int), "plan larger than budgeted");
 
-// Exclusive scan of c(i), i < n <= 2 * kThreads, into out[0 .. n] (out[n]
-// is the total).  c(i) may read out[i] (a scan in place): every c(i) is
-// read before anything is written.
-template <typename F>
-__device__ __forceinline__ void block_scan(int n, int* out, int* wsum, F c) {
+// Inclusive prefix sum over the wave's 64 lanes with DPP moves: shifts by 1,
+// 2, 4, 8 lanes inside each row of 16, then the last lane of row 0 added to
+// row 1 and of row 2 to row 3 (row_bcast:15), then lane 31 to rows 2 and 3
+// (row_bcast:31).  A lane with no source lane adds 0.
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false);  // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false);  // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false);  // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);  // row_bcast:15, rows 1 and 3
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);  // row_bcast:31, rows 2 and 3
+  return v;
+}
+
+// Exclusive scans over the workgroup of NV per-thread values at once (in
+// thread order): v[n] becomes the sum of v[n] over the threads before this
+// one, total[n] the sum over all.  wsum: NV * kWaves ints of LDS, free until
+// the next barrier after the call.
+template <int NV>
+__device__ __forceinline__ void block_excl_scan(int (&v)[NV], int (&total)[NV], int* wsum) {
   const int lane = threadIdx.x & 63;
   const int wv = threadIdx.x >> 6;
-  const int i0 = 2 * threadIdx.x;
-  const int c0 = i0 < n ? c(i0) : 0;
-  const int c1 = i0 + 1 < n ? c(i0 + 1) : 0;
-  int v = c0 + c1;
+  int inc[NV];
 #pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int t = __shfl_up(v, d, 64);
-    if (lane >= d) v += t;
-  }
-  if (lane == 63) wsum[wv] = v;
-  __syncthreads();
-  int before = 0, total = 0;
+  for (int n = 0; n < NV; ++n) inc[n] = wave_incl_scan(v[n]);
+  if (lane == 63)
 #pragma unroll
-  for (int w = 0; w < kWaves; ++w) {
-    before += w < wv ? wsum[w] : 0;
-    total += wsum[w];
-  }
-  const int excl = before + v - c0 - c1;
-  __syncthreads();  // every c(i) has been read
-  if (i0 < n) out[i0] = excl;
-  if (i0 + 1 < n) out[i0 + 1] = excl + c0;
-  if (threadIdx.x == 0) out[n] = total;
+    for (int n = 0; n < NV; ++n) wsum[n * kWaves + wv] = inc[n];
   __syncthreads();
+#pragma unroll
+  for (int n = 0; n < NV; ++n) {
+    int before = 0, sum = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const int x = wsum[n * kWaves + w];
+      before += w < wv ? x : 0;
+      sum += x;
+    }
+    v[n] = before + inc[n] - v[n];
+    total[n] = sum;
+  }
 }
 
 // Last index i in [0, n) with v[i] <= x (v non-decreasing, v[0] <= x).
-__device__ __forceinline__ int last_le(const int* v, int n, int x) {
+template <typename T>
+__device__ __forceinline__ int last_le(const T* v, int n, int x) {
   int lo = 0, up = n - 1;
   while (lo < up) {
     const int mid = (lo + up + 1) >> 1;
     if (v[mid] <= x) lo = mid; else up = mid - 1;
   }
   return lo;
+}
+
+// v / d for 0 <= v < 2^31, d >= 1 (rd = 1.0 / d): a double-precision
+// estimate, then one step of correction either way
+__device__ __forceinline__ int div_by(int v, int d, double rd) {
+  int q = static_cast<int>(static_cast<double>(v) * rd);
+  const int r = v - q * d;
+  q += r >= d ? 1 : 0;
+  q -= r < 0 ? 1 : 0;
+  return q;
 }
 
 template <int B>
@@ -98,69 +119,156 @@ __device__ __forceinline__ bool seq_ok(const AttnArgs& a, int L) {
 // the table and max_prefix and is no longer than any valid member; members
 // of an invalid group, and invalid sequences, give NaN.  Workgroup 0 also
 // records each sequence's parts, group leader and prefix for the merge.
+// Suffix items are listed by sequence, longest suffix first: a stable
+// counting sort on the steps of each sequence's own tokens (capped), so every
+// workgroup derives the same list.  Few barriers and dependent LDS reads: the
+// plan is all a workgroup does before its first loads.
+constexpr int kSortBins = 64;
+constexpr int kSortChunks = kMaxCompactSeqs / 64;  // 64 sequences a chunk, one wave each
+// scratch LDS: chunk histograms, group flags, item counts in sorted order,
+// bin offsets, scan partials
+constexpr int kPlanScratchInts =
+    kSortChunks * kSortBins + kMaxSharedGroups + kMaxCompactSeqs + kSortBins + 2 * kWaves;
+
 template <int B>
-__device__ void make_plan(const AttnArgs& a, Plan& p, int HGN, int chunks, int G) {
+__device__ void make_plan(const AttnArgs& a, Plan& p, int HGN, int chunks, int G, int* scratch) {
+  static_assert(kMaxCompactSeqs == 2 * kThreads && kMaxSharedGroups == 2 * kThreads &&
+                kSortBins <= 2 * kThreads, "plan layout: two sequences and groups a thread");
   constexpr int kUnit = B > 32 ? B : 32;  // partitions start on whole steps and blocks
   const int ng = a.num_groups, S = a.S, P = a.partition;
-  if (threadIdx.x == 0) p.bad = 0;
-  __syncthreads();
-  for (int i = threadIdx.x; i <= ng; i += kThreads) {
+  const double rP = 1.0 / P;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  int* hist = scratch;                         // [chunk][bin]: sequences of the chunk in the bin
+  int* gbad = hist + kSortChunks * kSortBins;  // [group]: a valid member is shorter than the prefix
+  int* cnt = gbad + kMaxSharedGroups;          // [rank]: suffix items of the rank's sequence
+  int* boff = cnt + kMaxCompactSeqs;           // [bin]: sequences in earlier bins
+  int* wsum = boff + kSortBins;
+
+  // 1. inputs, in one round of loads; clear the flags and histograms
+  bool bad = false;
+  if (tid == 0) p.bad = 0;
+  for (int i = tid; i < kSortChunks * kSortBins; i += kThreads) hist[i] = 0;
+  for (int i = tid; i < ng; i += kThreads) gbad[i] = 0;
+  for (int i = tid; i <= ng; i += kThreads) {
     const int v = a.group_starts[i];
-    if (v < 0 || v > S) p.bad = 1;
+    const int next = i < ng ? a.group_starts[i + 1] : S;
+    bad = bad || v < 0 || v > S || v > next || (i == 0 && v != 0) || (i == ng && v != S);
     p.gs[i] = static_cast<int16_t>(v);
   }
-  for (int i = threadIdx.x; i < S; i += kThreads) p.len[i] = a.lens[i];
+  for (int i = tid; i < ng; i += kThreads) p.glp[i] = a.prefix_lens[i];
+  for (int i = tid; i < S; i += kThreads) p.len[i] = a.lens[i];
   __syncthreads();
-  for (int i = threadIdx.x; i < ng; i += kThreads)
-    if (p.gs[i] > p.gs[i + 1]) p.bad = 1;
-  if (threadIdx.x == 0 && (p.gs[0] != 0 || p.gs[ng] != S)) p.bad = 1;
+
+  // 2. each sequence s = tid + 256 j: its group (meaningless, but in range,
+  // when the starts are bad) and whether it makes the group invalid
+  if (bad) p.bad = 1;
+  int grp[2], glen[2], len[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int s = tid + j * kThreads;
+    grp[j] = 0;
+    glen[j] = -1;
+    len[j] = 0;
+    if (s < S) {
+      grp[j] = last_le(p.gs, ng, s);
+      glen[j] = p.glp[grp[j]];
+      len[j] = p.len[s];
+      if (seq_ok<B>(a, len[j]) && len[j] < glen[j]) gbad[grp[j]] = 1;
+    }
+  }
   __syncthreads();
+
+  // 3. prefixes, item counts, sort keys; groups g = 2 tid + e
   const bool all_bad = p.bad != 0;
   const bool rec = blockIdx.x == 0;
-
-  // per group: its prefix items (into pscan, scanned below) and its members' prefix
-  for (int g = threadIdx.x; g < ng; g += kThreads) {
-    int count = 0;
-    p.glp[g] = 0;
-    if (!all_bad) {
-      const int s0 = p.gs[g], s1 = p.gs[g + 1];
-      const int lp = a.prefix_lens[g];
-      p.glp[g] = lp;
-      bool ok = lp >= 0 && lp <= a.max_prefix && lp % kUnit == 0 && (lp + B - 1) / B <= a.width;
-      for (int s = s0; s < s1 && ok; ++s)
-        if (seq_ok<B>(a, p.len[s]) && p.len[s] < lp) ok = false;
-      for (int s = s0; s < s1; ++s) {
-        const int L = p.len[s];
-        const bool good = ok && seq_ok<B>(a, L);
-        p.lp[s] = good ? lp : -1;
-        p.lead[s] = s0;
-        if (rec) {
-          a.ws_seq[s] = good ? (lp + P - 1) / P + (L - lp + P - 1) / P : -1;
-          a.ws_seq[S + s] = s0;
-          a.ws_seq[2 * S + s] = good ? lp : 0;
-        }
-      }
-      const int M = s1 - s0;
-      if (ok && lp > 0 && M > 0) count = HGN * ((M * G + 15) / 16) * ((lp + P - 1) / P);
-    }
-    p.pscan[g] = count;
-  }
-  if (all_bad)
-    for (int s = threadIdx.x; s < S; s += kThreads) {
-      p.lp[s] = -1;
-      p.lead[s] = s;
+  auto group_ok = [&](int g, int lp) {
+    return !all_bad && gbad[g] == 0 && lp >= 0 && lp <= a.max_prefix && lp % kUnit == 0 &&
+           (lp + B - 1) / B <= a.width;
+  };
+  const uint64_t below = (uint64_t{1} << lane) - 1;
+  int items[2], bin[2], pos[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int s = tid + j * kThreads;
+    const int L = len[j];
+    const int lp = s < S && group_ok(grp[j], glen[j]) && seq_ok<B>(a, L) ? glen[j] : -1;
+    if (s < S) {
+      p.lp[s] = lp;
       if (rec) {
-        a.ws_seq[s] = -1;
-        a.ws_seq[S + s] = s;
-        a.ws_seq[2 * S + s] = 0;
+        a.ws_seq[s] = lp >= 0 ? div_by(lp + P - 1, P, rP) + div_by(L - lp + P - 1, P, rP) : -1;
+        a.ws_seq[S + s] = all_bad ? s : p.gs[grp[j]];
+        a.ws_seq[2 * S + s] = lp >= 0 ? lp : 0;
       }
     }
+    items[j] = lp < 0 ? 0 : HGN * chunks * div_by(L - lp + P - 1, P, rP);
+    const int key = lp < 0 ? 0 : min((L - lp + kStep - 1) / kStep, kSortBins - 1);
+    // sequence s lies in chunk s / 64, lane s % 64; the lanes of its bin come
+    // from a ballot per bit of the bin
+    bin[j] = kSortBins - 1 - key;
+    uint64_t same = __ballot(s < S);
+#pragma unroll
+    for (int bit = 1; bit < kSortBins; bit <<= 1) {
+      const uint64_t m = __ballot((bin[j] & bit) != 0);
+      same &= (bin[j] & bit) ? m : ~m;
+    }
+    pos[j] = __popcll(same & below);
+    if (s < S && pos[j] == 0) hist[(s >> 6) * kSortBins + bin[j]] = __popcll(same);
+  }
+  int sc[2] = {0, 0};  // scanned: prefix items of groups 2 tid, 2 tid + 1; sequences in bins 2 tid, 2 tid + 1
+  int pre[2] = {0, 0};
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    const int g = 2 * tid + e;
+    if (g < ng) {
+      const int s0 = p.gs[g], M = p.gs[g + 1] - s0, lp = p.glp[g];
+      if (group_ok(g, lp) && lp > 0 && M > 0)
+        pre[e] = HGN * ((M * G + 15) / 16) * div_by(lp + P - 1, P, rP);
+    }
+  }
   __syncthreads();
-  block_scan(ng, p.pscan, p.wsum, [&](int g) { return p.pscan[g]; });
-  block_scan(S, p.sscan, p.wsum, [&](int s) {
-    const int lp = p.lp[s];
-    return lp < 0 ? 0 : HGN * chunks * ((p.len[s] - lp + P - 1) / P);
-  });
+
+  // 4. scans of the groups' prefix items and of the bins' sizes
+  int bsz[2] = {0, 0};
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    const int k = 2 * tid + e;
+    if (k < kSortBins)
+#pragma unroll
+      for (int c = 0; c < kSortChunks; ++c) bsz[e] += hist[c * kSortBins + k];
+  }
+  int v2[2] = {pre[0] + pre[1], bsz[0] + bsz[1]}, tot2[2];
+  block_excl_scan<2>(v2, tot2, wsum);
+  if (2 * tid < ng) p.pscan[2 * tid] = v2[0];
+  if (2 * tid + 1 < ng) p.pscan[2 * tid + 1] = v2[0] + pre[0];
+  if (tid == 0) p.pscan[ng] = tot2[0];
+  if (2 * tid < kSortBins) boff[2 * tid] = v2[1];
+  if (2 * tid + 1 < kSortBins) boff[2 * tid + 1] = v2[1] + bsz[0];
+  __syncthreads();
+
+  // 5. rank of each sequence: earlier bins, then earlier chunks of its bin,
+  // then lower lanes of its chunk
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int s = tid + j * kThreads;
+    if (s < S) {
+      int r = boff[bin[j]] + pos[j];
+      for (int c = 0; c < (s >> 6); ++c) r += hist[c * kSortBins + bin[j]];
+      p.order[r] = static_cast<int16_t>(s);
+      cnt[r] = items[j];
+    }
+  }
+  __syncthreads();
+
+  // 6. suffix items before each rank
+  const int c0 = 2 * tid < S ? cnt[2 * tid] : 0;
+  const int c1 = 2 * tid + 1 < S ? cnt[2 * tid + 1] : 0;
+  int v1[1] = {c0 + c1}, tot1[1];
+  block_excl_scan<1>(v1, tot1, wsum);
+  if (2 * tid < S) p.sscan[2 * tid] = v1[0];
+  if (2 * tid + 1 < S) p.sscan[2 * tid + 1] = v1[0] + c0;
+  if (tid == 0) p.sscan[S] = tot1[0];
+  __syncthreads();
 }
 
 template <int D, int B, int HG, bool NT, bool KL>
@@ -172,6 +280,8 @@ attention_bf16_shared_kernel(AttnArgs a) {
   constexpr int NSLOT = kWaves / HG;  // items a workgroup works on at once
   extern __shared__ float s_dyn[];
   __shared__ Plan p;
+  // the plan's scratch lies in the dynamic LDS (at least one result slot a wave)
+  static_assert(kPlanScratchInts <= kWaves * 16 * (D + 4), "plan scratch exceeds dynamic LDS");
 
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -182,7 +292,7 @@ attention_bf16_shared_kernel(AttnArgs a) {
   const int HGN = a.Hkv / HG;
   const int P = a.partition;
   const int ng = a.num_groups;
-  make_plan<B>(a, p, HGN, chunks, G);
+  make_plan<B>(a, p, HGN, chunks, G, reinterpret_cast<int*>(s_dyn));
   const int t_pre = p.pscan[ng];
   const int total = t_pre + p.sscan[a.S];
 
@@ -191,7 +301,9 @@ attention_bf16_shared_kernel(AttnArgs a) {
   // read)?  A mismatch makes the merge give NaN for s.
   if (wv == 0)
     for (int s = blockIdx.x; s < a.S; s += gridDim.x) {
-      const int lp = p.lp[s], lead = p.lead[s];
+      const int lp = p.lp[s];
+      // s's group (valid groups have non-decreasing starts): its leader
+      const int lead = lp > 0 ? p.gs[last_le(p.gs, ng, s)] : s;
       bool diff = false;
       if (lp > 0 && lead != s) {
         const int32_t* mine = a.tables + static_cast<int64_t>(s) * a.width;
@@ -285,11 +397,12 @@ attention_bf16_shared_kernel(AttnArgs a) {
     } else {
       // suffix item: sequence s, (kv-head group, query-head chunk) y, partition q
       const int x = it - t_pre;
-      const int s = last_le(p.sscan, a.S, x);
+      const int k = last_le(p.sscan, a.S, x);
+      const int s = p.order[k];
       const int lp = p.lp[s];
       const int L = p.len[s];
       const int NQ = (L - lp + P - 1) / P;
-      const int local = x - p.sscan[s];
+      const int local = x - p.sscan[k];
       const int q = local % NQ;
       const int y = local / NQ;
       const int chunk = y % chunks;

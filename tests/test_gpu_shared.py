@@ -180,3 +180,23 @@ def test_invalid_groups_give_nan_rows():
     assert np.isnan(got[9]).all()
     keep = [s for s in range(w.num_seqs) if s != 9]
     check_rows(got[keep], ref[keep], "the other members")
+
+
+def test_most_sequences_and_long_suffixes():
+    """512 sequences (the most the shared-prefix decode takes) in 64 groups,
+    own tokens 0-8500: suffix items are listed longest first by a sort whose
+    keys are capped at 63 steps (2016 tokens), over all eight 64-sequence
+    chunks; every row must match whichever workgroup takes it."""
+    w = workloads.shared_prefix(seed=65, num_prompts=64, prompt_len=64, forks=8,
+                                max_private=8500, num_q_heads=8, num_kv_heads=2, head_size=64,
+                                block_size=16)
+    assert w.num_seqs == 512
+    say(f"[shared] S=512 max_len={w.max_context_len}")
+    ref = oracle_out(w)
+    st = H.upload(w)
+    gs, pl, maxp = groups_on_device(w)
+    assert len(pl) == 64 and maxp == 64
+    got = attend_shared(st, gs, pl, maxp).cpu().numpy()
+    check_rows(got, ref, "512 sequences, long suffixes")
+    again = attend_shared(st, gs, pl, maxp).cpu().numpy()
+    assert np.array_equal(got, again), "repeated calls give identical bits"
