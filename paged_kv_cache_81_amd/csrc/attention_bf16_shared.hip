@@ -292,15 +292,18 @@ attention_bf16_shared_kernel(AttnArgs a) {
   const int HGN = a.Hkv / HG;
   const int P = a.partition;
   const int ng = a.num_groups;
+  // the grid's size from the arguments (read with the others at the start),
+  // not from the dispatch's hidden arguments
+  const int nwg = a.stream_waves / kWaves;
   make_plan<B>(a, p, HGN, chunks, G, reinterpret_cast<int*>(s_dyn));
   const int t_pre = p.pscan[ng];
   const int total = t_pre + p.sscan[a.S];
 
-  // Sequences s = blockIdx.x, + gridDim.x, ...: do s's own table entries for
+  // Sequences s = blockIdx.x, + nwg, ...: do s's own table entries for
   // its group's prefix match its leader's (whose table the prefix items
   // read)?  A mismatch makes the merge give NaN for s.
   if (wv == 0)
-    for (int s = blockIdx.x; s < a.S; s += gridDim.x) {
+    for (int s = blockIdx.x; s < a.S; s += nwg) {
       const int lp = p.lp[s];
       // s's group (valid groups have non-decreasing starts): its leader
       const int lead = lp > 0 ? p.gs[last_le(p.gs, ng, s)] : s;
@@ -317,7 +320,6 @@ attention_bf16_shared_kernel(AttnArgs a) {
   // Workgroup b runs on XCD b mod 8; with one item per workgroup, pair
   // workgroups b and b + 8 (same XCD) on consecutive items -- the column
   // blocks of one prefix partition.
-  const int nwg = gridDim.x;
   int b = blockIdx.x;
   if (NSLOT == 1 && nwg % 16 == 0) b = (b / 16) * 16 + 2 * (b % 8) + (b / 8) % 2;
 

@@ -189,18 +189,22 @@ __global__ void __launch_bounds__(64 * kWaves) reduce_stream_kernel(AttnArgs a) 
 // 0: an empty context, zero output); part p of (s, h) is workspace row
 // p*S*Hq + s*Hq + h, so each part of a sequence is Hq*D contiguous floats.
 // ws_seq[3S + s] is set when s's own table entries for its group's prefix
-// differ from those the prefix was read through: NaN.  One workgroup per
-// sequence; thread t combines the parts of dims 4e .. 4e + 3 of its rows (e =
-// t, t + 256, ...), parts in order, so every load instruction reads 4 KB of
-// one part.  A part with NaN statistics poisons its row.
-__global__ void __launch_bounds__(256) reduce_shared_kernel(AttnArgs a) {
-  const int s = blockIdx.x;
+// differ from those the prefix was read through: NaN.  Workgroup b takes
+// sequence b / per (per = 256-piece runs of its Hq*D/4 float4 pieces) and
+// thread t piece e = (b % per) * 256 + t, dims 4e .. 4e + 3 of its rows,
+// parts in order: one piece a thread keeps each thread's chain of dependent
+// loads short (the sequence's record, the parts' (m, l), their outputs), and
+// every load instruction reads 4 KB of one part.  A part with NaN statistics
+// poisons its row.
+__global__ void __launch_bounds__(256) reduce_shared_kernel(AttnArgs a, int per) {
+  const int s = blockIdx.x / per;
+  const int e = (blockIdx.x - s * per) * 256 + threadIdx.x;
   const int64_t SH = static_cast<int64_t>(a.S) * a.Hq;
   const int np = a.ws_seq[s];
   const bool bad = np < 0 || a.ws_seq[3 * a.S + s] != 0;
   const int nvec = a.Hq * a.D / 4;
   const int64_t row0 = static_cast<int64_t>(s) * a.Hq;
-  for (int e = threadIdx.x; e < nvec; e += blockDim.x) {
+  if (e < nvec) {
     const int h = 4 * e / a.D;
     const int64_t row = row0 + h;
     float4 r;
@@ -248,7 +252,8 @@ __global__ void __launch_bounds__(256) reduce_shared_kernel(AttnArgs a) {
 
 int launch_reduce_shared(const AttnArgs& a, hipStream_t stream) {
   if (a.S == 0) return PKV_OK;
-  reduce_shared_kernel<<<dim3(a.S), dim3(256), 0, stream>>>(a);
+  const int per = (a.Hq * a.D / 4 + 255) / 256;
+  reduce_shared_kernel<<<dim3(static_cast<unsigned>(a.S) * per), dim3(256), 0, stream>>>(a, per);
   return check_launch("partition merge (shared prefix)");
 }
 
