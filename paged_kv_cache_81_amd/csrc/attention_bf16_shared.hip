@@ -423,7 +423,7 @@ attention_bf16_shared_kernel(AttnArgs a) {
     if (used == K) flush();
     const int i = used++;
     w.begin_rows(a, qrow, tab, kvh, t0, t1);
-    w.run((t1 - t0 + kStep - 1) / kStep, [](int) {});
+    w.run_single((t1 - t0 + kStep - 1) / kStep, [](int) {});
     w.finish(rows + i * 16 * SROW, mls + 2 * i * 16, nh);
     if (lane == 0) {
       int* m = meta + kSharedMeta * i;

@@ -392,6 +392,20 @@ struct Wave {
     }
   }
 
+  // The same with one step in flight: issue step q, then fold it in.  For
+  // schedules that keep many waves per CU busy (the shared-prefix decode,
+  // eight waves a CU), this halves the bytes in flight and the K/V
+  // registers.
+  template <typename F>
+  __device__ __forceinline__ void run_single(int nsteps, F&& at_step) {
+    Step buf;
+    for (int q = 0; q < nsteps; ++q) {
+      issue(buf, q);
+      at_step(q);
+      compute<true>(buf, q);
+    }
+  }
+
   // Write the partition's normalised output rows [hh][SROW] (head hh of the
   // wave's query heads) and (m, l) pairs into LDS and start afresh.  Lane
   // (j, g) holds head j, dims NV*(4g + r) + n.  A poisoned partition gives NaN.
