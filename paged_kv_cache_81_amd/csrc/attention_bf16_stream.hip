@@ -210,7 +210,7 @@ attention_bf16_stream_kernel(AttnArgs a) {
                                       : a.tables[static_cast<int64_t>(s) * a.width + (L - 1) / B];
         bad_new = !store_new(phys);
       }
-      w.run((t1 - t0 + kStep - 1) / kStep, [](int) {});
+      w.run_single((t1 - t0 + kStep - 1) / kStep, [](int) {});
       if (bad_new) w.bad_blk = true;  // (the step reading it flags it too)
       w.finish(srow, sml, nh);
     }

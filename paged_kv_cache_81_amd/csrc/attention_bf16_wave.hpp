@@ -375,7 +375,9 @@ struct Wave {
   // loads in flight per CU deepen the HBM queues, as a plain streaming read
   // also shows; awaiting each step before issuing the next and overlapping
   // its arithmetic, 3% slower on the OPT-13B shape; one register buffer,
-  // and the same order as here with explicit waits, 5% slower on it.
+  // and the same order as here with explicit waits, 5% slower on it.  The
+  // fixed-partition kernel uses this loop; the stream and shared-prefix
+  // kernels use run_single below.
   // at_step(q) runs before step q is folded in (partition boundaries).
   template <typename F>
   __device__ __forceinline__ void run(int nsteps, F&& at_step) {
@@ -392,10 +394,13 @@ struct Wave {
     }
   }
 
-  // The same with one step in flight: issue step q, then fold it in.  For
-  // schedules that keep many waves per CU busy (the shared-prefix decode,
-  // eight waves a CU), this halves the bytes in flight and the K/V
-  // registers.
+  // The same with one step in flight: issue step q, then fold it in.  Half
+  // the bytes a wave has in flight at once and half the K/V registers (at
+  // head size 128, 153-165 VGPRs against 253).  Measured against run() on
+  // one box, each run after 20 s idle: OPT-13B-shaped stream 220.9-221.0 vs
+  // 222.2-222.9 us, long-context 328.5-328.6 vs 328.7-329.0 us, Qwen2-shaped
+  // 26.4-26.9 us both; the shared-prefix decode (eight waves a CU) 62.3-62.8
+  // vs 62.8-64.8 us.
   template <typename F>
   __device__ __forceinline__ void run_single(int nsteps, F&& at_step) {
     Step buf;
