@@ -215,3 +215,28 @@ def test_chunk_past_the_grid_gives_nan_rows():
         got = out.float().cpu().numpy()
         assert np.isnan(got[:300]).all(), "the 300-row chunk (grid: 2 tiles of 128 query vectors)"
         assert np.isfinite(got[300:]).all()
+
+
+def _scale_values(w, seq, pos_lo, pos_hi, factor):
+    """Multiply the values of sequence ``seq`` at positions [pos_lo, pos_hi)
+    by ``factor`` (rounded back to bf16) in the workload's K/V rows."""
+    m = (w.cached_seq == seq) & (w.cached_pos >= pos_lo) & (w.cached_pos < pos_hi)
+    w.cached_v[m] = workloads.to_bf16_bits(workloads.bf16_bits_to_f32(w.cached_v[m]) * factor)
+    if pos_lo <= w.new_pos[seq] < pos_hi:
+        w.new_v[seq] = workloads.to_bf16_bits(workloads.bf16_bits_to_f32(w.new_v[seq]) * factor)
+
+
+@pytest.mark.parametrize("D", [128, 64])
+def test_prefill_values_of_extreme_magnitude(D):
+    """Values far from N(0,1)'s scale: a 64-key step of values near 4e6,
+    three such tokens inside an otherwise ordinary step, a whole sequence of
+    values near 1e-7, one near 1e-3 (outside fp16's normal range at both
+    ends, inside bf16's); every row against the oracle."""
+    pw = workloads.prefill(985 + D, [0, 200, 70, 0], [300, 90, 130, 64], num_q_heads=8,
+                           num_kv_heads=2, head_size=D)
+    w = pw.cache
+    _scale_values(w, 0, 64, 128, 1e6)
+    _scale_values(w, 0, 200, 203, 3e5)
+    _scale_values(w, 1, 0, 290, 1e-7)
+    _scale_values(w, 2, 0, 200, 5e-4)
+    check_rows(pw, run(pw))
