@@ -14,12 +14,15 @@
 // Every item leaves a partial result (normalised rows and (m, l)) in the
 // workspace; the log-sum-exp merge then combines each sequence's parts.
 //
-// Work items are numbered group by group (prefix items first, then suffix
-// items sequence by sequence); a persistent grid of resident workgroups walks
-// them, HG waves (adjacent kv heads, reading each token as HG*D*2 contiguous
-// bytes) per item, round by round, every other round in reverse.  The column blocks of one prefix partition are numbered
-// next to each other and placed on the same XCD, so the second reads the
-// shared rows from that XCD's L2.
+// Work items are numbered group by group for the prefix items, then sequence
+// by sequence for the suffix items, longest suffix first; a persistent grid
+// of resident workgroups walks them, HG waves (adjacent kv heads, reading
+// each token as HG*D*2 contiguous bytes) per item, round by round, every
+// other round in reverse, so the slots that drew the longest suffix items
+// draw the shortest next.  Each wave keeps one 32-token step in flight.  The
+// column blocks of one prefix partition are numbered next to each other and
+// placed on the same XCD, so the second reads the shared rows from that
+// XCD's L2.
 #include "attention_bf16_wave.hpp"
 
 #include <algorithm>
