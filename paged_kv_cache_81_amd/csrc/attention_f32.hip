@@ -35,29 +35,32 @@ __global__ void __launch_bounds__(64) attention_f32_kernel(AttnArgs a) {
   const int s = blockIdx.z;
   const int B = a.B;
 
-  const int L = a.lens[s];
   const int P = a.partition;
+  const int t_begin = part * P;
+  const int nh = min(NH, G - chunk * kMaxHeads);
+  const int h0 = kvh * G + chunk * kMaxHeads;
+  const int32_t* trow = a.tables + static_cast<int64_t>(s) * a.width;
+  // The length, the table entry of the lane's first token and the query rows
+  // in one round of loads, so the key loads wait for one round trip, not
+  // two: the entry is read before the length is known (any entry below the
+  // table's width is the table's memory) and dropped if past it.
+  const int L = a.lens[s];
+  const int tb = (t_begin + lane) / B;
+  const int phys_spec = lane < P && tb < a.width ? trow[tb] : 0;
+  const float* q = static_cast<const float*>(a.query);
+  for (int i = lane; i < NH * D; i += 64)
+    s_q[i / D][i % D] = i < nh * D ? q[(static_cast<int64_t>(s) * a.Hq + h0) * D + i] : 0.f;
+
   const int nparts = L > 0 ? (L + P - 1) / P : 1;
   const bool bad_seq = L < 0 || (L + B - 1) / B > a.width || nparts > a.max_parts;
   if (part > 0 && (bad_seq || part >= nparts)) return;
-
-  const int nh = min(NH, G - chunk * kMaxHeads);
-  const int h0 = kvh * G + chunk * kMaxHeads;
-  const int t_begin = part * P;
   const int t_end = bad_seq ? t_begin : min(L, t_begin + P);
   const int n = max(0, t_end - t_begin);
   const int64_t row = static_cast<int64_t>(a.Hkv) * D;
   const float* kbase = static_cast<const float*>(a.kv) + static_cast<int64_t>(kvh) * D;
   const float* vbase = kbase + static_cast<int64_t>(a.NB) * B * row;
-  const int32_t* trow = a.tables + static_cast<int64_t>(s) * a.width;
   bool bad = bad_seq;
-
-  // the table entry of the lane's first token is loaded together with the
-  // query rows, so the key loads wait for one round trip, not two
-  const int phys_first = lane < n ? trow[(t_begin + lane) / B] : 0;
-  const float* q = static_cast<const float*>(a.query);
-  for (int i = lane; i < NH * D; i += 64)
-    s_q[i / D][i % D] = i < nh * D ? q[(static_cast<int64_t>(s) * a.Hq + h0) * D + i] : 0.f;
+  const int phys_first = lane < n ? phys_spec : 0;
   __syncthreads();
 
   // phase 1: scores
