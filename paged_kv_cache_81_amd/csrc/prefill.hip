@@ -410,21 +410,19 @@ prefill_bf16_kernel(PrefillArgs a) {
   // (k = 16) takes registers 8m .. 8m + 7, i.e. keys 16m + 4 h2 + 0..3 and
   // 16m + 8 + 4 h2 + 0..3, and the V^T operand reads the same keys.
   auto substep = [&](const char* buf, int kb, int hs) {
-    // at head size 128 two independent accumulation chains (even and odd k
-    // blocks), so the matrix core need not wait for each product before the
-    // next (at 64 the second chain's registers would cost occupancy)
-    f32x16 sc0 = {}, sc1 = {};
+    // one accumulation chain: the matrix core takes each product's result as
+    // the next one's accumulator without waiting (two chains, even and odd k
+    // blocks, added afterwards: 415-416 against 413-414 us on the OPT-13B
+    // shape, 16 more adds per 32 keys)
+    f32x16 sc = {};
     {
       const char* kb0 = buf + 32 * hs * Gm::KROW;
 #pragma unroll
       for (int c = 0; c < QK; ++c) {
         const bf16x8 kf = __builtin_bit_cast(bf16x8, *reinterpret_cast<const wave::u32x4*>(kb0 + kofs[c]));
-        if ((c & 1) && D == 128) sc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[c], sc1, 0, 0, 0);
-        else sc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[c], sc0, 0, 0, 0);
+        sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[c], sc, 0, 0, 0);
       }
     }
-    f32x16 sc = sc0;
-    if constexpr (D == 128) sc += sc1;
     const float sl2 = a.scale_log2;
     float xs[16];
 #pragma unroll
