@@ -679,6 +679,12 @@ def decode_bench(name, args, dev, headline: bool) -> dict:
         ws_bytes = pkv.shared_workspace_bytes(S, Hq, Hkv, D, B, n_groups, w.max_context_len,
                                               g_maxp, P)
         ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+        # the work list, made once per decode step (every layer reads the
+        # same tables) and read by each layer's launches
+        if not args.no_plan:
+            plan_bytes = pkv.shared_plan_bytes(S, Hq, Hkv, B, n_groups, w.max_context_len, g_maxp,
+                                               P)
+            plan_buf = torch.empty(max(plan_bytes, 256), dtype=torch.uint8, device=dev)
         log(f"[bench] shared-prefix decode: {n_groups} groups, longest prefix {g_maxp}, "
             f"partition {P}")
 
@@ -726,6 +732,23 @@ def decode_bench(name, args, dev, headline: bool) -> dict:
                     w.table_width, st.lens.data_ptr(), d_starts.data_ptr(), d_plens.data_ptr(),
                     n_groups, S, Hq, Hkv, D, B, NB, w.scale, w.max_context_len, g_maxp, P,
                     ws.data_ptr(), ws.numel(), dt, flags, stream_handle)
+            if not args.no_plan:
+                # the plan on the first layer's step: once per nl layer steps
+                pl_a = sh_a[:-1] + (plan_buf.data_ptr(), plan_buf.numel(), stream_handle)
+                mk_a = (plan_buf.data_ptr(), plan_buf.numel(), st.tables.data_ptr(),
+                        w.table_width, st.lens.data_ptr(), d_starts.data_ptr(),
+                        d_plens.data_ptr(), n_groups, S, Hq, Hkv, B, w.max_context_len, g_maxp,
+                        P, stream_handle)
+                plan_step = ({"plan": lambda: check(lib.paged_attention_shared_plan(*mk_a),
+                                                    "plan")} if layer == 0 else {})
+                return {
+                    **plan_step,
+                    **write_step,
+                    "attention": lambda: check(
+                        lib.paged_attention_shared_planned_partitions(*pl_a), "attention"),
+                    "merge": lambda: check(lib.paged_attention_shared_planned_merge(*pl_a),
+                                           "merge"),
+                }
             return {
                 **write_step,
                 "attention": lambda: check(lib.paged_attention_shared_partitions(*sh_a),
@@ -848,8 +871,9 @@ def decode_bench(name, args, dev, headline: bool) -> dict:
         del flush
     else:
         for kname_ in names:
+            # (the plan is only in the first layer's step)
             fns = [(lambda sh, layer=layer, kname_=kname_: calls(sh, layer)[kname_]())
-                   for layer in range(nl)]
+                   for layer in range(nl) if kname_ in eager[layer]]
             xs = _graph_avg_us(dev, fns, reps, replays=1 + args.spread_replays)
             kernel_us[kname_] = xs[0]
             kernel_dist[kname_] = _dist(xs)
@@ -891,7 +915,11 @@ def decode_bench(name, args, dev, headline: bool) -> dict:
                                "per sequence"),
             "kv_write": ("inside the attention launch" if fused_write else
                          "separate launch" + ("es" if args.separate_slot_mapping else "")),
-            **({"groups": n_groups, "max_prefix_len": g_maxp} if grouped else {}),
+            **({"groups": n_groups, "max_prefix_len": g_maxp,
+                "work_list": ("none: each attention launch derives it" if args.no_plan else
+                              f"one plan launch per {nl} layer steps (a decode step of an "
+                              f"{nl}-layer model), read by every layer's launches")}
+               if grouped else {}),
         },
         "roofline": {
             "bound": "hbm",
@@ -967,6 +995,9 @@ def main() -> int:
                     help="CPU oracle seconds per setting for the headline workload (a third "
                          "of it for the others)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-plan", action="store_true",
+                    help="shared-prefix decode: every attention launch derives its work list "
+                         "(no plan launch)")
     ap.add_argument("--no-block-ops", action="store_true",
                     help="skip the copy-on-write and swap copy timings")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -1097,7 +1128,7 @@ def _child(args, extra) -> dict:
     cmd = [sys.executable, "-u", os.path.abspath(__file__), "--steps", str(args.steps),
            "--warmup", str(args.warmup), "--spread-replays", str(args.spread_replays)]
     for flag in ("flush", "no_graph", "separate_write", "separate_slot_mapping",
-                 "no_shared_prefix"):
+                 "no_shared_prefix", "no_plan"):
         if getattr(args, flag):
             cmd.append("--" + flag.replace("_", "-"))
     if args.kv_flags != "auto":

@@ -448,6 +448,94 @@ int paged_attention_shared_merge(void* out, pkv_dtype out_dtype, const void* que
                                  unsigned flags, hipStream_t stream);
 
 /*
+ * Shared-prefix decode with a plan made once per decode step.  Every layer
+ * of a model reads its own cache through the same block tables (itan.pw
+ * walk-through, "ブロック割当のロジック": in the decode phase each layer's
+ * cache tensor is indexed by the one table), so the work list of
+ * paged_attention_decode_shared -- which depends only on the tables,
+ * context lengths and groups -- can be made once and read by every layer's
+ * launches, which then start reading K/V one load after they begin instead
+ * of first deriving the list.  Results are bit-identical to
+ * paged_attention_decode_shared with the same arguments.
+ *
+ * Bytes of the plan for these arguments (0 if they are invalid); host only.
+ */
+size_t paged_attention_shared_plan_bytes(int num_seqs, int num_q_heads, int num_kv_heads,
+                                         int block_size, int num_groups, int max_context_len,
+                                         int max_prefix_len, int partition_size);
+
+/*
+ * paged_attention_shared_plan -- make the plan: one launch on `stream`.
+ *
+ *   plan          device buffer of paged_attention_shared_plan_bytes() bytes,
+ *                 256-byte aligned, owned by the caller; overwritten
+ *   block_tables, table_width, context_lens, group_starts, prefix_lens,
+ *   num_groups, num_seqs, num_q_heads, num_kv_heads, block_size,
+ *   max_context_len, max_prefix_len, partition_size
+ *                 as for paged_attention_decode_shared (device arrays)
+ *
+ * The plan holds the arguments it was made for, each sequence's part count,
+ * group leader, prefix length and prefix-table check, and each work item's
+ * description and first block-table window.  It describes the tables,
+ * lengths and groups as they are when its launch runs: after any of them
+ * changes, make a new plan.  Errors as paged_attention_decode_shared
+ * (PKV_ERR_WORKSPACE for a plan buffer that is too small).
+ */
+int paged_attention_shared_plan(void* plan, size_t plan_bytes, const int32_t* block_tables,
+                                int table_width, const int32_t* context_lens,
+                                const int32_t* group_starts, const int32_t* prefix_lens,
+                                int num_groups, int num_seqs, int num_q_heads, int num_kv_heads,
+                                int block_size, int max_context_len, int max_prefix_len,
+                                int partition_size, hipStream_t stream);
+
+/*
+ * paged_attention_decode_shared_planned -- paged_attention_decode_shared
+ * (same arguments, same two launches, same output) reading its work list from
+ * `plan` (made by paged_attention_shared_plan, read only) instead of
+ * deriving it.  The kernels check that the plan was made for this call's
+ * num_seqs, num_q_heads, num_kv_heads, block_size, table_width,
+ * max_context_len, max_prefix_len, num_groups and (resolved) partition size,
+ * and that it recorded every item; if not, every output row is NaN.  The
+ * plan may be read by any number of calls (e.g. one per layer) until the
+ * tables, lengths or groups change.  plan_bytes: its size, at least
+ * paged_attention_shared_plan_bytes() for these arguments.
+ */
+int paged_attention_decode_shared_planned(void* out, pkv_dtype out_dtype, const void* query,
+                                          const void* kv_cache, const int32_t* block_tables,
+                                          int table_width, const int32_t* context_lens,
+                                          const int32_t* group_starts,
+                                          const int32_t* prefix_lens, int num_groups,
+                                          int num_seqs, int num_q_heads, int num_kv_heads,
+                                          int head_size, int block_size, int num_blocks,
+                                          float scale, int max_context_len, int max_prefix_len,
+                                          int partition_size, void* workspace,
+                                          size_t workspace_bytes, pkv_dtype dtype, unsigned flags,
+                                          const void* plan, size_t plan_bytes,
+                                          hipStream_t stream);
+
+/*
+ * Its two launches separately (attention pass, merge), as
+ * paged_attention_shared_partitions and paged_attention_shared_merge.
+ */
+int paged_attention_shared_planned_partitions(
+    void* out, pkv_dtype out_dtype, const void* query, const void* kv_cache,
+    const int32_t* block_tables, int table_width, const int32_t* context_lens,
+    const int32_t* group_starts, const int32_t* prefix_lens, int num_groups, int num_seqs,
+    int num_q_heads, int num_kv_heads, int head_size, int block_size, int num_blocks, float scale,
+    int max_context_len, int max_prefix_len, int partition_size, void* workspace,
+    size_t workspace_bytes, pkv_dtype dtype, unsigned flags, const void* plan, size_t plan_bytes,
+    hipStream_t stream);
+
+int paged_attention_shared_planned_merge(
+    void* out, pkv_dtype out_dtype, const void* query, const void* kv_cache,
+    const int32_t* block_tables, int table_width, const int32_t* context_lens,
+    const int32_t* group_starts, const int32_t* prefix_lens, int num_groups, int num_seqs,
+    int num_q_heads, int num_kv_heads, int head_size, int block_size, int num_blocks, float scale,
+    int max_context_len, int max_prefix_len, int partition_size, void* workspace,
+    size_t workspace_bytes, pkv_dtype dtype, unsigned flags, const void* plan, size_t plan_bytes,
+    hipStream_t stream);
+
+/*
  * paged_attention_prefill -- causal attention of chunks of query tokens over
  * their paged sequences: the prompt step (prefill) and chunked prefill.
  *

@@ -395,6 +395,44 @@ def shared_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_size, block
         max_prefix_len, requested))
 
 
+def shared_plan_bytes(num_seqs, num_q_heads, num_kv_heads, block_size, num_groups,
+                      max_context_len, max_prefix_len, requested: int = 0) -> int:
+    return int(lib.paged_attention_shared_plan_bytes(
+        num_seqs, num_q_heads, num_kv_heads, block_size, num_groups, max_context_len,
+        max_prefix_len, requested))
+
+
+def make_shared_plan(block_tables: torch.Tensor, context_lens: torch.Tensor,
+                     group_starts: torch.Tensor, prefix_lens: torch.Tensor, num_q_heads: int,
+                     num_kv_heads: int, block_size: int, max_context_len: int,
+                     max_prefix_len: int, partition_size: int = 0,
+                     plan: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """The work list of the shared-prefix decode for these tables, lengths and
+    groups (``paged_attention_shared_plan``), to pass as ``plan`` to every
+    :func:`attention_decode_shared` call over them (e.g. each layer of a
+    decode step).  Returns ``plan``, a uint8 device tensor."""
+    dev = block_tables.device
+    _need(block_tables, "block_tables", torch.int32, 2, dev)
+    _need(context_lens, "context_lens", torch.int32, 1, dev)
+    _need(group_starts, "group_starts", torch.int32, 1, dev)
+    _need(prefix_lens, "prefix_lens", torch.int32, 1, dev)
+    S, ng = block_tables.shape[0], prefix_lens.shape[0]
+    if context_lens.shape[0] != S or group_starts.shape[0] != ng + 1:
+        raise ValueError("block_tables, context_lens and the groups disagree in size")
+    need = shared_plan_bytes(S, num_q_heads, num_kv_heads, block_size, ng, max_context_len,
+                             max_prefix_len, partition_size)
+    if plan is None:
+        plan = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _need(plan, "plan", torch.uint8, 1, dev)
+    rc = lib.paged_attention_shared_plan(
+        plan.data_ptr(), plan.numel(), block_tables.data_ptr(), block_tables.shape[1],
+        context_lens.data_ptr(), group_starts.data_ptr(), prefix_lens.data_ptr(), ng, S,
+        num_q_heads, num_kv_heads, block_size, int(max_context_len), int(max_prefix_len),
+        int(partition_size), _stream(block_tables))
+    check(rc, "paged_attention_shared_plan")
+    return plan
+
+
 def attention_decode_shared(query: torch.Tensor, kv_cache: torch.Tensor, block_tables: torch.Tensor,
                             context_lens: torch.Tensor, group_starts: torch.Tensor,
                             prefix_lens: torch.Tensor, scale: float, max_context_len: int,
@@ -402,11 +440,15 @@ def attention_decode_shared(query: torch.Tensor, kv_cache: torch.Tensor, block_t
                             out: Optional[torch.Tensor] = None,
                             out_dtype: torch.dtype = torch.float32,
                             workspace: Optional[torch.Tensor] = None,
-                            cached_kv: bool = False) -> torch.Tensor:
+                            cached_kv: bool = False,
+                            plan: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Paged decode attention for groups of sequences sharing their first
     blocks (``paged_attention_decode_shared``): each group's prefix is read
     once for all its members.  ``group_starts`` [G + 1] and ``prefix_lens``
-    [G] are int32 device tensors (see :func:`prefix_groups`).  Returns ``out``."""
+    [G] are int32 device tensors (see :func:`prefix_groups`).  With ``plan``
+    (from :func:`make_shared_plan` over the same tables, lengths and groups)
+    the work list is read from it (``paged_attention_decode_shared_planned``).
+    Returns ``out``."""
     nb, b, hkv, d = _cache_dims(kv_cache)
     dev = kv_cache.device
     _need(query, "query", kv_cache.dtype, 3, dev)
@@ -432,13 +474,20 @@ def attention_decode_shared(query: torch.Tensor, kv_cache: torch.Tensor, block_t
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     _need(workspace, "workspace", torch.uint8, 1, dev)
-    rc = lib.paged_attention_decode_shared(
-        out.data_ptr(), _dt(out), query.data_ptr(), kv_cache.data_ptr(), block_tables.data_ptr(),
-        block_tables.shape[1], context_lens.data_ptr(), group_starts.data_ptr(),
-        prefix_lens.data_ptr(), ng, S, hq, hkv, d, b, nb, float(scale), int(max_context_len),
-        int(max_prefix_len), int(partition_size), workspace.data_ptr(), workspace.numel(),
-        _dt(kv_cache), PKV_ATTN_CACHED_KV if cached_kv else 0, _stream(kv_cache))
-    check(rc, "paged_attention_decode_shared")
+    args = (out.data_ptr(), _dt(out), query.data_ptr(), kv_cache.data_ptr(),
+            block_tables.data_ptr(), block_tables.shape[1], context_lens.data_ptr(),
+            group_starts.data_ptr(), prefix_lens.data_ptr(), ng, S, hq, hkv, d, b, nb,
+            float(scale), int(max_context_len), int(max_prefix_len), int(partition_size),
+            workspace.data_ptr(), workspace.numel(), _dt(kv_cache),
+            PKV_ATTN_CACHED_KV if cached_kv else 0)
+    if plan is None:
+        rc = lib.paged_attention_decode_shared(*args, _stream(kv_cache))
+        check(rc, "paged_attention_decode_shared")
+    else:
+        _need(plan, "plan", torch.uint8, 1, dev)
+        rc = lib.paged_attention_decode_shared_planned(*args, plan.data_ptr(), plan.numel(),
+                                                       _stream(kv_cache))
+        check(rc, "paged_attention_decode_shared_planned")
     return out
 
 

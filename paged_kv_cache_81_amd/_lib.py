@@ -26,6 +26,8 @@ _i, _sz, _p, _f, _u = ctypes.c_int, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_f
 _i64 = ctypes.c_int64
 _SHARED = (_i, [_p, _i, _p, _p, _p, _i, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _f, _i, _i, _i, _p,
                 _sz, _i, _u, _p])
+# the same with the plan (pointer, bytes) before the stream
+_PLANNED = (_i, _SHARED[1][:-1] + [_p, _sz, _p])
 SIGNATURES = {
     "pkv_last_error": (ctypes.c_char_p, []),
     "pkv_read_ceiling": (_i, [_p, _sz, _i, _i, _p, _p]),
@@ -55,6 +57,12 @@ SIGNATURES = {
     "paged_attention_decode_shared": _SHARED,
     "paged_attention_shared_partitions": _SHARED,
     "paged_attention_shared_merge": _SHARED,
+    "paged_attention_shared_plan_bytes": (_sz, [_i, _i, _i, _i, _i, _i, _i, _i]),
+    "paged_attention_shared_plan": (_i, [_p, _sz, _p, _i, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i,
+                                         _i, _p]),
+    "paged_attention_decode_shared_planned": _PLANNED,
+    "paged_attention_shared_planned_partitions": _PLANNED,
+    "paged_attention_shared_planned_merge": _PLANNED,
     "paged_attention_prefill": (_i, [_p, _i, _p, _p, _i, _i, _p, _p, _i, _p, _i, _i, _i, _i, _i,
                                      _i, _f, _i, _p]),
     "paged_kv_copy_blocks": (_i, [_p, _i, _p, _i, _p, _p, _i, _i, _i, _i, _i, _p]),

@@ -885,6 +885,22 @@ SharedLayout shared_layout(int S, int Hq, int D, int max_len, int max_prefix, in
   return l;
 }
 
+// Work items at most: prefix items are at most (kv-head groups) x (column
+// blocks, at most S*G/16 + groups) x parts, suffix items (kv-head groups) x
+// (head chunks) x parts per sequence.
+int64_t shared_item_bound(int S, int Hq, int Hkv, int num_groups, int max_len, int max_prefix,
+                          int P) {
+  const int G = Hq / Hkv;
+  const int64_t hgn = Hkv / bf16_heads_per_group(Hkv);
+  return hgn * (cdiv64(static_cast<int64_t>(S) * G, 16) + num_groups) * cdiv64(max_prefix, P) +
+         static_cast<int64_t>(S) * hgn * cdiv64(G, 16) * cdiv64(std::max(max_len, 1), P);
+}
+
+// Bytes of a plan: header, per-sequence records, one record per item.
+int64_t shared_plan_bytes(int S, int64_t items) {
+  return (plan_items_off(S) + items * kPlanItemInts) * static_cast<int64_t>(sizeof(int32_t));
+}
+
 }  // namespace
 }  // namespace pkv
 
@@ -977,6 +993,99 @@ size_t paged_attention_shared_workspace_bytes(int num_seqs, int num_q_heads, int
       shared_layout(num_seqs, num_q_heads, head_size, max_context_len, max_prefix_len, P).bytes);
 }
 
+size_t paged_attention_shared_plan_bytes(int num_seqs, int num_q_heads, int num_kv_heads,
+                                         int block_size, int num_groups, int max_context_len,
+                                         int max_prefix_len, int partition_size) {
+  clear_error();
+  if (!shape_ok(num_seqs, num_q_heads, num_kv_heads, 0, block_size, max_context_len, PKV_BF16) ||
+      max_prefix_len < 0 || num_seqs == 0 || num_groups < 1 || num_groups > num_seqs)
+    return 0;
+  const int P = resolve_shared_partition(num_seqs, num_q_heads, num_kv_heads, block_size,
+                                         num_groups, max_prefix_len, partition_size);
+  if (P <= 0) return 0;
+  return static_cast<size_t>(shared_plan_bytes(
+      num_seqs, shared_item_bound(num_seqs, num_q_heads, num_kv_heads, num_groups, max_context_len,
+                                  max_prefix_len, P)));
+}
+
+int paged_attention_shared_plan(void* plan, size_t plan_bytes, const int32_t* block_tables,
+                                int table_width, const int32_t* context_lens,
+                                const int32_t* group_starts, const int32_t* prefix_lens,
+                                int num_groups, int num_seqs, int num_q_heads, int num_kv_heads,
+                                int block_size, int max_context_len, int max_prefix_len,
+                                int partition_size, hipStream_t stream) {
+  clear_error();
+  if (!shape_ok(num_seqs, num_q_heads, num_kv_heads, 0, block_size, max_context_len, PKV_BF16))
+    return PKV_ERR_INVALID;
+  if (block_size != 8 && block_size != 16 && block_size != 32 && block_size != 64) {
+    set_error("block_size %d is not built (8, 16, 32 or 64)", block_size);
+    return PKV_ERR_UNSUPPORTED;
+  }
+  if (num_seqs > kMaxCompactSeqs) {
+    set_error("shared-prefix plan: num_seqs %d above %d", num_seqs, kMaxCompactSeqs);
+    return PKV_ERR_UNSUPPORTED;
+  }
+  if (table_width <= 0) { set_error("table_width must be positive"); return PKV_ERR_INVALID; }
+  if (max_prefix_len < 0) { set_error("max_prefix_len %d < 0", max_prefix_len); return PKV_ERR_INVALID; }
+  if (num_seqs == 0) return PKV_OK;
+  if (num_groups < 1 || num_groups > num_seqs) {
+    set_error("num_groups %d outside [1, num_seqs = %d]", num_groups, num_seqs);
+    return PKV_ERR_INVALID;
+  }
+  if (!plan || !block_tables || !context_lens || !group_starts || !prefix_lens) {
+    set_error("null pointer argument");
+    return PKV_ERR_INVALID;
+  }
+  if (reinterpret_cast<uintptr_t>(plan) & 255u) {
+    set_error("plan must be 256-byte aligned");
+    return PKV_ERR_INVALID;
+  }
+  const int P = resolve_shared_partition(num_seqs, num_q_heads, num_kv_heads, block_size,
+                                         num_groups, max_prefix_len, partition_size);
+  if (P <= 0) {
+    set_error("partition_size %d is not a positive multiple of %d", partition_size,
+              partition_unit(block_size));
+    return PKV_ERR_INVALID;
+  }
+  const int64_t items = shared_item_bound(num_seqs, num_q_heads, num_kv_heads, num_groups,
+                                          max_context_len, max_prefix_len, P);
+  if (items >= (int64_t{1} << 31)) {
+    set_error("shared-prefix plan: too many work items");
+    return PKV_ERR_UNSUPPORTED;
+  }
+  const int64_t need = shared_plan_bytes(num_seqs, items);
+  if (plan_bytes < static_cast<size_t>(need)) {
+    set_error("plan of %zu bytes is smaller than the %lld needed", plan_bytes,
+              static_cast<long long>(need));
+    return PKV_ERR_WORKSPACE;
+  }
+  const int resident = shared_resident_wgs();
+  if (resident <= 0) {
+    set_error("cannot query the current device");
+    return PKV_ERR_HIP;
+  }
+  // about two items a wave
+  const int64_t wgs = std::max<int64_t>(1, std::min<int64_t>(resident, cdiv64(items, 8)));
+  AttnArgs a{};
+  a.tables = block_tables;
+  a.lens = context_lens;
+  a.width = table_width;
+  a.S = num_seqs;
+  a.Hq = num_q_heads;
+  a.Hkv = num_kv_heads;
+  a.B = block_size;
+  a.partition = P;
+  a.max_len = max_context_len;
+  a.group_starts = group_starts;
+  a.prefix_lens = prefix_lens;
+  a.num_groups = num_groups;
+  a.max_prefix = max_prefix_len;
+  a.stream_waves = static_cast<int>(wgs) * 4;
+  int32_t* pl = static_cast<int32_t*>(plan);
+  a.ws_seq = pl + kPlanHeaderInts;
+  return launch_shared_plan(a, pl, items, stream);
+}
+
 }  // extern "C"
 
 namespace {
@@ -988,7 +1097,7 @@ int decode_shared_impl(int phases, void* out, pkv_dtype out_dtype, const void* q
                        int num_kv_heads, int head_size, int block_size, int num_blocks,
                        float scale, int max_context_len, int max_prefix_len, int partition_size,
                        void* workspace, size_t workspace_bytes, pkv_dtype dtype, unsigned flags,
-                       hipStream_t stream) {
+                       bool planned, const void* plan, size_t plan_bytes, hipStream_t stream) {
   clear_error();
   if (!shape_ok(num_seqs, num_q_heads, num_kv_heads, head_size, block_size, max_context_len, dtype))
     return PKV_ERR_INVALID;
@@ -1048,19 +1157,26 @@ int decode_shared_impl(int phases, void* out, pkv_dtype out_dtype, const void* q
     set_error("workspace must be 256-byte aligned");
     return PKV_ERR_INVALID;
   }
-  // work items (counted in 32-bit integers): prefix items are at most
-  // (kv-head groups) x (column blocks, at most S*G/16 + groups) x parts,
-  // suffix items (kv-head groups) x (head chunks) x parts per sequence
-  const int G = num_q_heads / num_kv_heads;
+  // work items (counted in 32-bit integers)
   const int HG = bf16_heads_per_group(num_kv_heads);
-  const int64_t hgn = num_kv_heads / HG;
-  const int64_t upper =
-      hgn * (cdiv64(static_cast<int64_t>(num_seqs) * G, 16) + num_groups) *
-          cdiv64(max_prefix_len, P) +
-      static_cast<int64_t>(num_seqs) * hgn * cdiv64(G, 16) * cdiv64(std::max(max_context_len, 1), P);
+  const int64_t upper = shared_item_bound(num_seqs, num_q_heads, num_kv_heads, num_groups,
+                                          max_context_len, max_prefix_len, P);
   if (upper >= (int64_t{1} << 31) || lay.parts * num_seqs * num_q_heads >= (int64_t{1} << 31)) {
     set_error("shared-prefix decode: too many work items or workspace rows");
     return PKV_ERR_UNSUPPORTED;
+  }
+  if (planned) {
+    if (!plan) { set_error("null plan"); return PKV_ERR_INVALID; }
+    if (reinterpret_cast<uintptr_t>(plan) & 255u) {
+      set_error("plan must be 256-byte aligned");
+      return PKV_ERR_INVALID;
+    }
+    const int64_t need = shared_plan_bytes(num_seqs, upper);
+    if (plan_bytes < static_cast<size_t>(need)) {
+      set_error("plan of %zu bytes is smaller than the %lld needed", plan_bytes,
+                static_cast<long long>(need));
+      return PKV_ERR_WORKSPACE;
+    }
   }
   const int resident = shared_resident_wgs();
   if (resident <= 0) {
@@ -1102,6 +1218,7 @@ int decode_shared_impl(int phases, void* out, pkv_dtype out_dtype, const void* q
   a.ws_o = reinterpret_cast<float*>(ws);
   a.ws_ml = reinterpret_cast<float*>(ws + lay.ml_off);
   a.ws_seq = reinterpret_cast<int*>(ws + lay.seq_off);
+  if (planned) a.plan = static_cast<const int32_t*>(plan);
   if (phases & kAttend) {
     const int rc = launch_attention_bf16_shared(a, stream);
     if (rc != PKV_OK) return rc;
@@ -1116,7 +1233,7 @@ int decode_shared_impl(int phases, void* out, pkv_dtype out_dtype, const void* q
   out, out_dtype, query, kv_cache, block_tables, table_width, context_lens, group_starts,        \
       prefix_lens, num_groups, num_seqs, num_q_heads, num_kv_heads, head_size, block_size,       \
       num_blocks, scale, max_context_len, max_prefix_len, partition_size, workspace,             \
-      workspace_bytes, dtype, flags, stream
+      workspace_bytes, dtype, flags
 
 #define PKV_SHARED_PARAMS                                                                        \
   void *out, pkv_dtype out_dtype, const void *query, const void *kv_cache,                       \
@@ -1124,20 +1241,35 @@ int decode_shared_impl(int phases, void* out, pkv_dtype out_dtype, const void* q
       const int32_t *group_starts, const int32_t *prefix_lens, int num_groups, int num_seqs,     \
       int num_q_heads, int num_kv_heads, int head_size, int block_size, int num_blocks,          \
       float scale, int max_context_len, int max_prefix_len, int partition_size, void *workspace, \
-      size_t workspace_bytes, pkv_dtype dtype, unsigned flags, hipStream_t stream
+      size_t workspace_bytes, pkv_dtype dtype, unsigned flags
 
 extern "C" {
 
-int paged_attention_decode_shared(PKV_SHARED_PARAMS) {
-  return decode_shared_impl(kAttend | kMerge, PKV_SHARED_ARGS);
+int paged_attention_decode_shared(PKV_SHARED_PARAMS, hipStream_t stream) {
+  return decode_shared_impl(kAttend | kMerge, PKV_SHARED_ARGS, false, nullptr, 0, stream);
 }
 
-int paged_attention_shared_partitions(PKV_SHARED_PARAMS) {
-  return decode_shared_impl(kAttend, PKV_SHARED_ARGS);
+int paged_attention_shared_partitions(PKV_SHARED_PARAMS, hipStream_t stream) {
+  return decode_shared_impl(kAttend, PKV_SHARED_ARGS, false, nullptr, 0, stream);
 }
 
-int paged_attention_shared_merge(PKV_SHARED_PARAMS) {
-  return decode_shared_impl(kMerge, PKV_SHARED_ARGS);
+int paged_attention_shared_merge(PKV_SHARED_PARAMS, hipStream_t stream) {
+  return decode_shared_impl(kMerge, PKV_SHARED_ARGS, false, nullptr, 0, stream);
+}
+
+int paged_attention_decode_shared_planned(PKV_SHARED_PARAMS, const void* plan, size_t plan_bytes,
+                                          hipStream_t stream) {
+  return decode_shared_impl(kAttend | kMerge, PKV_SHARED_ARGS, true, plan, plan_bytes, stream);
+}
+
+int paged_attention_shared_planned_partitions(PKV_SHARED_PARAMS, const void* plan,
+                                              size_t plan_bytes, hipStream_t stream) {
+  return decode_shared_impl(kAttend, PKV_SHARED_ARGS, true, plan, plan_bytes, stream);
+}
+
+int paged_attention_shared_planned_merge(PKV_SHARED_PARAMS, const void* plan, size_t plan_bytes,
+                                         hipStream_t stream) {
+  return decode_shared_impl(kMerge, PKV_SHARED_ARGS, true, plan, plan_bytes, stream);
 }
 
 }  // extern "C"

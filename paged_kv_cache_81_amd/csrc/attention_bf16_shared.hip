@@ -23,6 +23,13 @@
 // column blocks of one prefix partition are numbered next to each other and
 // placed on the same XCD, so the second reads the shared rows from that
 // XCD's L2.
+//
+// The item list depends only on the tables, lengths and groups, which every
+// layer of a decode step shares.  So it can also be made once per step by a
+// plan launch, which writes each item's description and first block-table
+// window to a plan buffer; the attention launches given that plan skip the
+// list's derivation and start each item's K/V loads one load after it is
+// dealt.
 #include "attention_bf16_wave.hpp"
 
 #include <algorithm>
@@ -274,6 +281,131 @@ __device__ void make_plan(const AttnArgs& a, Plan& p, int HGN, int chunks, int G
   __syncthreads();
 }
 
+// One work item, for all HG kv heads of its group (each wave of the item
+// adds its own head to kvg).
+struct Item {
+  int part;   // partition number of the results in its sequences' workspace rows
+  int seq;    // prefix item: the group's first sequence (its table is read); suffix item: the sequence
+  int kvg;    // first kv head of the item's group of HG
+  int col0;   // prefix item: first score column (member col0 / G, head col0 % G); suffix item: -1
+  int nh;     // score columns (query heads) of the item
+  int t0, t1; // tokens read
+  int chunk;  // suffix item: the query heads 16 chunk .. of each kv head
+};
+static_assert(sizeof(Item) == kPlanItemFields * sizeof(int), "plan item record layout");
+
+// Item it of the list the plan p describes (t_pre prefix items first).
+__device__ __forceinline__ Item decode_item(const AttnArgs& a, const Plan& p, int it, int t_pre,
+                                            int HG, int G, int chunks) {
+  const int P = a.partition;
+  Item m;
+  if (it < t_pre) {
+    // prefix item: group g, kv-head group, partition pp, column block cb
+    const int g = last_le(p.pscan, a.num_groups, it);
+    const int s0 = p.gs[g];
+    const int M = p.gs[g + 1] - s0;
+    const int lp = p.glp[g];
+    const int CB = (M * G + 15) / 16;
+    const int NP = (lp + P - 1) / P;
+    const int local = it - p.pscan[g];
+    const int cb = local % CB;
+    const int r = local / CB;
+    const int pp = r % NP;
+    m.part = pp;
+    m.seq = s0;
+    m.kvg = (r / NP) * HG;
+    m.col0 = 16 * cb;
+    m.nh = min(16, M * G - m.col0);
+    m.t0 = pp * P;
+    m.t1 = min(lp, m.t0 + P);
+    m.chunk = 0;
+  } else {
+    // suffix item: sequence s, (kv-head group, query-head chunk) y, partition q
+    const int x = it - t_pre;
+    const int k = last_le(p.sscan, a.S, x);
+    const int s = p.order[k];
+    const int lp = p.lp[s];
+    const int L = p.len[s];
+    const int NQ = (L - lp + P - 1) / P;
+    const int local = x - p.sscan[k];
+    const int q = local % NQ;
+    const int y = local / NQ;
+    m.chunk = y % chunks;
+    m.part = (lp + P - 1) / P + q;
+    m.seq = s;
+    m.kvg = (y / chunks) * HG;
+    m.col0 = -1;
+    m.nh = min(16, G - 16 * m.chunk);
+    m.t0 = lp + q * P;
+    m.t1 = min(L, m.t0 + P);
+  }
+  return m;
+}
+
+// Sequences s = blockIdx.x, + nwg, ... (wave 0 of each workgroup): do s's
+// own table entries for its group's prefix match its leader's (whose table
+// the prefix items read)?  A mismatch makes the merge give NaN for s.
+template <int B>
+__device__ __forceinline__ void check_prefix_tables(const AttnArgs& a, const Plan& p, int nwg,
+                                                    int lane) {
+  for (int s = blockIdx.x; s < a.S; s += nwg) {
+    const int lp = p.lp[s];
+    // s's group (valid groups have non-decreasing starts): its leader
+    const int lead = lp > 0 ? p.gs[last_le(p.gs, a.num_groups, s)] : s;
+    bool diff = false;
+    if (lp > 0 && lead != s) {
+      const int32_t* mine = a.tables + static_cast<int64_t>(s) * a.width;
+      const int32_t* theirs = a.tables + static_cast<int64_t>(lead) * a.width;
+      for (int i = lane; i < (lp + B - 1) / B; i += 64) diff = diff || mine[i] != theirs[i];
+    }
+    const bool any = __ballot(diff) != 0;
+    if (lane == 0) a.ws_seq[3 * a.S + s] = any ? 1 : 0;
+  }
+}
+
+// The plan launch: every workgroup makes the plan (as the attention
+// workgroups do without one), workgroup 0 records the header and the
+// sequences' records for the merge (a.ws_seq points into the plan), each
+// workgroup checks its share of the sequences' prefix tables and records its
+// share of the items, one a wave at a time.  nwg = a.stream_waves / 4.
+template <int B>
+__global__ void __launch_bounds__(kThreads)
+shared_plan_kernel(AttnArgs a, int32_t* plan, int64_t capacity) {
+  __shared__ Plan p;
+  __shared__ int scratch[kPlanScratchInts];
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int G = a.Hq / a.Hkv;
+  const int chunks = (G + 15) >> 4;
+  const int HG = bf16_heads_per_group(a.Hkv);
+  const int nwg = a.stream_waves / kWaves;
+  make_plan<B>(a, p, a.Hkv / HG, chunks, G, scratch);
+  const int t_pre = p.pscan[a.num_groups];
+  const int total = t_pre + p.sscan[a.S];
+  const bool fits = total <= capacity;
+  if (blockIdx.x == 0 && threadIdx.x < kPlFields) {
+    const int f = threadIdx.x;
+    const int v = f == kPlMagic ? kPlanMagic : f == kPlS ? a.S : f == kPlHq ? a.Hq :
+                  f == kPlHkv ? a.Hkv : f == kPlB ? a.B : f == kPlWidth ? a.width :
+                  f == kPlMaxLen ? a.max_len : f == kPlMaxPrefix ? a.max_prefix :
+                  f == kPlGroups ? a.num_groups : f == kPlPartition ? a.partition :
+                  f == kPlStatus ? (fits ? 0 : 1) : f == kPlPrefixItems ? t_pre : total;
+    plan[f] = v;
+  }
+  if (wv == 0) check_prefix_tables<B>(a, p, nwg, lane);
+  if (!fits) return;
+  int32_t* items = plan + plan_items_off(a.S);
+  for (int it = blockIdx.x * kWaves + wv; it < total; it += nwg * kWaves) {
+    const Item m = decode_item(a, p, it, t_pre, HG, G, chunks);
+    int32_t* r = items + static_cast<int64_t>(it) * kPlanItemInts;
+    if (lane < kPlanItemFields)
+      r[lane] = lane == 0 ? m.part : lane == 1 ? m.seq : lane == 2 ? m.kvg : lane == 3 ? m.col0 :
+                lane == 4 ? m.nh : lane == 5 ? m.t0 : lane == 6 ? m.t1 : m.chunk;
+    r[kPlanItemFields + lane] =
+        wave::table_window<B>(a.tables + static_cast<int64_t>(m.seq) * a.width, m.t0, m.t1, 0, lane);
+  }
+}
+
 template <int D, int B, int HG, bool NT, bool KL>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
 attention_bf16_shared_kernel(AttnArgs a) {
@@ -293,32 +425,39 @@ attention_bf16_shared_kernel(AttnArgs a) {
   const int G = a.Hq / a.Hkv;
   const int chunks = (G + 15) >> 4;
   const int HGN = a.Hkv / HG;
-  const int P = a.partition;
   const int ng = a.num_groups;
   // the grid's size from the arguments (read with the others at the start),
   // not from the dispatch's hidden arguments
   const int nwg = a.stream_waves / kWaves;
-  make_plan<B>(a, p, HGN, chunks, G, reinterpret_cast<int*>(s_dyn));
-  const int t_pre = p.pscan[ng];
-  const int total = t_pre + p.sscan[a.S];
-
-  // Sequences s = blockIdx.x, + nwg, ...: do s's own table entries for
-  // its group's prefix match its leader's (whose table the prefix items
-  // read)?  A mismatch makes the merge give NaN for s.
-  if (wv == 0)
-    for (int s = blockIdx.x; s < a.S; s += nwg) {
-      const int lp = p.lp[s];
-      // s's group (valid groups have non-decreasing starts): its leader
-      const int lead = lp > 0 ? p.gs[last_le(p.gs, ng, s)] : s;
-      bool diff = false;
-      if (lp > 0 && lead != s) {
-        const int32_t* mine = a.tables + static_cast<int64_t>(s) * a.width;
-        const int32_t* theirs = a.tables + static_cast<int64_t>(lead) * a.width;
-        for (int i = lane; i < (lp + B - 1) / B; i += 64) diff = diff || mine[i] != theirs[i];
-      }
-      const bool any = __ballot(diff) != 0;
-      if (lane == 0) a.ws_seq[3 * a.S + s] = any ? 1 : 0;
+  // With a plan: its item counts (none if it was made for other arguments:
+  // the merge then gives NaN), and its item records.  Without: make it.
+  const bool planned = a.plan != nullptr;
+  const int32_t* items = planned ? a.plan + plan_items_off(a.S) : nullptr;
+  int t_pre, total;
+  if (planned) {
+    const int n_pre = a.plan[kPlPrefixItems];
+    const int n_all = a.plan[kPlItems];
+    const bool ok = plan_matches(a);
+    t_pre = __builtin_amdgcn_readfirstlane(ok ? n_pre : 0);
+    total = __builtin_amdgcn_readfirstlane(ok ? n_all : 0);
+    // the sequences' records for the merge, from the plan into the
+    // workspace (a record written this late is still in the caches when the
+    // merge reads it); parts -1 (NaN rows) when the plan does not match
+    if (wv == 0) {
+      const int32_t* rec = a.plan + kPlanHeaderInts;
+      for (int s = blockIdx.x * 64 + lane; s < a.S; s += nwg * 64)
+#pragma unroll
+        for (int f = 0; f < 4; ++f) {
+          const int v = rec[f * a.S + s];
+          a.ws_seq[f * a.S + s] = ok ? v : (f == 0 ? -1 : 0);
+        }
     }
+  } else {
+    make_plan<B>(a, p, HGN, chunks, G, reinterpret_cast<int*>(s_dyn));
+    t_pre = p.pscan[ng];
+    total = t_pre + p.sscan[a.S];
+    if (wv == 0) check_prefix_tables<B>(a, p, nwg, lane);
+  }
 
   // Workgroup b runs on XCD b mod 8; with one item per workgroup, pair
   // workgroups b and b + 8 (same XCD) on consecutive items -- the column
@@ -373,68 +512,54 @@ attention_bf16_shared_kernel(AttnArgs a) {
   for (int it0 = b * NSLOT + slot, round = 0; it0 < total + stride; it0 += stride, ++round) {
     const int it = (round & 1) ? (2 * round + 1) * stride - 1 - it0 : it0;
     if (it >= total) continue;
-    int part, seq, kvh, hbase, t0, t1, nh, col0, tab;
-    int64_t qrow;
-    if (it < t_pre) {
-      // prefix item: group g, kv-head group hgi, partition pp, column block cb
-      const int g = last_le(p.pscan, ng, it);
-      const int s0 = p.gs[g];
-      const int M = p.gs[g + 1] - s0;
-      const int lp = p.glp[g];
-      const int CB = (M * G + 15) / 16;
-      const int NP = (lp + P - 1) / P;
-      const int local = it - p.pscan[g];
-      const int cb = local % CB;
-      const int r = local / CB;
-      const int pp = r % NP;
-      kvh = (r / NP) * HG + hi;
-      hbase = kvh * G;
-      col0 = 16 * cb;
-      nh = min(16, M * G - col0);
-      const int c = col0 + (lane & 15);
-      const int mem = c / G;
-      qrow = (lane & 15) < nh ? static_cast<int64_t>(s0 + mem) * a.Hq + kvh * G + (c - mem * G) : -1;
-      tab = s0;
-      seq = s0;
-      part = pp;
-      t0 = pp * P;
-      t1 = min(lp, t0 + P);
+    Item m;
+    int win0 = 0;
+    if (planned) {
+      // the record in two loads issued together: lane l takes field l % 8
+      // of the description and entry l of the table window
+      const int32_t* r = items + static_cast<int64_t>(it) * kPlanItemInts;
+      const int f = r[lane % kPlanItemFields];
+      win0 = r[kPlanItemFields + lane];
+      m.part = __builtin_amdgcn_readlane(f, 0);
+      m.seq = __builtin_amdgcn_readlane(f, 1);
+      m.kvg = __builtin_amdgcn_readlane(f, 2);
+      m.col0 = __builtin_amdgcn_readlane(f, 3);
+      m.nh = __builtin_amdgcn_readlane(f, 4);
+      m.t0 = __builtin_amdgcn_readlane(f, 5);
+      m.t1 = __builtin_amdgcn_readlane(f, 6);
+      m.chunk = __builtin_amdgcn_readlane(f, 7);
     } else {
-      // suffix item: sequence s, (kv-head group, query-head chunk) y, partition q
-      const int x = it - t_pre;
-      const int k = last_le(p.sscan, a.S, x);
-      const int s = p.order[k];
-      const int lp = p.lp[s];
-      const int L = p.len[s];
-      const int NQ = (L - lp + P - 1) / P;
-      const int local = x - p.sscan[k];
-      const int q = local % NQ;
-      const int y = local / NQ;
-      const int chunk = y % chunks;
-      kvh = (y / chunks) * HG + hi;
-      col0 = -1;
-      nh = min(16, G - 16 * chunk);
-      hbase = kvh * G + 16 * chunk;
-      qrow = (lane & 15) < nh ? static_cast<int64_t>(s) * a.Hq + hbase + (lane & 15) : -1;
-      tab = s;
-      seq = s;
-      part = (lp + P - 1) / P + q;
-      t0 = lp + q * P;
-      t1 = min(L, t0 + P);
+      m = decode_item(a, p, it, t_pre, HG, G, chunks);
+    }
+    // this wave's kv head, its first query head, and the query row of score
+    // column lane % 16 (-1: none)
+    const int kvh = m.kvg + hi;
+    const int jc = lane & 15;
+    int hbase;
+    int64_t qrow = -1;
+    if (m.col0 >= 0) {
+      hbase = kvh * G;
+      const int c = m.col0 + jc;
+      const int mem = c / G;
+      if (jc < m.nh) qrow = static_cast<int64_t>(m.seq + mem) * a.Hq + hbase + (c - mem * G);
+    } else {
+      hbase = kvh * G + 16 * m.chunk;
+      if (jc < m.nh) qrow = static_cast<int64_t>(m.seq) * a.Hq + hbase + jc;
     }
 
     if (used == K) flush();
     const int i = used++;
-    w.begin_rows(a, qrow, tab, kvh, t0, t1);
-    w.run_single((t1 - t0 + kStep - 1) / kStep, [](int) {});
-    w.finish(rows + i * 16 * SROW, mls + 2 * i * 16, nh);
+    if (planned) w.begin_rows(a, qrow, m.seq, kvh, m.t0, m.t1, win0);
+    else w.begin_rows(a, qrow, m.seq, kvh, m.t0, m.t1);
+    w.run_single((m.t1 - m.t0 + kStep - 1) / kStep, [](int) {});
+    w.finish(rows + i * 16 * SROW, mls + 2 * i * 16, m.nh);
     if (lane == 0) {
-      int* m = meta + kSharedMeta * i;
-      m[0] = part;
-      m[1] = seq;
-      m[2] = hbase;
-      m[3] = col0;
-      m[4] = nh;
+      int* md = meta + kSharedMeta * i;
+      md[0] = m.part;
+      md[1] = m.seq;
+      md[2] = hbase;
+      md[3] = m.col0;
+      md[4] = m.nh;
     }
   }
   flush();
@@ -467,6 +592,21 @@ int launch(const AttnArgs& a, hipStream_t stream) {
 }
 
 }  // namespace
+
+int launch_shared_plan(const AttnArgs& a, int32_t* plan, int64_t capacity, hipStream_t stream) {
+  if (a.S == 0) return PKV_OK;
+  const dim3 grid(a.stream_waves / kWaves), block(kThreads);
+  switch (a.B) {
+    case 8: shared_plan_kernel<8><<<grid, block, 0, stream>>>(a, plan, capacity); break;
+    case 16: shared_plan_kernel<16><<<grid, block, 0, stream>>>(a, plan, capacity); break;
+    case 32: shared_plan_kernel<32><<<grid, block, 0, stream>>>(a, plan, capacity); break;
+    case 64: shared_plan_kernel<64><<<grid, block, 0, stream>>>(a, plan, capacity); break;
+    default:
+      set_error("shared-prefix plan: block_size %d is not built", a.B);
+      return PKV_ERR_UNSUPPORTED;
+  }
+  return check_launch("shared-prefix plan");
+}
 
 int launch_attention_bf16_shared(const AttnArgs& a, hipStream_t stream) {
   if (a.S == 0) return PKV_OK;

@@ -74,6 +74,22 @@ __device__ __forceinline__ bf16x8 load_bf16x8(const void* p) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Block-table entries per 32-token step: one per 16-token tile, or one per
+// block when blocks are smaller than a tile (B = 8: a tile spans two).
+template <int B>
+__host__ __device__ constexpr int window_entries_per_step() { return B < 16 ? kStep / B : 2; }
+
+// Block-table window of the token run [t0, t1) read through table row trow:
+// lane l holds the physical block of piece l % EPS (a 16-token tile, or a
+// block of 8 tokens) of step q0 + l / EPS, -1 past the run, so 64 / EPS
+// steps take one load.
+template <int B>
+__device__ __forceinline__ int table_window(const int32_t* trow, int t0, int t1, int q0, int lane) {
+  constexpr int EPS = window_entries_per_step<B>();
+  const int tt = t0 + (q0 + lane / EPS) * kStep + (kStep / EPS) * (lane % EPS);
+  return tt < t1 ? trow[tt / B] : -1;
+}
+
 // Floats of LDS one wave's K tile takes (32 tokens x D bf16).
 __host__ __device__ constexpr int k_tile_floats(int D) { return 16 * D; }
 
@@ -84,9 +100,7 @@ struct Wave {
   static constexpr int NW = NV / 2;  // 32-bit words per lane per V token
   static constexpr int NCH = D / 8;  // 16-byte chunks per K row
   static constexpr int SROW = D + 4;  // LDS floats per finished head row (padded)
-  // block-table entries per 32-token step: one per 16-token tile, or one
-  // per block when blocks are smaller than a tile (B = 8: a tile spans two)
-  static constexpr int EPS = B < 16 ? 32 / B : 2;
+  static constexpr int EPS = window_entries_per_step<B>();
   static constexpr int WIN = 64 / EPS;  // steps one table window covers
   static_assert(B >= 8 && 64 % EPS == 0, "unsupported block size");
 
@@ -149,12 +163,10 @@ struct Wave {
     bad_blk = false;
   }
 
-  // Block-table window: lane l holds the physical block of piece l % EPS
-  // (a 16-token tile, or a block of 8 tokens) of step q0 + l / EPS, so WIN
-  // steps need one load; per step the entries are read back as scalars.
+  // Block-table window of steps q0 .. q0 + WIN - 1 of the run (see
+  // table_window); per step the entries are read back as scalars.
   __device__ __forceinline__ int load_window(int q0) const {
-    const int tt = t_begin + (q0 + lane / EPS) * kStep + (kStep / EPS) * (lane % EPS);
-    return tt < t_end ? trow[tt / B] : -1;
+    return table_window<B>(trow, t_begin, t_end, q0, lane);
   }
 
   // Start reading tokens [t0, t1) of sequence s for kv head kvh and query
@@ -170,6 +182,24 @@ struct Wave {
   // lane's j, and the tokens are read through table row s.
   __device__ __forceinline__ void begin_rows(const AttnArgs& a, int64_t qrow, int s, int kvh, int t0,
                                              int t1) {
+    start_rows(a, qrow, s, kvh, t0, t1);
+    win = load_window(0);
+    asm volatile("" ::"v"(win));
+    win_next = load_window(WIN);
+  }
+
+  // The same with the run's first table window given (win0: this lane's
+  // entry of it, as load_window(0) would return), e.g. from a plan.
+  __device__ __forceinline__ void begin_rows(const AttnArgs& a, int64_t qrow, int s, int kvh, int t0,
+                                             int t1, int win0) {
+    start_rows(a, qrow, s, kvh, t0, t1);
+    win = win0;
+    win_next = load_window(WIN);
+  }
+
+  // query fragments and the run's addresses
+  __device__ __forceinline__ void start_rows(const AttnArgs& a, int64_t qrow, int s, int kvh, int t0,
+                                             int t1) {
     const uint16_t* qp = static_cast<const uint16_t*>(a.query) + (qrow < 0 ? 0 : qrow) * D + 8 * g;
 #pragma unroll
     for (int c = 0; c < QC; ++c) qf[c] = (qrow >= 0) ? load_bf16x8<false>(qp + 32 * c) : bf16x8{};
@@ -180,9 +210,6 @@ struct Wave {
     t_begin = t0;
     t_end = t1;
     win_q0 = 0;
-    win = load_window(0);
-    asm volatile("" ::"v"(win));
-    win_next = load_window(WIN);
   }
 
   // Issue the loads of step q (tokens t_begin + 32q ..), steps in order.

@@ -111,6 +111,9 @@ struct AttnArgs {
   // written to the cache and folded in from these rows (nullptr: none)
   const void* k_new;
   const void* v_new;
+  // shared-prefix schedule with a plan made beforehand (nullptr: every
+  // workgroup of the attention launch makes its own)
+  const int32_t* plan;
 };
 
 // Stream schedule: wave w of W reads stream steps [start(w), start(w + 1))
@@ -201,6 +204,36 @@ inline void shared_lds_plan(int D, bool k_tile, int* slots, int* wave_floats) {
   *wave_floats = (tile + k * shared_slot_floats(D) + 3) / 4 * 4;
 }
 
+// Shared-prefix plan, made once for a batch's tables, lengths and groups and
+// read by every attention and merge launch over them (every layer of a
+// decode step): a header of kPlanHeaderInts ints, the per-sequence records
+// the merge reads ([4][S], as ws_seq, padded to 64 ints), then one record of
+// kPlanItemInts ints per work item -- its description (part, sequence, first
+// kv head, first score column or -1, columns, first and end token, query-head
+// chunk) and the first block-table window its waves read.
+enum PlanField {
+  kPlMagic, kPlS, kPlHq, kPlHkv, kPlB, kPlWidth, kPlMaxLen, kPlMaxPrefix, kPlGroups,
+  kPlPartition, kPlStatus, kPlPrefixItems, kPlItems, kPlFields
+};
+constexpr int kPlanHeaderInts = 64;
+constexpr int kPlanItemInts = 72;
+constexpr int kPlanItemFields = 8;
+constexpr int32_t kPlanMagic = 0x53504b50;
+__host__ __device__ inline int64_t plan_items_off(int S) {
+  return kPlanHeaderInts + (static_cast<int64_t>(4) * S + 63) / 64 * 64;
+}
+// Does the plan describe a batch of these arguments, with every item
+// recorded?  (kPlStatus: 0, or 1 when the items exceeded the capacity.)
+// Its per-sequence records are copied into the workspace by the attention
+// launch, so the merge reads them as without a plan.
+__device__ inline bool plan_matches(const AttnArgs& a) {
+  const int32_t* h = a.plan;
+  return h[kPlMagic] == kPlanMagic && h[kPlS] == a.S && h[kPlHq] == a.Hq && h[kPlHkv] == a.Hkv &&
+         h[kPlB] == a.B && h[kPlWidth] == a.width && h[kPlMaxLen] == a.max_len &&
+         h[kPlMaxPrefix] == a.max_prefix && h[kPlGroups] == a.num_groups &&
+         h[kPlPartition] == a.partition && h[kPlStatus] == 0;
+}
+
 // Prefill (chunked) attention: sequence s's chunk is query rows
 // [qstart[s], qstart[s + 1]) at positions lens[s] - chunk_len .. lens[s] - 1.
 struct PrefillArgs {
@@ -227,6 +260,8 @@ int launch_prefill_f32(const PrefillArgs& a, hipStream_t stream);
 
 int launch_attention_bf16(const AttnArgs& a, hipStream_t stream);
 int launch_attention_bf16_shared(const AttnArgs& a, hipStream_t stream);
+// the plan launch: a's schedule fields, the plan, its item capacity
+int launch_shared_plan(const AttnArgs& a, int32_t* plan, int64_t capacity, hipStream_t stream);
 int launch_reduce_shared(const AttnArgs& a, hipStream_t stream);
 int launch_attention_bf16_stream(const AttnArgs& a, hipStream_t stream);
 int launch_attention_f32(const AttnArgs& a, hipStream_t stream);

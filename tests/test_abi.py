@@ -187,6 +187,49 @@ def test_shared_prefix_host_checks(lib):
                                         None) == -1
 
 
+def test_shared_plan_host_checks(lib):
+    """Sizing and argument checks of the shared-prefix plan and the planned
+    decode, all made before anything is launched."""
+    p = ctypes.c_void_p(0x1000)  # never dereferenced: the checks fail first
+    BF16 = 1
+    # header of 64 ints, the sequences' records [4][S] padded to 64 ints, then
+    # 72 ints per item; items at most: (kv-head groups) x (column blocks
+    # S*G/16 + groups) x prefix parts + S x (kv-head groups) x (head chunks)
+    # x parts of the longest sequence -- here 1 x (2 + 2) x 2 + 8 x 1 x 1 x 4
+    S, Hq, Hkv, B, ng, L, Lp, P = 8, 8, 2, 16, 2, 1000, 512, 256
+    items = 1 * (2 + 2) * 2 + 8 * 1 * 1 * 4
+    want = (64 + 64 + items * 72) * 4
+    assert lib.paged_attention_shared_plan_bytes(S, Hq, Hkv, B, ng, L, Lp, P) == want
+    assert lib.paged_attention_shared_plan_bytes(S, Hq, Hkv, B, ng, L, Lp, 48) == 0
+    assert lib.paged_attention_shared_plan_bytes(S, Hq, Hkv, B, 0, L, Lp, P) == 0
+
+    pa = dict(plan=p, plan_bytes=1 << 30, tables=p, width=4, lens=p, gs=p, pl=p, ng=2, S=4, Hq=8,
+              Hkv=2, B=16, max_len=64, max_prefix=32, P=0, stream=None)
+
+    def plan(**kw):
+        a = dict(pa, **kw)
+        return lib.paged_attention_shared_plan(
+            a["plan"], a["plan_bytes"], a["tables"], a["width"], a["lens"], a["gs"], a["pl"],
+            a["ng"], a["S"], a["Hq"], a["Hkv"], a["B"], a["max_len"], a["max_prefix"], a["P"],
+            a["stream"])
+    assert plan(plan=None) == -1 and plan(gs=None) == -1
+    assert plan(plan=ctypes.c_void_p(0x1010)) == -1   # 256-byte alignment
+    assert plan(plan_bytes=64) == -3
+    assert plan(B=12) == -2 and plan(S=600) == -2
+    assert plan(ng=0) == -1 and plan(ng=5) == -1
+    assert plan(P=48) == -1 and plan(max_prefix=-1) == -1 and plan(Hq=7) == -1
+    assert plan(S=0) == 0
+
+    args = [p, 0, p, p, p, 4, p, p, p, 2, 4, 8, 2, 128, 16, 10, 0.1, 64, 32, 0, p, 1 << 30, BF16, 0]
+    for fn in (lib.paged_attention_decode_shared_planned,
+               lib.paged_attention_shared_planned_partitions,
+               lib.paged_attention_shared_planned_merge):
+        assert fn(*args, None, 1 << 30, None) == -1              # no plan
+        assert fn(*args, ctypes.c_void_p(0x1010), 1 << 30, None) == -1
+        assert fn(*args, p, 64, None) == -3                      # plan too small
+        assert fn(*(args[:10] + [0] + args[11:]), p, 64, None) == 0  # no sequences
+
+
 def test_decode_append_host_checks(lib):
     """Argument checks of the decode step with its write, made before
     anything is launched (the new tokens' key and value must both be given

@@ -7,6 +7,10 @@ float64 oracle within the same per-row relative error (2e-3 for bf16
 inputs).  Groups come from ``paged_attention_prefix_groups`` on the host
 tables, as a caller would get them, or are given by hand for the edge and
 error cases.
+
+The planned form (``paged_attention_shared_plan`` once, then
+``paged_attention_decode_shared_planned``) must give the same bits as the
+unplanned call on every case here, NaN rows included.
 """
 from functools import lru_cache
 
@@ -47,11 +51,27 @@ def groups_on_device(w, starts=None, plens=None):
             torch.from_numpy(np.asarray(plens, dtype=np.int32)).to(dev), maxp)
 
 
-def attend_shared(st, gs, pl, maxp, P=0, out_dtype=torch.float32, cached_kv=False):
+def make_plan(st, gs, pl, maxp, P=0):
+    w = st.w
+    return pkv.make_shared_plan(st.tables, st.lens, gs, pl, w.num_q_heads, w.num_kv_heads,
+                                w.block_size, w.max_context_len, maxp, partition_size=P)
+
+
+def attend_shared(st, gs, pl, maxp, P=0, out_dtype=torch.float32, cached_kv=False, plan=None):
     w = st.w
     return pkv.attention_decode_shared(st.query, st.kv, st.tables, st.lens, gs, pl, w.scale,
                                        w.max_context_len, maxp, partition_size=P,
-                                       out_dtype=out_dtype, cached_kv=cached_kv)
+                                       out_dtype=out_dtype, cached_kv=cached_kv, plan=plan)
+
+
+def attend_both(st, gs, pl, maxp, P=0, **kw):
+    """The unplanned result, after checking that the planned call gives the
+    same bits (NaN rows in the same places)."""
+    got = attend_shared(st, gs, pl, maxp, P=P, **kw)
+    planned = attend_shared(st, gs, pl, maxp, P=P, plan=make_plan(st, gs, pl, maxp, P), **kw)
+    a, b = got.float().cpu().numpy(), planned.float().cpu().numpy()
+    assert np.array_equal(a, b, equal_nan=True), "planned and unplanned calls differ"
+    return got
 
 
 def check_rows(got, ref, what, tol=TOL):
@@ -81,7 +101,7 @@ def test_small_every_row(Hq, Hkv, D, B):
     assert maxp == 256
     unit = max(32, B)
     for P in sorted({0, unit, 2 * unit, 512}):
-        got = attend_shared(st, gs, pl, maxp, P=P).cpu().numpy()
+        got = attend_both(st, gs, pl, maxp, P=P).cpu().numpy()
         check_rows(got, ref, f"{Hq}/{Hkv} D={D} B={B} P={P}")
 
 
@@ -97,7 +117,7 @@ def test_full_size_every_row():
     say(f"[shared] S={w.num_seqs} max_len={w.max_context_len}")
     st = H.upload(w)
     gs, pl, maxp = groups_on_device(w)
-    got = attend_shared(st, gs, pl, maxp).cpu().numpy()
+    got = attend_both(st, gs, pl, maxp).cpu().numpy()
     got_cached = attend_shared(st, gs, pl, maxp, cached_kv=True).cpu().numpy()
     del st
     ref = oracle_out(w)
@@ -112,7 +132,7 @@ def test_empty_suffixes():
     st = H.upload(w)
     gs, pl, maxp = groups_on_device(w)
     assert maxp == 320
-    check_rows(attend_shared(st, gs, pl, maxp).cpu().numpy(), ref, "empty suffixes")
+    check_rows(attend_both(st, gs, pl, maxp).cpu().numpy(), ref, "empty suffixes")
 
 
 def test_independent_sequences_and_edge_lengths():
@@ -126,7 +146,7 @@ def test_independent_sequences_and_edge_lengths():
     gs, pl, maxp = groups_on_device(w)
     assert maxp == 0 and len(pl) == len(lens)
     for P in (0, 32, 256):
-        got = attend_shared(st, gs, pl, maxp, P=P).cpu().numpy()
+        got = attend_both(st, gs, pl, maxp, P=P).cpu().numpy()
         assert not got[0].any(), "a sequence of length 0 gives zeros"
         check_rows(got[1:], ref[1:], f"independent P={P}")
 
@@ -154,7 +174,7 @@ def test_invalid_groups_give_nan_rows():
 
     def run(st_, starts_, plens_, maxp_=256):
         gs, pl, _ = groups_on_device(w, starts_, plens_)
-        return attend_shared(st_, gs, pl, maxp_).cpu().numpy()
+        return attend_both(st_, gs, pl, maxp_).cpu().numpy()
 
     # a prefix that is not a whole number of 32-token units
     bad = plens.copy(); bad[1] = 240
@@ -197,7 +217,54 @@ def test_most_sequences_and_long_suffixes():
     st = H.upload(w)
     gs, pl, maxp = groups_on_device(w)
     assert len(pl) == 64 and maxp == 64
-    got = attend_shared(st, gs, pl, maxp).cpu().numpy()
+    got = attend_both(st, gs, pl, maxp).cpu().numpy()
     check_rows(got, ref, "512 sequences, long suffixes")
     again = attend_shared(st, gs, pl, maxp).cpu().numpy()
     assert np.array_equal(got, again), "repeated calls give identical bits"
+
+
+def test_plan_serves_several_caches():
+    """One plan, two layers' caches read through the same tables (the second
+    pool's values scaled): each planned call gives the unplanned call's bits,
+    in bf16 and fp32 output, with cached and streamed loads."""
+    w = workloads.shared_prefix(seed=66, num_prompts=4, prompt_len=512, forks=6, max_private=200,
+                                num_q_heads=16, num_kv_heads=4, head_size=64, block_size=16)
+    st = H.upload(w)
+    gs, pl, maxp = groups_on_device(w)
+    plan = make_plan(st, gs, pl, maxp)
+    st2 = H.DeviceStep(**{**st.__dict__, "kv": (st.kv.float() * 0.5).to(st.kv.dtype)})
+    for s_ in (st, st2, st):
+        for kw in ({}, {"out_dtype": torch.bfloat16}, {"cached_kv": True}):
+            a = attend_shared(s_, gs, pl, maxp, **kw)
+            b = attend_shared(s_, gs, pl, maxp, plan=plan, **kw)
+            assert torch.equal(a, b), f"planned call differs ({kw})"
+
+
+def test_plan_for_other_arguments_gives_nan():
+    """A plan made for another partition size, prefix bound or batch gives
+    NaN rows (never reads outside its buffers); its own arguments give the
+    right rows."""
+    w = workloads.shared_prefix(seed=67, num_prompts=3, prompt_len=256, forks=4, max_private=90)
+    ref = oracle_out(w)
+    st = H.upload(w)
+    gs, pl, maxp = groups_on_device(w)
+    plan = make_plan(st, gs, pl, maxp, P=64)
+    check_rows(attend_shared(st, gs, pl, maxp, P=64, plan=plan).cpu().numpy(), ref,
+               "planned at its own partition size")
+    assert torch.isnan(attend_shared(st, gs, pl, maxp, P=128, plan=plan)).all()
+    # a buffer smaller than the call's arguments need is refused on the host;
+    # in one large enough, the plan is checked on the device
+    with pytest.raises(pkv.PagedKVError):
+        attend_shared(st, gs, pl, maxp + 32, P=64, plan=plan)
+
+    def padded(plan_):
+        big = torch.zeros(1 << 20, dtype=torch.uint8, device=plan_.device)
+        big[:plan_.numel()] = plan_
+        return big
+    assert torch.isnan(attend_shared(st, gs, pl, maxp + 32, P=64, plan=padded(plan))).all()
+    # a plan for the first 8 sequences (two groups), used for all 12
+    S8 = 8
+    small = pkv.make_shared_plan(st.tables[:S8], st.lens[:S8], gs[:3].clone(), pl[:2].clone(),
+                                 w.num_q_heads, w.num_kv_heads, w.block_size, w.max_context_len,
+                                 maxp, partition_size=64)
+    assert torch.isnan(attend_shared(st, gs, pl, maxp, P=64, plan=padded(small))).all()
