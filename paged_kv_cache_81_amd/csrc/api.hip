@@ -1218,7 +1218,10 @@ int decode_shared_impl(int phases, void* out, pkv_dtype out_dtype, const void* q
   a.ws_o = reinterpret_cast<float*>(ws);
   a.ws_ml = reinterpret_cast<float*>(ws + lay.ml_off);
   a.ws_seq = reinterpret_cast<int*>(ws + lay.seq_off);
-  if (planned) a.plan = static_cast<const int32_t*>(plan);
+  if (planned) {
+    a.plan = static_cast<const int32_t*>(plan);
+    a.plan_capacity = upper;
+  }
   if (phases & kAttend) {
     const int rc = launch_attention_bf16_shared(a, stream);
     if (rc != PKV_OK) return rc;

@@ -429,10 +429,25 @@ attention_bf16_shared_kernel(AttnArgs a) {
   // the grid's size from the arguments (read with the others at the start),
   // not from the dispatch's hidden arguments
   const int nwg = a.stream_waves / kWaves;
+  // Workgroup b runs on XCD b mod 8; with one item per workgroup, pair
+  // workgroups b and b + 8 (same XCD) on consecutive items -- the column
+  // blocks of one prefix partition.
+  int b = blockIdx.x;
+  if (NSLOT == 1 && nwg % 16 == 0) b = (b / 16) * 16 + 2 * (b % 8) + (b / 8) % 2;
+  const int it_first = b * NSLOT + slot;  // this wave's item of the first round
+
   // With a plan: its item counts (none if it was made for other arguments:
   // the merge then gives NaN), and its item records.  Without: make it.
   const bool planned = a.plan != nullptr;
   const int32_t* items = planned ? a.plan + plan_items_off(a.S) : nullptr;
+  // the record of the first round's item (see the item loop), loaded with
+  // the header: any record below the capacity lies in the plan buffer
+  int first_f = 0, first_win = 0;
+  if (planned && it_first < a.plan_capacity) {
+    const int32_t* r = items + static_cast<int64_t>(it_first) * kPlanItemInts;
+    first_f = r[lane % kPlanItemFields];
+    first_win = r[kPlanItemFields + lane];
+  }
   int t_pre, total;
   if (planned) {
     const int n_pre = a.plan[kPlPrefixItems];
@@ -458,12 +473,6 @@ attention_bf16_shared_kernel(AttnArgs a) {
     total = t_pre + p.sscan[a.S];
     if (wv == 0) check_prefix_tables<B>(a, p, nwg, lane);
   }
-
-  // Workgroup b runs on XCD b mod 8; with one item per workgroup, pair
-  // workgroups b and b + 8 (same XCD) on consecutive items -- the column
-  // blocks of one prefix partition.
-  int b = blockIdx.x;
-  if (NSLOT == 1 && nwg % 16 == 0) b = (b / 16) * 16 + 2 * (b % 8) + (b / 8) % 2;
 
   // LDS of this wave: its K tile, then stream_slots finished results of 16
   // rows [hh][SROW], their (m, l) pairs, and where each goes
@@ -509,17 +518,22 @@ attention_bf16_shared_kernel(AttnArgs a) {
   // rounds are dealt in reverse, so the slots that drew the long prefix items
   // (which come first) draw the short items at the end of the next round.
   const int stride = nwg * NSLOT;
-  for (int it0 = b * NSLOT + slot, round = 0; it0 < total + stride; it0 += stride, ++round) {
+  for (int it0 = it_first, round = 0; it0 < total + stride; it0 += stride, ++round) {
     const int it = (round & 1) ? (2 * round + 1) * stride - 1 - it0 : it0;
     if (it >= total) continue;
     Item m;
     int win0 = 0;
     if (planned) {
       // the record in two loads issued together: lane l takes field l % 8
-      // of the description and entry l of the table window
-      const int32_t* r = items + static_cast<int64_t>(it) * kPlanItemInts;
-      const int f = r[lane % kPlanItemFields];
-      win0 = r[kPlanItemFields + lane];
+      // of the description and entry l of the table window (the first
+      // round's, it == it_first, are loaded already)
+      int f = first_f;
+      win0 = first_win;
+      if (round > 0) {
+        const int32_t* r = items + static_cast<int64_t>(it) * kPlanItemInts;
+        f = r[lane % kPlanItemFields];
+        win0 = r[kPlanItemFields + lane];
+      }
       m.part = __builtin_amdgcn_readlane(f, 0);
       m.seq = __builtin_amdgcn_readlane(f, 1);
       m.kvg = __builtin_amdgcn_readlane(f, 2);

@@ -112,8 +112,10 @@ struct AttnArgs {
   const void* k_new;
   const void* v_new;
   // shared-prefix schedule with a plan made beforehand (nullptr: every
-  // workgroup of the attention launch makes its own)
+  // workgroup of the attention launch makes its own), and the item records
+  // its buffer holds room for
   const int32_t* plan;
+  int64_t plan_capacity;
 };
 
 // Stream schedule: wave w of W reads stream steps [start(w), start(w + 1))
