@@ -24,7 +24,10 @@ __global__ void __launch_bounds__(64) attention_f32_kernel(AttnArgs a) {
   constexpr int PER = D / 64;  // output dims per lane
   __shared__ float s_q[NH][D];
   __shared__ float s_p[NH][kMaxPart];
-  __shared__ int s_phys[kMaxPart];  // physical block of each token of the partition
+  // element offset of each token's row in the K (and V) half of the pool, -1
+  // for a token on a block outside the pool: phase 3 then addresses a value
+  // row with one add, and its loads go out back to back
+  __shared__ int64_t s_off[kMaxPart];
 
   const int lane = threadIdx.x;
   const int G = a.Hq / a.Hkv;
@@ -67,14 +70,16 @@ __global__ void __launch_bounds__(64) attention_f32_kernel(AttnArgs a) {
   for (int i = lane; i < n; i += 64) {
     const int t = t_begin + i;
     const int phys = i == lane ? phys_first : trow[t / B];
-    s_phys[i] = phys;
+    const bool in_pool = phys >= 0 && phys < a.NB;
+    const int64_t off = (static_cast<int64_t>(phys) * B + t % B) * row;
+    s_off[i] = in_pool ? off : -1;
     float dot[NH];
 #pragma unroll
     for (int h = 0; h < NH; ++h) dot[h] = 0.f;
-    if (phys < 0 || phys >= a.NB) {
+    if (!in_pool) {
       bad = true;
     } else {
-      const float4* kr = reinterpret_cast<const float4*>(kbase + (static_cast<int64_t>(phys) * B + t % B) * row);
+      const float4* kr = reinterpret_cast<const float4*>(kbase + off);
       for (int c = 0; c < D / 4; ++c) {
         const float4 kk = kr[c];
 #pragma unroll
@@ -94,19 +99,19 @@ __global__ void __launch_bounds__(64) attention_f32_kernel(AttnArgs a) {
   // 64 tokens per batch of value loads when one head's accumulators are all
   // a lane holds, 32 for a few heads, 16 when many heads' accumulators fill
   // the registers.  Every load of a batch is issued (a token past the end, or
-  // on a block outside the pool -- flagged in phase 1 -- reads block 0 and
-  // its value is then zeroed), so no branch separates them; the first batch
-  // is issued before phase 2, whose arithmetic then covers its latency.
+  // on a block outside the pool -- flagged in phase 1 -- reads the pool's
+  // first row and its value is then zeroed), so no branch separates them;
+  // the first batch is issued before phase 2, whose arithmetic then covers
+  // its latency.
   constexpr int kBatch = NH * PER == 1 ? 64 : (NH * PER >= 16 ? 16 : 32);
   float v[kBatch][PER];
   auto load_batch = [&](int i0) {
 #pragma unroll
     for (int k = 0; k < kBatch; ++k) {
       const int i = i0 + k;
-      const int phys = i < n ? s_phys[i] : -1;
-      const bool ok = phys >= 0 && phys < a.NB;
-      const float* vr = vbase + (static_cast<int64_t>(ok ? phys : 0) * B + (t_begin + i) % B) * row +
-                        lane * PER;
+      const int64_t off = i < n ? s_off[i] : -1;
+      const bool ok = off >= 0;
+      const float* vr = vbase + (ok ? off : 0) + lane * PER;
 #pragma unroll
       for (int e = 0; e < PER; ++e) v[k][e] = vr[e];
 #pragma unroll
