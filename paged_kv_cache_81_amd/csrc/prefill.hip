@@ -581,7 +581,9 @@ __global__ void __launch_bounds__(64) prefill_f32_kernel(PrefillArgs a) {
   constexpr int PER = D / 64;
   __shared__ float s_q[D];
   __shared__ float s_p[64];
-  __shared__ int s_phys[64];
+  // element offset of each key's row in the K (and V) half of the pool, -1
+  // for a key past the row's causal end or on a block outside the pool
+  __shared__ int64_t s_off[64];
   const int lane = threadIdx.x;
   const int row = blockIdx.x, h = blockIdx.y;
   // the sequence whose chunk holds this row: largest s with qstart[s] <= row
@@ -635,22 +637,35 @@ __global__ void __launch_bounds__(64) prefill_f32_kernel(PrefillArgs a) {
     const float m_new = fmaxf(m, wave_max(sc));
     const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
     const float alpha = __builtin_amdgcn_exp2f(m - m_use);
-    const float p = __builtin_amdgcn_exp2f(sc - m_use);
+    const float p = __builtin_amdgcn_exp2f(sc - m_use);  // 0 for a key without a score
     l = l * alpha + wave_sum(p);
     m = m_new;
     s_p[lane] = p;
-    s_phys[lane] = phys;
+    s_off[lane] = phys >= 0 ? (static_cast<int64_t>(phys) * B + t % B) * rowst : -1;
     __syncthreads();
 #pragma unroll
     for (int e = 0; e < PER; ++e) acc[e] *= alpha;
+    // values KB keys at a time, every load issued (a key without a row reads
+    // the pool's first row, zeroed), so no branch separates them
+    constexpr int KB = 16;
     const int cnt = min(64, n - t0);
-    for (int k = 0; k < cnt; ++k) {
-      const int ph = s_phys[k];
-      if (ph < 0) continue;
-      const float pk = s_p[k];
-      const float* vr = vbase + (static_cast<int64_t>(ph) * B + (t0 + k) % B) * rowst + lane * PER;
+    for (int k0 = 0; k0 < cnt; k0 += KB) {
+      float v[KB][PER];
 #pragma unroll
-      for (int e = 0; e < PER; ++e) acc[e] = fmaf(pk, vr[e], acc[e]);
+      for (int k = 0; k < KB; ++k) {
+        const int64_t off = s_off[k0 + k];
+        const float* vr = vbase + (off >= 0 ? off : 0) + lane * PER;
+#pragma unroll
+        for (int e = 0; e < PER; ++e) v[k][e] = vr[e];
+#pragma unroll
+        for (int e = 0; e < PER; ++e) v[k][e] = off >= 0 ? v[k][e] : 0.f;
+      }
+#pragma unroll
+      for (int k = 0; k < KB; ++k) {
+        const float pk = s_p[k0 + k];
+#pragma unroll
+        for (int e = 0; e < PER; ++e) acc[e] = fmaf(pk, v[k][e], acc[e]);
+      }
     }
     __syncthreads();
   }
