@@ -452,8 +452,9 @@ def test_bf16_output_is_rounded_fp32_output():
     assert torch.equal(f32.to(torch.bfloat16).view(torch.int16), b16.view(torch.int16))
 
 
-def test_bad_table_entry_poisons_only_its_sequence():
-    w = workloads.custom(8, [40, 300, 700], dtype="bf16", num_q_heads=4, num_kv_heads=2,
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_bad_table_entry_poisons_only_its_sequence(dtype):
+    w = workloads.custom(8, [40, 300, 700], dtype=dtype, num_q_heads=4, num_kv_heads=2,
                          head_size=64, block_size=16)
     st = H.upload(w)
     clean = H.attend(st, partition_size=64).cpu().numpy()

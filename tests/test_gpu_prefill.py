@@ -164,6 +164,33 @@ def test_prefill_chunked_equals_whole_prompt():
     assert err <= 2e-3, err
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_table_entry_outside_the_pool_gives_nan_rows(dtype):
+    """A table entry outside the pool among sequence 1's keys: its rows, which
+    all attend that block, are NaN; the other sequences' rows are unchanged
+    bit for bit."""
+    pw = workloads.prefill(973, [0, 100, 20], [60, 40, 30], dtype=dtype, num_q_heads=4,
+                           num_kv_heads=2, head_size=64)
+    w = pw.cache
+    st = H.upload(w, device=DEV)
+    q = H.to_torch(pw.query, w.dtype, DEV)
+    qs = torch.from_numpy(pw.query_start).to(DEV)
+
+    def attend():
+        out = pkv.attention_prefill(q, st.kv, st.tables, st.lens, qs, w.scale,
+                                    max_query_len=pw.max_query_len)
+        torch.cuda.synchronize()
+        return out.float().cpu().numpy()
+    clean = attend()
+    assert np.isfinite(clean).all()
+    st.tables[1, 3] = w.num_blocks + 5  # keys 48..63 of sequence 1; its rows sit at 100..139
+    bad = attend()
+    r0, r1 = int(pw.query_start[1]), int(pw.query_start[2])
+    assert np.isnan(bad[r0:r1]).all()
+    others = np.r_[0:r0, r1:pw.num_tokens]
+    assert np.array_equal(bad[others], clean[others])
+
+
 def test_prefill_edge_cases():
     """Empty chunks write nothing, rows outside every chunk stay untouched,
     a chunk longer than its sequence or than max_query_len gives NaN rows."""
