@@ -85,9 +85,10 @@ def check_rows(got, ref, what, tol=TOL):
 # head shapes (Hq, Hkv, D, B): the parallel-sampling shape, Qwen2-like GQA
 # (7 heads per kv head: two members per 16-column block), MHA, 16 heads per
 # kv head (one member per block), 40 heads per kv head (a member spans three
-# blocks; suffix items in three query-head chunks), blocks of 8, 32 and 64
+# blocks; suffix items in three query-head chunks), 16 kv heads of 128 (keys
+# rearranged through LDS), blocks of 8, 32 and 64
 SHAPES = [(32, 8, 128, 16), (14, 2, 64, 16), (8, 8, 128, 32), (16, 1, 64, 64), (8, 2, 128, 8),
-          (12, 4, 64, 32), (40, 1, 128, 16)]
+          (12, 4, 64, 32), (40, 1, 128, 16), (32, 16, 128, 16)]
 
 
 @pytest.mark.parametrize("Hq,Hkv,D,B", SHAPES)
