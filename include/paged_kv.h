@@ -289,11 +289,11 @@ int paged_attention_merge(void* out, pkv_dtype out_dtype, const void* query,
  * same -1 cases as paged_kv_write_positions: nothing is written), then
  * everything is as paged_attention_decode.  Cache and output are
  * bit-identical to paged_kv_write_positions (positions L - 1) followed by
- * paged_attention_decode.  Under the stream schedule, when few of its pieces
- * hold a sequence's last step, the write happens inside the attention launch
- * (the wave that reads a sequence's last step stores the new row first, then
- * reads it back like the rest: one launch less); otherwise the library
- * launches the write first.  Sequences whose last token is
+ * paged_attention_decode.  With fp32 caches, and under the stream schedule
+ * when few of its pieces hold a sequence's last step, the write happens
+ * inside the attention launch (the waves that read a sequence's last token
+ * store the new row first, then read it back like the rest: one launch
+ * less); otherwise the library launches the write first.  Sequences whose last token is
  * already cached (e.g. a fork still on its shared prompt) must use the
  * separate calls.
  *
@@ -312,8 +312,9 @@ int paged_attention_decode_append(void* out, pkv_dtype out_dtype, const void* qu
 
 /*
  * Whether paged_attention_decode_append with these arguments stores the new
- * tokens inside its attention launch (1) or launches the write first (0);
- * -1 for inconsistent head counts or when the device cannot be queried.
+ * tokens inside its attention launch (1: always with fp32 caches) or
+ * launches the write first (0); -1 for inconsistent head counts or when the
+ * device cannot be queried.
  * Needs the device the call will run on to be current.  Host only.
  */
 int paged_attention_append_in_launch(int num_seqs, int num_q_heads, int num_kv_heads,

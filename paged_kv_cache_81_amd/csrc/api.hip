@@ -611,10 +611,15 @@ int decode_impl(int phases, void* out, pkv_dtype out_dtype, const void* query,
     a.ws_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) +
                                        (rows * head_size * 4 + 255) / 256 * 256);
   }
+  // fp32: the attention launch stores the new tokens itself (each
+  // sequence's at position context_lens[s] - 1); the bf16 fixed partitions
+  // write them first, then read them like the rest
+  if (key_new && dtype == PKV_F32) {
+    a.k_new = key_new;
+    a.v_new = value_new;
+  }
   if (phases & kAttend) {
-    // the other schedules write the new tokens first (each sequence's at
-    // position context_lens[s] - 1), then read them like the rest
-    if (key_new) {
+    if (key_new && dtype != PKV_F32) {
       const int rc = launch_write_positions(key_new, value_new, const_cast<void*>(kv_cache),
                                             block_tables, table_width, nullptr, context_lens, -1,
                                             nullptr, num_seqs, num_seqs, num_blocks, block_size,
@@ -817,6 +822,7 @@ int paged_attention_append_in_launch(int num_seqs, int num_q_heads, int num_kv_h
                                      int partition_size, pkv_dtype dtype) {
   (void)block_size;
   if (num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0 || num_seqs < 0) return -1;
+  if (dtype == PKV_F32) return 1;
   if (!uses_stream(num_seqs, num_q_heads, num_kv_heads, max_context_len, partition_size, dtype))
     return 0;
   const int waves = stream_waves(head_size);

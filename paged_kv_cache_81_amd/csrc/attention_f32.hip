@@ -53,6 +53,14 @@ __global__ void __launch_bounds__(64) attention_f32_kernel(AttnArgs a) {
   const float* q = static_cast<const float*>(a.query);
   for (int i = lane; i < NH * D; i += 64)
     s_q[i / D][i % D] = i < nh * D ? q[(static_cast<int64_t>(s) * a.Hq + h0) * D + i] : 0.f;
+  // the kv head's row of the sequence's new key and value (if given), in the
+  // same round: lane l < D/4 holds dims 4l .. 4l + 3
+  float4 k_new = make_float4(0.f, 0.f, 0.f, 0.f), v_new = k_new;
+  if (a.k_new != nullptr && lane < D / 4) {
+    const int64_t nrow = (static_cast<int64_t>(s) * a.Hkv + kvh) * D + 4 * lane;
+    k_new = *reinterpret_cast<const float4*>(static_cast<const float*>(a.k_new) + nrow);
+    v_new = *reinterpret_cast<const float4*>(static_cast<const float*>(a.v_new) + nrow);
+  }
 
   const int nparts = L > 0 ? (L + P - 1) / P : 1;
   const bool bad_seq = L < 0 || (L + B - 1) / B > a.width || nparts > a.max_parts;
@@ -64,6 +72,31 @@ __global__ void __launch_bounds__(64) attention_f32_kernel(AttnArgs a) {
   const float* vbase = kbase + static_cast<int64_t>(a.NB) * B * row;
   bool bad = bad_seq;
   const int phys_first = lane < n ? phys_spec : 0;
+
+  // With new tokens given, token L - 1 of the sequence is stored into the
+  // cache by every work item that reads it (each query-head chunk of the kv
+  // head stores the same bytes; an invalid sequence's token is stored by its
+  // partition 0, as the write kernel would), before the loads below read it
+  // back: a wavefront's own stores precede its later loads of the same
+  // address, and the release/acquire pair keeps the compiler from moving
+  // those loads above the stores.  The slot rule and its -1 cases are the
+  // write kernel's.  The token's block comes from the entries loaded above
+  // when it lies among the partition's first 64 tokens.
+  if (a.k_new != nullptr && L > 0 && part == (bad_seq ? 0 : nparts - 1)) {
+    const int tl = L - 1;
+    if (tl / B < a.width) {
+      const int k = tl - t_begin;
+      const int phys = k >= 0 && k < 64 && k < P ? __shfl(phys_spec, k, 64) : trow[tl / B];
+      if (phys >= 0 && phys < a.NB && lane < D / 4) {
+        float* kd = const_cast<float*>(kbase) + (static_cast<int64_t>(phys) * B + tl % B) * row +
+                    4 * lane;
+        *reinterpret_cast<float4*>(kd) = k_new;
+        *reinterpret_cast<float4*>(kd + static_cast<int64_t>(a.NB) * B * row) = v_new;
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  }
   __syncthreads();
 
   // phase 1: scores

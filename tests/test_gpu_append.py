@@ -96,22 +96,42 @@ def test_fp32_append_matches_write_then_decode():
     _compare(w)
 
 
-def test_append_edge_cases():
+# fp32 caches store the new token inside the attention launch: head shapes,
+# blocks of 5 and 48 tokens, partitions whose last token lies past their
+# first 64 (its block then comes from a table load of its own), two chunks of
+# query heads per kv head (both store the row)
+@pytest.mark.parametrize("hq,hkv,D,B,P", [(4, 4, 64, 16, 64), (40, 2, 128, 5, 320),
+                                          (6, 3, 64, 48, 96), (8, 2, 128, 16, 512),
+                                          (12, 4, 64, 8, 0)])
+def test_fp32_append_shapes(hq, hkv, D, B, P):
+    w = workloads.custom(9600 + hq + D + B, [1, 2, 17, 64, 65, 130, 300, 511, 700],
+                         dtype="f32", num_q_heads=hq, num_kv_heads=hkv, head_size=D,
+                         block_size=B)
+    say(f"[append] fp32 {hq}/{hkv} D={D} B={B} P={P}")
+    assert pkv.lib.paged_attention_append_in_launch(w.num_seqs, hq, hkv, D, B,
+                                                     w.max_context_len, P, 0) == 1
+    _compare(w, P=P)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_append_edge_cases(dtype):
     """A length-0 sequence (nothing written, zeros), an out-of-range table
     entry for a new token's block (NaN, nothing written), a sequence longer
-    than max_context_len (NaN; its token is still written, as the write kernel
-    does) and bf16 output: all exactly as the separate calls."""
-    w = workloads.custom(9300, [0, 40, 33, 100, 17, 64], num_q_heads=8, num_kv_heads=2,
-                         head_size=64, block_size=16)
+    than max_context_len (its token is still written, as the write kernel
+    does; NaN under the bf16 stream schedule, which checks that bound, and
+    attended normally by the fp32 kernel, whose fixed partitions still cover
+    it) and bf16 output: all exactly as the separate calls."""
+    w = workloads.custom(9300, [0, 40, 33, 100, 17, 64], dtype=dtype, num_q_heads=8,
+                         num_kv_heads=2, head_size=64, block_size=16)
     w.block_tables[1, (40 - 1) // 16] = w.num_blocks + 7   # new token's block out of range
     w.block_tables[4, (17 - 1) // 16] = -3                 # ... and negative
     say("[append] edge cases")
     got = _compare(w, max_len=80, oracle_check=False)
     out = got.cpu().numpy()
     assert np.all(out[0] == 0)
-    for s in (1, 3, 4):
+    for s in (1, 3, 4) if dtype == "bf16" else (1, 4):
         assert np.all(np.isnan(out[s])), s
-    assert np.all(np.isfinite(out[[2, 5]]))
+    assert np.all(np.isfinite(out[[2, 5] if dtype == "bf16" else [2, 3, 5]]))
     _compare(w, max_len=80, out_dtype=torch.bfloat16, oracle_check=False)
 
 
@@ -144,8 +164,9 @@ def test_append_partitions_then_merge_and_repeat():
 def test_write_placement_for_the_benchmark_shapes():
     """Where the write goes on this device: inside the attention launch for
     the Qwen2-shaped and long-context batches (few pieces hold a sequence's
-    last step), a launch of its own for the OPT-13B-shaped one."""
-    want = {"qwen2_gqa": 1, "long_context": 1, "opt13b_mha": 0, "tiny": 0}
+    last step) and for fp32 caches, a launch of its own for the OPT-13B-shaped
+    one."""
+    want = {"qwen2_gqa": 1, "long_context": 1, "opt13b_mha": 0, "tiny": 1}
     for name, exp in want.items():
         w = workloads.make(name)
         got = pkv.lib.paged_attention_append_in_launch(
