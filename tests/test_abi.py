@@ -257,7 +257,7 @@ def test_decode_append_host_checks(lib):
     # where the write goes: only the stream schedule (bf16, automatic
     # partitioning) can store it inside the attention launch
     assert lib.paged_attention_append_in_launch(4, 7, 2, 128, 16, 64, 0, 1) == -1
-    assert lib.paged_attention_append_in_launch(4, 8, 2, 128, 16, 64, 0, 0) == 0   # fp32
+    assert lib.paged_attention_append_in_launch(4, 8, 2, 128, 16, 64, 0, 0) == 1   # fp32: in launch
     assert lib.paged_attention_append_in_launch(4, 8, 2, 128, 16, 64, 64, 1) == 0  # fixed
 
 
